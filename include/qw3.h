@@ -1,0 +1,220 @@
+/*
+ * qw3.h -- C ABI of the MI355X (gfx950) Qwen3 decoder-block library, libqw3.so.
+ *
+ * The library evaluates the Qwen3 decoder forward pass in the order fixed by
+ * "Scalar-Native Qwen3 Reference Runtime As The Numerical Authority", section 2
+ * ("Decoder-Layer Mathematical Formulation", items 1-7): RMSNorm, bias-free
+ * Q/K/V projections, per-head QK-Norm, RoPE, grouped-query attention over a KV
+ * cache, o_proj + residual, SwiGLU MLP + residual, then a final RMSNorm and
+ * tied-embedding logits, with greedy (lowest-id-on-ties) argmax.
+ *
+ * ABI conventions ("Portable WebAssembly Runtime Architecture for TinyRustLM",
+ * "Typed host/Wasm API" and "Generational handles"):
+ *   - extern "C", fixed-width integers, no C++ types, no exceptions.
+ *   - A model is named by a uint64 handle: generation << 32 | slot.  Using a
+ *     destroyed handle returns QW3_STALE_HANDLE; a never-issued one
+ *     QW3_INVALID_HANDLE.
+ *   - Every call returns an int32 status (qw3_status_t); 0 is success.
+ *
+ * Memory ownership: the library never allocates device memory.  The caller
+ * allocates one device arena of the size qw3_preflight reports (for example a
+ * torch uint8 tensor) and keeps it alive until qw3_destroy.  The library owns
+ * the layout inside the arena.  All other device pointers (tokens, logits,
+ * argmax, hidden states) belong to the caller.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ * Device work is enqueued asynchronously on it; device pointers passed to a
+ * call must stay valid until the stream has passed that call.  Host-side
+ * checks (arguments, shapes, context length) run before anything is enqueued:
+ * when they fail, nothing is launched and no state changes.  A handle is not
+ * thread-safe; use one handle per stream.
+ */
+#ifndef QW3_H
+#define QW3_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QW3_ABI_VERSION 1u
+
+/* Status codes; numbering follows the error taxonomy of "Portable WebAssembly Runtime Architecture for
+ * TinyRustLM" ("Error taxonomy"), plus QW3_DEVICE_ERROR for a failed HIP runtime call. */
+typedef enum {
+    QW3_OK = 0,
+    QW3_INVALID_ARGUMENT = 1,
+    QW3_UNSUPPORTED_ABI = 2,
+    QW3_INVALID_HANDLE = 4,
+    QW3_STALE_HANDLE = 5,
+    QW3_BOUNDS = 6,
+    QW3_ALIGNMENT = 7,
+    QW3_INTEGER_OVERFLOW = 8,
+    QW3_OUT_OF_MEMORY = 9,
+    QW3_INVALID_MODEL = 10,
+    QW3_UNSUPPORTED_QUANTIZATION = 12,
+    QW3_UNSUPPORTED_SHAPE = 13,
+    QW3_CONTEXT_EXCEEDED = 14,
+    QW3_NUMERICAL_FAILURE = 18,
+    QW3_INTERNAL_INVARIANT = 20,
+    QW3_DEVICE_ERROR = 21
+} qw3_status_t;
+
+enum { QW3_WEIGHTS_BF16 = 1, QW3_WEIGHTS_Q8 = 2 };
+enum { QW3_INPUT_TOKENS = 0, QW3_INPUT_HIDDEN = 1 };
+
+/* Model and session shape.  Every field is explicit; nothing is defaulted ("M1 — Load the weights",
+ * Config::load: no silent defaults).  Supported shapes (else QW3_UNSUPPORTED_SHAPE):
+ *   head_dim == 128; n_q_heads % n_kv_heads == 0 and n_q_heads / n_kv_heads in {1, 2, 4};
+ *   hidden, n_q_heads*128 and intermediate multiples of 512 (bf16) or 1024 (Q8);
+ *   1 <= n_seq <= 16; 1 <= max_prefill; max_ctx >= 1; vocab_size >= 1 in token mode.
+ * weight_format QW3_WEIGHTS_Q8 stores every matrix (projections, MLP, embedding) as int8 codes in
+ * [-127, 127] with one f32 scale per 32 consecutive input elements ("Scalar-Native ...", section 3
+ * "Mixed-Q8 Quantization Definition", with the scale widened to f32).  Norm weights are bf16 in the
+ * bf16 format and f32 in the Q8 format.
+ * input_mode QW3_INPUT_HIDDEN runs the layer stack on caller-supplied f32 hidden states (no embedding,
+ * no final norm, no logits; vocab_size must be 0). */
+typedef struct qw3_config {
+    uint32_t abi_version;   /* must equal QW3_ABI_VERSION */
+    uint32_t weight_format; /* QW3_WEIGHTS_BF16 or QW3_WEIGHTS_Q8 */
+    uint32_t input_mode;    /* QW3_INPUT_TOKENS or QW3_INPUT_HIDDEN */
+    int32_t vocab_size;
+    int32_t hidden;
+    int32_t n_layers;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t intermediate;
+    int32_t max_ctx;     /* admitted context per sequence (KV positions) */
+    int32_t n_seq;       /* independent sequences decoded together */
+    int32_t max_prefill; /* tokens per prefill tile (longer prefills run tile by tile) */
+    float rms_eps;
+    double rope_theta;
+} qw3_config_t;
+
+/* Arena budget in bytes, per region; total is what qw3_create needs. */
+typedef struct qw3_sizes {
+    uint64_t total;
+    uint64_t weights;
+    uint64_t kv;
+    uint64_t scratch;
+    uint64_t state;
+} qw3_sizes_t;
+
+/* Tensor kinds: the per-model inventory of "M1 — Load the weights" ("What it prints", tensor table). */
+enum {
+    QW3_T_EMBED = 0,      /* [vocab, hidden] model.embed_tokens */
+    QW3_T_FINAL_NORM = 1, /* [hidden] model.norm */
+    QW3_T_LM_HEAD = 2,    /* [vocab, hidden] optional; tied: must be byte-identical to QW3_T_EMBED */
+    QW3_T_ATTN_NORM = 3,  /* [hidden] input_layernorm */
+    QW3_T_Q = 4,          /* [n_q_heads*head_dim, hidden] */
+    QW3_T_K = 5,          /* [n_kv_heads*head_dim, hidden] */
+    QW3_T_V = 6,          /* [n_kv_heads*head_dim, hidden] */
+    QW3_T_Q_NORM = 7,     /* [head_dim] */
+    QW3_T_K_NORM = 8,     /* [head_dim] */
+    QW3_T_O = 9,          /* [hidden, n_q_heads*head_dim] */
+    QW3_T_MLP_NORM = 10,  /* [hidden] post_attention_layernorm */
+    QW3_T_GATE = 11,      /* [intermediate, hidden] */
+    QW3_T_UP = 12,        /* [intermediate, hidden] */
+    QW3_T_DOWN = 13       /* [hidden, intermediate] */
+};
+enum { QW3_DT_BF16 = 1, QW3_DT_F32 = 2, QW3_DT_Q8 = 3 };
+
+/* One canonical host tensor.  Matrices are [rows = out, cols = in] row-major (y = x W^T).
+ * QW3_DT_BF16: data = uint16 bf16 bit patterns.  QW3_DT_F32: data = float.
+ * QW3_DT_Q8: data = int8 codes [rows, cols], scales = float [rows, cols/32].
+ * Norm tensors are vectors: rows = 1, cols = length.  layer = -1 for global tensors. */
+typedef struct qw3_tensor {
+    int32_t kind;
+    int32_t layer;
+    int32_t dtype;
+    int32_t reserved;
+    int64_t rows;
+    int64_t cols;
+    const void *data;
+    const float *scales;
+} qw3_tensor_t;
+
+/* ABI version the library was built with. */
+uint32_t qw3_abi_version(void);
+
+/* Validates cfg and reports the arena budget.  Allocates nothing ("Portable WebAssembly Runtime ...",
+ * memory formulas: preflight rejects a model/context pair before allocating).  Sizes use checked 64-bit
+ * arithmetic (QW3_INTEGER_OVERFLOW on wrap).  Errors: QW3_INVALID_ARGUMENT (NULL), QW3_UNSUPPORTED_ABI,
+ * QW3_UNSUPPORTED_SHAPE, QW3_UNSUPPORTED_QUANTIZATION (unknown format). */
+int32_t qw3_preflight(const qw3_config_t *cfg, qw3_sizes_t *out);
+
+/* Creates a model in a caller-owned device arena of at least qw3_preflight(cfg).total bytes, 256-byte
+ * aligned (QW3_ALIGNMENT otherwise; QW3_OUT_OF_MEMORY if too small).  No device work is done here;
+ * the arena is initialised by qw3_load_weights.  Writes the new handle to *handle_out. */
+int32_t qw3_create(const qw3_config_t *cfg, void *arena_dev, uint64_t arena_bytes, uint64_t *handle_out);
+
+/* Validates and uploads the whole tensor set, packing it into the arena's device layout, then resets
+ * every sequence's KV length to 0.  `tensors` lists n host tensors; each expected tensor must appear
+ * exactly once with the configured shape and dtype, lm_head may be absent or byte-identical to the
+ * embedding ("M1 — Load the weights", cross-check: missing, mis-shaped and unexpected tensors are
+ * problems; tied lm_head may be omitted or shipped as a copy).  Any violation returns
+ * QW3_INVALID_MODEL before any device work.  Host buffers are read during the call only; the call
+ * returns after the copies have completed on `stream`. */
+int32_t qw3_load_weights(uint64_t handle, const qw3_tensor_t *tensors, int32_t n, void *stream);
+
+/* Prefill of sequence `seq`: appends n_tokens tokens at positions len..len+n_tokens-1 (KV cache, "Scalar-
+ * Native ...", section 6 "Continuation and Append") and writes the last position's logits (vocab f32,
+ * may be NULL) and greedy argmax (one int32, may be NULL).  tokens_dev: int32 device array [n_tokens],
+ * each in [0, vocab).  len+n_tokens > max_ctx returns QW3_CONTEXT_EXCEEDED before any launch
+ * (section 6 "Maximum Context Overflow": no ring buffering).  bf16 models run the tiled MFMA prefill;
+ * Q8 models run token by token.  The length advances (commit) only when the step completes. */
+int32_t qw3_prefill(uint64_t handle, int32_t seq, const int32_t *tokens_dev, int32_t n_tokens, float *logits_dev,
+                    int32_t *argmax_dev, void *stream);
+
+/* One greedy decode step for all n_seq sequences: tokens_dev int32 [n_seq] (may alias the previous
+ * step's argmax_dev), logits_dev f32 [n_seq, vocab] (may be NULL), argmax_dev int32 [n_seq] (required).
+ * Each sequence appends one position and commits len += 1.  Any sequence at len == max_ctx returns
+ * QW3_CONTEXT_EXCEEDED with nothing launched.  A non-finite logit latches QW3_NUMERICAL_FAILURE
+ * ("Scalar-Native ...", section 4 "NaN/Inf Rejection"), reported by qw3_status_poll and by every later
+ * call until qw3_reset_kv; the argmax of steps completed before stays valid (section 8). */
+int32_t qw3_decode_step(uint64_t handle, const int32_t *tokens_dev, float *logits_dev, int32_t *argmax_dev,
+                        void *stream);
+
+/* Resets the KV length of `seq` (or of all sequences when seq == -1) to 0 and clears a latched
+ * numerical failure.  No memset: old positions become unreachable because attention is bounded by the
+ * length ("Scalar-Native ...", section 6 "Cancellation and Reset").  Host-side only. */
+int32_t qw3_reset_kv(uint64_t handle, int32_t seq);
+
+/* Waits for `stream` and returns the latched device status (QW3_OK or QW3_NUMERICAL_FAILURE). */
+int32_t qw3_status_poll(uint64_t handle, void *stream);
+
+/* Host copy of a sequence's committed KV length. */
+int32_t qw3_get_len(uint64_t handle, int32_t seq, int32_t *len_out);
+
+/* Releases the handle (the arena stays owned by the caller).  Later use returns QW3_STALE_HANDLE. */
+int32_t qw3_destroy(uint64_t handle);
+
+/* ---- test and benchmark hooks (not part of the serving path) ------------------------------------- */
+
+/* Layer stack on caller hidden states (input_mode QW3_INPUT_HIDDEN, sequence 0): hidden_in_dev f32
+ * [n_tokens, hidden] at positions len..len+n_tokens-1, writes hidden_out_dev f32 [n_tokens, hidden]
+ * (every position's output).  n_tokens == 1 runs the decode kernels, n_tokens > 1 the prefill kernels. */
+int32_t qw3_block_forward(uint64_t handle, const float *hidden_in_dev, int32_t n_tokens, float *hidden_out_dev,
+                          void *stream);
+
+/* Writes n_pos cache positions of one (seq, layer): k_dev, v_dev bf16 bits [n_kv_heads, n_pos, head_dim].
+ * Does not change the length.  QW3_BOUNDS when pos0+n_pos > max_ctx. */
+int32_t qw3_kv_write(uint64_t handle, int32_t seq, int32_t layer, int32_t pos0, int32_t n_pos, const uint16_t *k_dev,
+                     const uint16_t *v_dev, void *stream);
+
+/* Reads n_pos cache positions of one (seq, layer) into k_dev, v_dev (same layout as qw3_kv_write). */
+int32_t qw3_kv_read(uint64_t handle, int32_t seq, int32_t layer, int32_t pos0, int32_t n_pos, uint16_t *k_dev,
+                    uint16_t *v_dev, void *stream);
+
+/* Sets the committed KV length of `seq` (after qw3_kv_write).  QW3_BOUNDS when len > max_ctx. */
+int32_t qw3_set_len(uint64_t handle, int32_t seq, int32_t len, void *stream);
+
+/* Dequantized f32 copy of a packed matrix as the kernels read it: kind in QW3_T_Q..QW3_T_DOWN (with
+ * layer) or QW3_T_EMBED; out_dev f32 [rows, cols].  For Q8 each element is one f32 multiply code*scale. */
+int32_t qw3_dequant(uint64_t handle, int32_t kind, int32_t layer, float *out_dev, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QW3_H */

@@ -259,3 +259,42 @@ Q8_BATCHED = Workload("28-layer Q8 16 sequences x KV context 8192, 64 greedy ite
                       kv_prefill=8192, decode=64)
 
 WORKLOADS = (SINGLE_BLOCK, BF16_DECODE, Q8_DECODE, BF16_PREFILL, Q8_BATCHED)
+
+
+# ---------------------------------------------------------------------------------------------
+# Marshalling helpers: the canonical tensors and shape as plain dicts for the library binding
+# ---------------------------------------------------------------------------------------------
+def abi_config_kwargs(shape: ModelShape) -> dict:
+    return dict(weight_format=shape.fmt, input_mode=shape.input_mode, vocab=shape.vocab, hidden=shape.hidden,
+                n_layers=shape.n_layers, n_q_heads=shape.n_q_heads, n_kv_heads=shape.n_kv_heads,
+                head_dim=shape.head_dim, inter=shape.inter, max_ctx=shape.max_ctx, n_seq=shape.n_seq,
+                max_prefill=shape.max_prefill, eps=shape.eps, theta=shape.theta)
+
+
+def abi_tensors(w: Weights, with_lm_head: bool = False) -> list:
+    """Tensor list (kind name, layer, dtype code, arrays) in the order of the inventory; dtype codes
+    1 = bf16 bits, 2 = f32, 3 = int8 codes + f32 scales."""
+    q8 = w.shape.fmt == FMT_Q8
+    out = []
+
+    def mat(kind, layer, m):
+        if q8:
+            out.append(dict(kind=kind, layer=layer, dtype=3, data=m.codes, scales=m.scales))
+        else:
+            out.append(dict(kind=kind, layer=layer, dtype=1, data=m.bf16))
+
+    def vec(kind, layer, v):
+        out.append(dict(kind=kind, layer=layer, dtype=2 if q8 else 1, data=v))
+
+    if w.embed is not None:
+        mat("embed", -1, w.embed)
+        vec("final_norm", -1, w.final_norm)
+        if with_lm_head:
+            mat("lm_head", -1, w.embed)
+    for l, d in enumerate(w.layers):
+        for slot in LAYER_SLOTS:
+            if slot in MATRIX_SLOTS:
+                mat(slot, l, d[slot])
+            else:
+                vec(slot, l, d[slot])
+    return out

@@ -1,0 +1,165 @@
+"""GPU parity of the decode path against the oracle (through the C ABI).
+
+Shapes: real-width blocks (hidden 1024, head_dim 128) with few layers and a ragged vocabulary (1000 rows:
+not a multiple of any GEMV tile), plus the GQA group sizes the kernels support, at sizes the oracle
+finishes in seconds.
+"""
+import sys
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import argmax_ok, assert_close, build_gpu_model
+
+pytestmark = pytest.mark.gpu
+
+SMALL = replace(synth.QWEN3_06B, vocab=1000, n_layers=2, n_q_heads=8, n_kv_heads=4, inter=1024, max_ctx=64,
+                max_prefill=32)
+
+
+def _torch():
+    import torch
+    assert torch.cuda.is_available()
+    return torch
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_BF16, synth.FMT_Q8])
+def test_dequant_bit_exact(fmt):
+    torch = _torch()
+    shp = replace(SMALL, fmt=fmt)
+    _say("dequant", shp)
+    W = synth.make_weights(shp, seed=21)
+    m = build_gpu_model(W)
+    for kind, layer in (("q", 0), ("k", 1), ("v", 1), ("o", 0), ("gate", 1), ("up", 0), ("down", 1),
+                        ("embed", -1)):
+        mat = W.embed if kind == "embed" else W.layers[layer][kind]
+        got = m.dequant(kind, layer, mat.rows, mat.cols).cpu().numpy()
+        torch.cuda.synchronize()
+        rows = np.arange(mat.rows)
+        ref = np.stack([oracle.dequant_row(mat, r) for r in rows])
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), kind
+
+
+def test_kv_write_read_roundtrip_and_bounds():
+    torch = _torch()
+    m = build_gpu_model(synth.make_weights(SMALL, seed=22))
+    k, v = synth.kv_fill(22, 0, 1, SMALL.n_kv_heads, 7, SMALL.head_dim)
+    kt = torch.from_numpy(k.view(np.int16)).cuda()
+    vt = torch.from_numpy(v.view(np.int16)).cuda()
+    m.kv_write(0, 1, 5, kt, vt)
+    k2, v2 = m.kv_read(0, 1, 5, 7)
+    assert np.array_equal(k2.cpu().numpy().view(np.uint16), k)
+    assert np.array_equal(v2.cpu().numpy().view(np.uint16), v)
+    import transformer_qwen3_block_amd as q
+    with pytest.raises(q.Qw3Error) as e:
+        m.kv_write(0, 1, SMALL.max_ctx - 3, kt, vt)
+    assert e.value.code == 6
+
+
+def _greedy_vs_oracle(shp, seed, steps, prefill_tokens=0, kv_fill_len=0, seqs_checked=None):
+    """Free-running GPU greedy decode, replayed through the oracle (teacher forcing)."""
+    torch = _torch()
+    W = synth.make_weights(shp, seed=seed)
+    m = build_gpu_model(W)
+    S = shp.n_seq
+    orc = oracle.Model(W)
+    if kv_fill_len:
+        for s in range(S):
+            for l in range(shp.n_layers):
+                k, v = synth.kv_fill(seed, s, l, shp.n_kv_heads, kv_fill_len, shp.head_dim)
+                m.kv_write(s, l, 0, torch.from_numpy(k.view(np.int16)).cuda(),
+                           torch.from_numpy(v.view(np.int16)).cuda())
+                orc.kv_write(s, l, 0, k, v)
+            m.set_len(s, kv_fill_len)
+            orc.set_len(s, kv_fill_len)
+    toks = synth.tokens(seed, 1, S, shp.vocab)
+    cur = torch.from_numpy(toks.copy()).cuda()
+    am = torch.empty(S, dtype=torch.int32, device="cuda")
+    logits = torch.empty((S, shp.vocab), dtype=torch.float32, device="cuda")
+    worst = (0.0, 0.0)
+    for step in range(steps):
+        m.decode_step(cur, am, logits)
+        torch.cuda.synchronize()
+        g_logits = logits.cpu().numpy()
+        g_am = am.cpu().numpy()
+        for s in (seqs_checked if seqs_checked is not None else range(S)):
+            rc, o_am, o_logits, _ = orc.step(s, int(cur[s].item()))
+            assert rc == 0
+            mab, r = assert_close(g_logits[s], o_logits, f"step {step} seq {s}")
+            worst = (max(worst[0], mab), max(worst[1], r))
+            assert argmax_ok(int(g_am[s]), o_logits, g_logits[s]), (step, s, int(g_am[s]), o_am)
+        cur = am.clone()
+    assert m.status() == 0
+    for s in range(S):
+        assert m.get_len(s) == kv_fill_len + steps
+    return worst
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_BF16, synth.FMT_Q8])
+def test_decode_small_vs_oracle(fmt):
+    shp = replace(SMALL, fmt=fmt)
+    _say("decode small", shp)
+    worst = _greedy_vs_oracle(shp, seed=23, steps=12)
+    _say("worst max-abs / rel-L2", worst)
+
+
+@pytest.mark.parametrize("heads", [(8, 8), (8, 2)])
+def test_decode_gqa_group_sizes(heads):
+    shp = replace(SMALL, n_q_heads=heads[0], n_kv_heads=heads[1], n_layers=1)
+    _say("gqa", heads)
+    _greedy_vs_oracle(shp, seed=24, steps=6)
+
+
+def test_decode_over_prefilled_cache_ragged_context():
+    """Context lengths that are not multiples of the 16-position groups or of the split count."""
+    shp = replace(SMALL, fmt=synth.FMT_Q8, max_ctx=400)
+    _greedy_vs_oracle(shp, seed=25, steps=4, kv_fill_len=333)
+
+
+def test_decode_batched_sequences():
+    shp = replace(SMALL, fmt=synth.FMT_Q8, n_seq=5, max_ctx=200)
+    _greedy_vs_oracle(shp, seed=26, steps=3, kv_fill_len=150)
+
+
+def test_context_exceeded_leaves_state():
+    torch = _torch()
+    import transformer_qwen3_block_amd as q
+    shp = replace(SMALL, max_ctx=3)
+    m = build_gpu_model(synth.make_weights(shp, seed=27))
+    cur = torch.zeros(1, dtype=torch.int32, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        m.decode_step(cur, am)
+    with pytest.raises(q.Qw3Error) as e:
+        m.decode_step(cur, am)
+    assert e.value.code == 14 and m.get_len(0) == 3
+    m.reset_kv(0)
+    assert m.get_len(0) == 0
+    m.decode_step(cur, am)
+    torch.cuda.synchronize()
+    assert m.get_len(0) == 1 and m.status() == 0
+
+
+def test_single_block_decode_hidden_states():
+    """Single real-size block in hidden-state mode, one position at a time."""
+    torch = _torch()
+    shp = replace(synth.SINGLE_BLOCK.shape)
+    W = synth.make_weights(shp, seed=1)
+    m = build_gpu_model(W)
+    orc = oracle.Model(W)
+    hin = synth.hidden_inputs(1, 1, 8, shp.hidden)
+    out = torch.empty((1, shp.hidden), dtype=torch.float32, device="cuda")
+    for t in range(8):
+        m.block_forward(torch.from_numpy(hin[t:t + 1]).cuda(), out)
+        torch.cuda.synchronize()
+        rc, _, _, ref = orc.step(0, hidden_in=hin[t], want_hidden=True)
+        assert rc == 0
+        assert_close(out.cpu().numpy()[0], ref, f"position {t}")

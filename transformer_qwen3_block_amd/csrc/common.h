@@ -1,0 +1,127 @@
+// Internal declarations shared by the host side and the gfx950 kernels of libqw3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qw3.h"
+
+namespace qw3 {
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxSeq = 16;
+constexpr int kMaxSplit = 64;          // decode attention splits of the context per (seq, kv head)
+constexpr int kPartStride = 2 + kHeadDim;  // per split partial: running max, running sum, o[128]
+constexpr int kLmMaxBlocks = 16384;    // upper bound on lm_head workgroups (argmax partials)
+
+// Byte offsets of every region inside the caller's arena.  Per-layer weight blocks repeat with a fixed
+// stride, so layer l's block starts at layer0 + l * layer_stride.
+struct Layout {
+    // weights
+    uint64_t embed, embed_scales, final_norm;
+    uint64_t layer0, layer_stride;
+    uint64_t l_wqkv, l_sqkv, l_wo, l_so, l_wgu, l_sgu, l_wd, l_sd;  // relative to the layer block
+    uint64_t l_attn_norm, l_mlp_norm, l_q_norm, l_k_norm;           // f32 vectors
+    uint64_t rope_cos, rope_sin;                                     // f32 [max_ctx][head_dim/2]
+    // KV cache, bf16 [seq][layer][kv_head][pos][head_dim]
+    uint64_t kcache, vcache;
+    // state
+    uint64_t len, status, att_counters, lm_counter;
+    // scratch
+    uint64_t x, xn16, qkv, q16, attn, attn16, act, act16, part, argpart, logits, tokens;
+    uint64_t weights_end, kv_end, state_end, scratch_end;
+};
+
+// Shape constants derived from the configuration.
+struct Dims {
+    int H, L, HQ, HKV, G, I, V, S, max_ctx, max_prefill;
+    int Nqkv;        // (HQ + 2*HKV) * 128
+    int q_dim;       // HQ * 128
+    bool q8;
+    bool hidden_mode;
+    float eps;
+};
+
+// ---- device helpers -------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// f32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (read-once data: weights, KV cache).
+__device__ __forceinline__ uint4 load_nt16(const void *p) {
+    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// ---- launchers (stream-ordered, no host synchronisation) ------------------------------------------
+enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+
+struct GemvArgs {
+    const void *w;          // bf16 bits or int8 codes, [rows][K]
+    const float *scales;    // Q8: [rows][K/32]
+    int N;                  // output units (rows; SwiGLU: gate/up pairs, up rows start at row N)
+    int K;
+    int S;                  // vectors (sequences)
+    const float *x;         // input [S][ldx]
+    int ldx;
+    const float *norm_w;    // optional RMSNorm weight applied to x first (f32 [K])
+    float eps;
+    float *y;               // output [S][ldy]
+    int ldy;
+    // EPI_LOGITS only
+    float *argpart;         // [S][gridDim.x][2]
+    unsigned *counter;
+    int *len;               // committed lengths of the S sequences (indexed from seq0)
+    int commit_add;
+    int *argmax_out;        // [S]
+    int *status;
+};
+
+hipError_t launch_gemv(bool q8, GemvEpi epi, const GemvArgs &a, hipStream_t st);
+
+struct AttnDecodeArgs {
+    const float *qkv;       // raw projections [S][ldqkv]
+    int ldqkv;
+    const float *q_norm, *k_norm;   // f32 [128]
+    const float *rope_cos, *rope_sin;
+    uint16_t *kcache, *vcache;      // base of (seq0, layer) head 0: [HKV][max_ctx][128]
+    long long seq_stride;           // elements between consecutive sequences' blocks of this layer
+    int max_ctx, HQ, HKV, S, n_split;
+    const int *len;                 // [S] (already offset to seq0)
+    float *part;                    // [S][HQ][kMaxSplit][kPartStride]
+    unsigned *counters;             // [S][HKV]
+    float *out;                     // [S][ldo]
+    int ldo;
+    float eps;
+};
+hipError_t launch_attn_decode(int G, const AttnDecodeArgs &a, hipStream_t st);
+
+hipError_t launch_embed(bool q8, const void *table, const float *scales, int H, const int *tokens, int S, float *x,
+                        int *status, int vocab, hipStream_t st);
+hipError_t launch_set_lens(int *len_dev, int n, const int *vals, int mask, int *status, int clear_status,
+                           hipStream_t st);
+hipError_t launch_commit(int *len_dev, int n, int add, hipStream_t st);
+hipError_t launch_dequant(bool q8, const void *w, const float *scales, long long rows, int cols, float *out,
+                          hipStream_t st);
+
+}  // namespace qw3

@@ -1,0 +1,11 @@
+// Tiled bf16 prefill on MFMA (internal).
+#pragma once
+#include "common.h"
+
+namespace qw3 {
+
+// Runs every layer for T tokens of sequence `seq` whose f32 inputs are in the x scratch rows 0..T-1,
+// at positions pos0..pos0+T-1, appending their K/V to the cache.  On return x holds the layer-stack output.
+int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, int pos0, int T, hipStream_t st);
+
+}  // namespace qw3
