@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Throughput of the Qwen3-0.6B-shaped decoder on one MI355X, through the C ABI.
+
+Step = one greedy decode token of the 28-layer Qwen3-0.6B shape with Q8 block-32 weights (int8 codes,
+one f32 scale per 32 inputs) at batch 1 over a KV context of 2048 positions: embedding, 28 x (RMSNorm +
+QKV, QK-Norm + RoPE + KV append + GQA attention, o_proj + residual, RMSNorm + gate/up SwiGLU,
+down + residual), final norm, tied logits and argmax.  Inputs are synthetic (seeded PCG32): codes uniform
+in [-127,127], scales U(1e-3,1e-2), norms 1+N(0,0.1), KV positions 0..2047 bf16 N(0,1).
+
+Prints one JSON line: decode tok/s (value), end-to-end HBM GB/s, per-kernel times with their achieved
+GB/s, the roofline entry of the dominant kernel (HIP events on the launch stream), the bf16 MFMA prefill
+of 2048 tokens (prefill tok/s), and the oracle timed on the host cores on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_kernel_bytes(shp, ctx):
+    """Algorithmic HBM bytes of one launch of each decode kernel at batch 1 (weights incl. Q8 scales,
+    KV positions read, activation vectors in/out)."""
+    H, I, Q, KV, V = shp.hidden, shp.inter, shp.q_dim, shp.kv_dim, shp.vocab
+    q8 = shp.fmt == 2
+
+    def w(rows, cols):
+        return rows * cols + rows * (cols // 32) * 4 if q8 else rows * cols * 2
+
+    nqkv = Q + 2 * KV
+    return {
+        "qkv_gemv": w(nqkv, H) + 4 * H + 4 * nqkv,
+        "attn_decode": ctx * shp.n_kv_heads * shp.head_dim * 2 * 2 + 4 * nqkv + 4 * Q,
+        "o_gemv": w(H, Q) + 4 * Q + 8 * H,
+        "gateup_gemv": w(2 * I, H) + 4 * H + 4 * I,
+        "down_gemv": w(H, I) + 4 * I + 8 * H,
+        "lm_head_argmax": w(V, H) + 4 * H + 4 * V,
+    }
+
+
+def run_decode(args, torch, q, synth):
+    wl = synth.Q8_DECODE
+    shp = wl.shape
+    t0 = time.time()
+    W = synth.make_weights(shp, seed=wl.seed)
+    cfg = q.make_config(**synth.abi_config_kwargs(shp))
+    m = q.Model(cfg, device="cuda:0")
+    m.load_weights(synth.abi_tensors(W))
+    ctx0 = wl.kv_prefill
+    for l in range(shp.n_layers):
+        k, v = synth.kv_fill(wl.seed, 0, l, shp.n_kv_heads, ctx0, shp.head_dim)
+        m.kv_write(0, l, 0, torch.from_numpy(k.view("int16")).cuda(), torch.from_numpy(v.view("int16")).cuda())
+    m.set_len(0, ctx0)
+    torch.cuda.synchronize()
+    log(f"decode workload ready in {time.time() - t0:.1f}s")
+
+    stream = torch.cuda.current_stream()   # a side stream: decode steps replay as captured HIP graphs
+    tok = torch.tensor(synth.tokens(wl.seed, 1, 1, shp.vocab), dtype=torch.int32, device="cuda:0")
+    am = torch.empty(1, dtype=torch.int32, device="cuda:0")
+    m.decode_step(tok, am)
+    for _ in range(args.warmup - 1):
+        m.decode_step(am, am)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        m.decode_step(am, am)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / args.steps
+    assert m.status() == 0, "numerical failure latched during the timed decode"
+    ctx_mid = ctx0 + args.warmup + args.steps // 2
+    log(f"decode: {ms * 1e3:.1f} us/token (wall {wall / args.steps * 1e6:.1f} us/token)")
+
+    # per-kernel timing: back-to-back launches of one kernel bracketed by HIP events on the launch stream
+    ctx_now = m.get_len(0)
+    kb = decode_kernel_bytes(shp, ctx_now + 1)
+    ids = {"qkv_gemv": 1, "attn_decode": 2, "o_gemv": 3, "gateup_gemv": 4, "down_gemv": 5, "lm_head_argmax": 6}
+    per_step = {k: (1 if k == "lm_head_argmax" else shp.n_layers) for k in ids}
+    kernels = {}
+    reps = args.kernel_reps
+    for name, kid in ids.items():
+        for r in range(3):
+            m.bench_kernel(kid, r % shp.n_layers)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for r in range(reps):
+            m.bench_kernel(kid, r % shp.n_layers)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        kernels[name] = {"us": round(us, 3), "bytes": kb[name], "GBps": round(kb[name] / us / 1e3, 1),
+                         "launches_per_step": per_step[name]}
+    step_bytes = sum(decode_kernel_bytes(shp, ctx_mid)[k] * per_step[k] for k in ids)
+    dom = max(kernels, key=lambda k: kernels[k]["us"] * kernels[k]["launches_per_step"])
+    del m
+    torch.cuda.empty_cache()
+    return dict(shp=shp, wl=wl, W=W, ms=ms, wall_us=wall / args.steps * 1e6, kernels=kernels, dominant=dom,
+                step_bytes=step_bytes, ctx_mid=ctx_mid)
+
+
+def run_prefill(args, torch, q, synth):
+    wl = synth.BF16_PREFILL
+    shp = wl.shape
+    W = synth.make_weights(shp, seed=wl.seed)
+    m = q.Model(q.make_config(**synth.abi_config_kwargs(shp)), device="cuda:0")
+    m.load_weights(synth.abi_tensors(W))
+    del W
+    toks = torch.tensor(synth.tokens(wl.seed, 0, wl.prefill, shp.vocab), dtype=torch.int32, device="cuda:0")
+    am = torch.empty(1, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        m.reset_kv(0)
+        m.prefill(toks, 0, None, am)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(args.prefill_reps):
+        m.reset_kv(0)
+        e0.record(stream)
+        m.prefill(toks, 0, None, am)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    assert m.status() == 0
+    times.sort()
+    ms = times[len(times) // 2]
+    T = wl.prefill
+    H, I, Q, KV, L = shp.hidden, shp.inter, shp.q_dim, shp.kv_dim, shp.n_layers
+    linear = 2 * T * L * (H * (Q + 2 * KV) + Q * H + 2 * H * I + I * H)
+    attn = 2 * 2 * shp.n_q_heads * shp.head_dim * L * (T * (T + 1) // 2)   # QK^T and PV over j <= i only
+    lm = 2 * shp.vocab * H
+    flops = linear + attn + lm
+    del m
+    torch.cuda.empty_cache()
+    return dict(tokens=T, ms=ms, tok_s=T / ms * 1e3, flops=flops, tflops=flops / ms / 1e9)
+
+
+def cpu_baseline(res, oracle, budget_s):
+    """The oracle as it stands, on the host cores, decoding greedy tokens of the same Q8 workload."""
+    import numpy as np
+    import synth
+    shp, wl, W = res["shp"], res["wl"], res["W"]
+    orc = oracle.Model(W, n_seq=1)
+    for l in range(shp.n_layers):
+        k, v = synth.kv_fill(wl.seed, 0, l, shp.n_kv_heads, wl.kv_prefill, shp.head_dim)
+        orc.kv_write(0, l, 0, k, v)
+    orc.set_len(0, wl.kv_prefill)
+    tok = int(synth.tokens(wl.seed, 1, 1, shp.vocab)[0])
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        rc, tok, _, _ = orc.step(0, tok, want_logits=False)
+        assert rc == 0
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    orc.close()
+    return {"value": round(n / dt, 4), "unit": "tok/s", "cores": oracle.get_threads(), "kind": "oracle",
+            "sample": f"{n} greedy decode tokens of the same 28-layer Q8 workload from KV context "
+                      f"{wl.kv_prefill} (strict f32, token by token), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--kernel-reps", type=int, default=56)
+    ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle decode (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the sequence-parallel "
+              "multi-GPU layout is described, not run.", file=sys.stderr)
+        sys.exit(2)
+    if args.warmup < 1 or args.steps < 1:
+        sys.exit("--warmup and --steps must be >= 1")
+
+    import torch
+
+    import synth
+    import transformer_qwen3_block_amd as q
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    q.lib()  # fail loudly when the native library is missing
+
+    side = torch.cuda.Stream(device="cuda:0")
+    with torch.cuda.stream(side):
+        res = run_decode(args, torch, q, synth)
+    pre = None
+    if not args.no_prefill:
+        try:
+            with torch.cuda.stream(side):
+                pre = run_prefill(args, torch, q, synth)
+            log(f"prefill 2048: {pre['ms']:.3f} ms, {pre['tok_s']:.0f} tok/s, {pre['tflops']:.1f} TFLOP/s")
+        except q.Qw3Error as e:
+            log(f"prefill unavailable: {e}")
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+        cpu = cpu_baseline(res, oracle, args.cpu_budget)
+        log(f"oracle: {cpu['value']} tok/s on {cpu['cores']} threads")
+
+    ms = res["ms"]
+    tok_s = 1e3 / ms
+    dom = res["dominant"]
+    dk = res["kernels"][dom]
+    out = {
+        "metric": "decode tok/s + achieved HBM GB/s (0.6B-shape, B=1, Q8); prefill tok/s",
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "28-layer Qwen3-0.6B-shape decode, batch 1, Q8 block-32 weights (int8 + f32 scale), "
+                               "KV context 2048 (bf16)",
+                   "hidden": 1024, "layers": 28, "q_heads": 16, "kv_heads": 8, "head_dim": 128, "mlp": 3072,
+                   "vocab": 151936, "kv_context_start": res["wl"].kv_prefill},
+        "hbm_GBps": round(res["step_bytes"] / ms / 1e6, 1),
+        "step_bytes": res["step_bytes"],
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dk["GBps"] / HBM_PEAK_GBS, 4), "traffic": None},
+        "kernels": res["kernels"],
+        "cpu_baseline": cpu,
+    }
+    if pre is not None:
+        out["prefill"] = {"workload": "28-layer Qwen3-0.6B-shape bf16 prefill of 2048 tokens, batch 1",
+                          "tok_s": round(pre["tok_s"], 1), "ms": round(pre["ms"], 4),
+                          "TFLOPs": round(pre["tflops"], 2), "flop": pre["flops"],
+                          "frac_bf16_mfma_peak": round(pre["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -163,3 +163,37 @@ def test_single_block_decode_hidden_states():
         rc, _, _, ref = orc.step(0, hidden_in=hin[t], want_hidden=True)
         assert rc == 0
         assert_close(out.cpu().numpy()[0], ref, f"position {t}")
+
+
+def test_graph_replay_matches_eager_bitwise():
+    """Decode steps replayed from a captured HIP graph (side stream) equal eager launches (null stream) bit
+    for bit, over several replays with host work and synchronisations between them."""
+    torch = _torch()
+    import os
+    shp = replace(SMALL, fmt=synth.FMT_Q8, max_ctx=64)
+    W = synth.make_weights(shp, seed=28)
+    os.environ["QW3_NO_GRAPH"] = "1"
+    try:
+        eager = build_gpu_model(W)
+    finally:
+        del os.environ["QW3_NO_GRAPH"]
+    graphed = build_gpu_model(W)
+    side = torch.cuda.Stream()
+    tok0 = torch.tensor(synth.tokens(28, 1, 1, shp.vocab), dtype=torch.int32, device="cuda")
+    am_e = torch.empty(1, dtype=torch.int32, device="cuda")
+    am_g = torch.empty(1, dtype=torch.int32, device="cuda")
+    lg_e = torch.empty((1, shp.vocab), dtype=torch.float32, device="cuda")
+    lg_g = torch.empty((1, shp.vocab), dtype=torch.float32, device="cuda")
+    cur_e, cur_g = tok0.clone(), tok0.clone()
+    for step in range(6):
+        eager.decode_step(cur_e, am_e, lg_e)
+        with torch.cuda.stream(side):
+            graphed.decode_step(cur_g, am_g, lg_g)
+        side.synchronize()
+        torch.cuda.synchronize()
+        assert np.array_equal(lg_e.cpu().numpy().view(np.uint32), lg_g.cpu().numpy().view(np.uint32)), step
+        assert int(am_e.item()) == int(am_g.item())
+        cur_e.copy_(am_e)
+        cur_g.copy_(am_g)
+        torch.cuda.synchronize()
+    assert graphed.get_len(0) == 6 and graphed.status() == 0

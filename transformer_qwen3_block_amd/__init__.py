@@ -74,7 +74,7 @@ class Tensor(ctypes.Structure):
 
 EXPORTS = ["qw3_abi_version", "qw3_preflight", "qw3_create", "qw3_load_weights", "qw3_prefill", "qw3_decode_step",
            "qw3_reset_kv", "qw3_status_poll", "qw3_get_len", "qw3_destroy", "qw3_block_forward", "qw3_kv_write",
-           "qw3_kv_read", "qw3_set_len", "qw3_dequant"]
+           "qw3_kv_read", "qw3_set_len", "qw3_dequant", "qw3_bench_kernel"]
 
 _lib = None
 
@@ -103,6 +103,7 @@ def lib():
             "qw3_kv_read": (I32, [U64, I32, I32, I32, I32, P, P, V]),
             "qw3_set_len": (I32, [U64, I32, I32, V]),
             "qw3_dequant": (I32, [U64, I32, I32, P, V]),
+            "qw3_bench_kernel": (I32, [U64, I32, I32, V]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -221,6 +222,9 @@ class Model:
         out = torch.empty((rows, cols), dtype=torch.float32, device=self.device)
         check(lib().qw3_dequant(self.handle, KIND[kind], layer, _ptr(out), _stream(stream)), "qw3_dequant")
         return out
+
+    def bench_kernel(self, kernel, layer=0, stream=None):
+        check(lib().qw3_bench_kernel(self.handle, kernel, layer, _stream(stream)), "qw3_bench_kernel")
 
     def close(self):
         if getattr(self, "handle", None) and _lib is not None:

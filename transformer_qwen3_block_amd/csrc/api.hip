@@ -6,6 +6,7 @@
 //   [P2] "M1 — Load the weights"
 //   [P4] "Portable WebAssembly Runtime Architecture for TinyRustLM"
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -44,6 +45,16 @@ struct Model {
     bool poisoned = false;      // a numerical failure was observed by qw3_status_poll
     bool lens_dirty = false;    // host lengths changed without a device update yet
     bool status_dirty = false;  // device status word must be cleared
+    // Replayable decode steps: one captured graph per (tokens, logits, argmax) pointer triple.
+    struct StepGraph {
+        const void *tokens, *logits, *argmax;
+        hipGraphExec_t exec;
+    };
+    std::vector<StepGraph> graphs;
+    bool graphs_enabled = true;
+    ~Model() {
+        for (auto &g : graphs) hipGraphExecDestroy(g.exec);
+    }
 };
 
 constexpr int kSlots = 64;
@@ -296,6 +307,8 @@ int32_t qw3_create(const qw3_config_t *cfg, void *arena_dev, uint64_t arena_byte
     m->arena = (uint8_t *)arena_dev;
     m->arena_bytes = arena_bytes;
     m->len.assign(d.S, 0);
+    const char *ng = getenv("QW3_NO_GRAPH");
+    m->graphs_enabled = !(ng && ng[0] == '1');
     std::lock_guard<std::mutex> lk(g_mu);
     for (int i = 0; i < kSlots; ++i) {
         if (!g_slots[i].m) {
@@ -451,90 +464,98 @@ int32_t qw3_status_poll(uint64_t h, void *stream) {
 //   -> gemv(RMSNorm -> W_gate/W_up, SwiGLU) -> gemv(W_down) + residual
 // then the final RMSNorm + tied logits + argmax + commit ([P1] section 2 item 7).
 // ---------------------------------------------------------------------------------------------------
-static int32_t run_layers_decode(Model *m, int seq0, int S, hipStream_t st) {
+enum DecodeKernel { DK_QKV = 1, DK_ATTN = 2, DK_O = 3, DK_GATEUP = 4, DK_DOWN = 5 };
+
+// Launches one kernel of layer l's decode sequence for sequences seq0..seq0+S-1.
+static int32_t launch_decode_kernel(Model *m, int which, int l, int seq0, int S, hipStream_t st) {
     const Dims &d = m->d;
     const Layout &L = m->lay;
     float *x = at<float>(m, L.x);
     float *qkv = at<float>(m, L.qkv);
     float *attn = at<float>(m, L.attn);
     float *act = at<float>(m, L.act);
-    const long long seq_stride = (long long)d.L * d.HKV * d.max_ctx * kHeadDim;
-    int n_split = kMaxSplit / S;
-    if (n_split < 1) n_split = 1;
-    for (int l = 0; l < d.L; ++l) {
-        const uint64_t b = L.layer0 + (uint64_t)l * L.layer_stride;
-        GemvArgs g{};
-        g.S = S;
-        g.eps = d.eps;
-        // Q/K/V projections with the pre-attention RMSNorm fused in
-        g.w = m->arena + b + L.l_wqkv;
-        g.scales = d.q8 ? at<float>(m, b + L.l_sqkv) : nullptr;
-        g.N = d.Nqkv;
-        g.K = d.H;
-        g.x = x;
-        g.ldx = d.H;
-        g.norm_w = at<float>(m, b + L.l_attn_norm);
-        g.y = qkv;
-        g.ldy = d.Nqkv;
-        QW3_HIP(launch_gemv(d.q8, EPI_STORE, g, st));
-        // attention
-        AttnDecodeArgs a{};
-        a.qkv = qkv;
-        a.ldqkv = d.Nqkv;
-        a.q_norm = at<float>(m, b + L.l_q_norm);
-        a.k_norm = at<float>(m, b + L.l_k_norm);
-        a.rope_cos = at<float>(m, L.rope_cos);
-        a.rope_sin = at<float>(m, L.rope_sin);
-        const size_t layer_off = (size_t)seq0 * seq_stride + (size_t)l * d.HKV * d.max_ctx * kHeadDim;
-        a.kcache = at<uint16_t>(m, L.kcache) + layer_off;
-        a.vcache = at<uint16_t>(m, L.vcache) + layer_off;
-        a.seq_stride = seq_stride;
-        a.max_ctx = d.max_ctx;
-        a.HQ = d.HQ;
-        a.HKV = d.HKV;
-        a.S = S;
-        a.n_split = n_split;
-        a.len = at<int>(m, L.len) + seq0;
-        a.part = at<float>(m, L.part);
-        a.counters = at<unsigned>(m, L.att_counters);
-        a.out = attn;
-        a.ldo = d.q_dim;
-        a.eps = d.eps;
-        QW3_HIP(launch_attn_decode(d.G, a, st));
-        // o_proj + residual
-        g.w = m->arena + b + L.l_wo;
-        g.scales = d.q8 ? at<float>(m, b + L.l_so) : nullptr;
-        g.N = d.H;
-        g.K = d.q_dim;
-        g.x = attn;
-        g.ldx = d.q_dim;
-        g.norm_w = nullptr;
-        g.y = x;
-        g.ldy = d.H;
-        QW3_HIP(launch_gemv(d.q8, EPI_RESID, g, st));
-        // RMSNorm + gate/up + SwiGLU
-        g.w = m->arena + b + L.l_wgu;
-        g.scales = d.q8 ? at<float>(m, b + L.l_sgu) : nullptr;
-        g.N = d.I;
-        g.K = d.H;
-        g.x = x;
-        g.ldx = d.H;
-        g.norm_w = at<float>(m, b + L.l_mlp_norm);
-        g.y = act;
-        g.ldy = d.I;
-        QW3_HIP(launch_gemv(d.q8, EPI_SWIGLU, g, st));
-        // down + residual
-        g.w = m->arena + b + L.l_wd;
-        g.scales = d.q8 ? at<float>(m, b + L.l_sd) : nullptr;
-        g.N = d.H;
-        g.K = d.I;
-        g.x = act;
-        g.ldx = d.I;
-        g.norm_w = nullptr;
-        g.y = x;
-        g.ldy = d.H;
-        QW3_HIP(launch_gemv(d.q8, EPI_RESID, g, st));
+    const uint64_t b = L.layer0 + (uint64_t)l * L.layer_stride;
+    GemvArgs g{};
+    g.S = S;
+    g.eps = d.eps;
+    switch (which) {
+        case DK_QKV:  // Q/K/V projections with the pre-attention RMSNorm fused in
+            g.w = m->arena + b + L.l_wqkv;
+            g.scales = d.q8 ? at<float>(m, b + L.l_sqkv) : nullptr;
+            g.N = d.Nqkv;
+            g.K = d.H;
+            g.x = x;
+            g.ldx = d.H;
+            g.norm_w = at<float>(m, b + L.l_attn_norm);
+            g.y = qkv;
+            g.ldy = d.Nqkv;
+            return dev(launch_gemv(d.q8, EPI_STORE, g, st));
+        case DK_ATTN: {
+            const long long seq_stride = (long long)d.L * d.HKV * d.max_ctx * kHeadDim;
+            int n_split = kMaxSplit / S;
+            if (n_split < 1) n_split = 1;
+            AttnDecodeArgs a{};
+            a.qkv = qkv;
+            a.ldqkv = d.Nqkv;
+            a.q_norm = at<float>(m, b + L.l_q_norm);
+            a.k_norm = at<float>(m, b + L.l_k_norm);
+            a.rope_cos = at<float>(m, L.rope_cos);
+            a.rope_sin = at<float>(m, L.rope_sin);
+            const size_t layer_off = (size_t)seq0 * seq_stride + (size_t)l * d.HKV * d.max_ctx * kHeadDim;
+            a.kcache = at<uint16_t>(m, L.kcache) + layer_off;
+            a.vcache = at<uint16_t>(m, L.vcache) + layer_off;
+            a.seq_stride = seq_stride;
+            a.max_ctx = d.max_ctx;
+            a.HQ = d.HQ;
+            a.HKV = d.HKV;
+            a.S = S;
+            a.n_split = n_split;
+            a.len = at<int>(m, L.len) + seq0;
+            a.part = at<float>(m, L.part);
+            a.counters = at<unsigned>(m, L.att_counters);
+            a.out = attn;
+            a.ldo = d.q_dim;
+            a.eps = d.eps;
+            return dev(launch_attn_decode(d.G, a, st));
+        }
+        case DK_O:  // o_proj + residual
+            g.w = m->arena + b + L.l_wo;
+            g.scales = d.q8 ? at<float>(m, b + L.l_so) : nullptr;
+            g.N = d.H;
+            g.K = d.q_dim;
+            g.x = attn;
+            g.ldx = d.q_dim;
+            g.y = x;
+            g.ldy = d.H;
+            return dev(launch_gemv(d.q8, EPI_RESID, g, st));
+        case DK_GATEUP:  // RMSNorm + gate/up + SwiGLU
+            g.w = m->arena + b + L.l_wgu;
+            g.scales = d.q8 ? at<float>(m, b + L.l_sgu) : nullptr;
+            g.N = d.I;
+            g.K = d.H;
+            g.x = x;
+            g.ldx = d.H;
+            g.norm_w = at<float>(m, b + L.l_mlp_norm);
+            g.y = act;
+            g.ldy = d.I;
+            return dev(launch_gemv(d.q8, EPI_SWIGLU, g, st));
+        case DK_DOWN:  // down + residual
+            g.w = m->arena + b + L.l_wd;
+            g.scales = d.q8 ? at<float>(m, b + L.l_sd) : nullptr;
+            g.N = d.H;
+            g.K = d.I;
+            g.x = act;
+            g.ldx = d.I;
+            g.y = x;
+            g.ldy = d.H;
+            return dev(launch_gemv(d.q8, EPI_RESID, g, st));
     }
+    return QW3_INVALID_ARGUMENT;
+}
+
+static int32_t run_layers_decode(Model *m, int seq0, int S, hipStream_t st) {
+    for (int l = 0; l < m->d.L; ++l)
+        for (int k = DK_QKV; k <= DK_DOWN; ++k) QW3_TRY(launch_decode_kernel(m, k, l, seq0, S, st));
     return QW3_OK;
 }
 
@@ -569,6 +590,17 @@ static int32_t check_ready(Model *m) {
     return QW3_OK;
 }
 
+static int32_t enqueue_decode_step(Model *m, const int32_t *tokens_dev, float *logits_dev, int32_t *argmax_dev,
+                                   hipStream_t st) {
+    const Dims &d = m->d;
+    const Layout &L = m->lay;
+    QW3_HIP(launch_embed(d.q8, m->arena + L.embed, d.q8 ? at<float>(m, L.embed_scales) : nullptr, d.H, tokens_dev, d.S,
+                         at<float>(m, L.x), at<int>(m, L.status), d.V, st));
+    QW3_TRY(run_layers_decode(m, 0, d.S, st));
+    return run_logits(m, 0, d.S, at<float>(m, L.x), logits_dev ? logits_dev : at<float>(m, L.logits), argmax_dev, 1,
+                      st);
+}
+
 int32_t qw3_decode_step(uint64_t h, const int32_t *tokens_dev, float *logits_dev, int32_t *argmax_dev, void *stream) {
     Model *m;
     QW3_TRY(lookup(h, &m));
@@ -579,12 +611,36 @@ int32_t qw3_decode_step(uint64_t h, const int32_t *tokens_dev, float *logits_dev
         if (m->len[s] >= d.max_ctx) return QW3_CONTEXT_EXCEEDED;
     hipStream_t st = (hipStream_t)stream;
     QW3_TRY(sync_state(m, st));
-    const Layout &L = m->lay;
-    QW3_HIP(launch_embed(d.q8, m->arena + L.embed, d.q8 ? at<float>(m, L.embed_scales) : nullptr, d.H, tokens_dev, d.S,
-                         at<float>(m, L.x), at<int>(m, L.status), d.V, st));
-    QW3_TRY(run_layers_decode(m, 0, d.S, st));
-    QW3_TRY(run_logits(m, 0, d.S, at<float>(m, L.x), logits_dev ? logits_dev : at<float>(m, L.logits), argmax_dev, 1,
-                       st));
+    // The step reads positions from the device length array, so one captured graph replays any step with
+    // the same buffers.  The legacy null stream cannot be captured: it runs eagerly.
+    hipGraphExec_t exec = nullptr;
+    if (m->graphs_enabled && st != nullptr) {
+        for (auto &g : m->graphs)
+            if (g.tokens == tokens_dev && g.logits == logits_dev && g.argmax == argmax_dev) exec = g.exec;
+        if (!exec) {
+            hipGraph_t graph = nullptr;
+            bool ok = hipStreamBeginCapture(st, hipStreamCaptureModeRelaxed) == hipSuccess;
+            int32_t rc = ok ? enqueue_decode_step(m, tokens_dev, logits_dev, argmax_dev, st) : QW3_OK;
+            if (ok) ok = hipStreamEndCapture(st, &graph) == hipSuccess && rc == QW3_OK;
+            if (ok) ok = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess;
+            if (graph) hipGraphDestroy(graph);
+            if (!ok) {
+                (void)hipGetLastError();
+                exec = nullptr;
+                m->graphs_enabled = false;  // this stream cannot be captured: stay eager
+            } else {
+                if (m->graphs.size() >= 4) {
+                    hipGraphExecDestroy(m->graphs.front().exec);
+                    m->graphs.erase(m->graphs.begin());
+                }
+                m->graphs.push_back({tokens_dev, logits_dev, argmax_dev, exec});
+            }
+        }
+    }
+    if (exec)
+        QW3_HIP(hipGraphLaunch(exec, st));
+    else
+        QW3_TRY(enqueue_decode_step(m, tokens_dev, logits_dev, argmax_dev, st));
     for (int s = 0; s < d.S; ++s) m->len[s] += 1;
     return QW3_OK;
 }
@@ -737,6 +793,23 @@ int32_t qw3_dequant(uint64_t h, int32_t kind, int32_t layer, float *out_dev, voi
     return dev(launch_dequant(d.q8, m->arena + w + (uint64_t)row0 * e.cols * eb,
                               d.q8 ? at<float>(m, s) + (size_t)row0 * (e.cols / 32) : nullptr, e.rows, (int)e.cols,
                               out_dev, (hipStream_t)stream));
+}
+
+int32_t qw3_bench_kernel(uint64_t h, int32_t kernel, int32_t layer, void *stream) {
+    Model *m;
+    QW3_TRY(lookup(h, &m));
+    QW3_TRY(check_ready(m));
+    const Dims &d = m->d;
+    if (layer < 0 || layer >= d.L) return QW3_INVALID_ARGUMENT;
+    for (int s = 0; s < d.S; ++s)
+        if (m->len[s] >= d.max_ctx) return QW3_CONTEXT_EXCEEDED;
+    hipStream_t st = (hipStream_t)stream;
+    QW3_TRY(sync_state(m, st));
+    if (kernel >= DK_QKV && kernel <= DK_DOWN) return launch_decode_kernel(m, kernel, layer, 0, d.S, st);
+    if (kernel == 6 && !d.hidden_mode)
+        return run_logits(m, 0, d.S, at<float>(m, m->lay.x), at<float>(m, m->lay.logits), at<int>(m, m->lay.tokens), 0,
+                          st);
+    return QW3_INVALID_ARGUMENT;
 }
 
 }  // extern "C"

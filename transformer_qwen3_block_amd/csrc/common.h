@@ -62,6 +62,26 @@ __device__ __forceinline__ uint4 load_nt16(const void *p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Cross-workgroup exchange without an L2 writeback: values are stored and loaded as relaxed agent-scope
+// atomics (device-coherent "sc1" accesses), and a writer waits for its stores to complete before it
+// increments the arrival counter.  (A plain __threadfence() writes back the whole L2 of the XCD.)
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until every memory operation this thread issued has completed.
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+// Arrival ticket of a workgroup on `counter`; returns true for the last of `n` arrivals.  Call after
+// __syncthreads() from one thread, once every thread of the workgroup has called wait_memory().
+__device__ __forceinline__ bool arrive_last(unsigned *counter, unsigned n) {
+    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
+}
+__device__ __forceinline__ void reset_counter(unsigned *counter) {
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -37,260 +37,81 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4 &w, float (&o)[8]) {
 // ---------------------------------------------------------------------------------------------------
 // GEMV: y[s][unit] = epilogue( sum_k W[row][k] * xhat[s][k] ) for S input vectors.
 //
-// One wave (64 lanes) owns R output units; the lanes split K in 16-byte slices (8 bf16 or 16 Q8 codes),
-// so every weight row is read once, fully coalesced, and reduced across the wave at the end.  The input
-// vectors (RMS-normalised when norm_w is given, [P1] section 2 items 1 and 6) are staged in LDS in
-// chunks of KC columns.  Q8 slices are dequantised in registers and the per-32 scale is applied to the
-// slice's partial sum.  Each output element is produced by exactly one wave: no float atomics.
+// One wave (64 lanes) owns a group of R output units at a time; the lanes split K in 16-byte slices
+// (8 bf16 or 16 Q8 codes, KS slices per lane per chunk of KC = KS*64*E columns), so every weight row is
+// read once, fully coalesced, and reduced across the wave.  Weight loads never wait for activations: the
+// first group's loads are issued before the input staging, and when the inputs fit in LDS in one chunk a
+// wave walks its groups (grid-stride) with the next group's weights in flight while it computes the
+// current one.  The inputs (RMS-normalised when norm_w is given, [P1] section 2 items 1 and 6) are staged
+// in LDS.  Q8 slices are dequantised in registers and the per-32 scale multiplies the slice's partial sum.
+// Each output element is produced by exactly one wave: no float atomics.
 // ---------------------------------------------------------------------------------------------------
-template <int Q8, int SM, int R, int EPI>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a, int KC) {
+template <int Q8, int NR, int KS>
+__device__ __forceinline__ void gemv_load(const GemvArgs &a, const long long (&row)[NR], bool ok, int k0, int lane,
+                                          uint4 (&wv)[NR][KS], float (&sc)[NR][KS]) {
     constexpr int E = Q8 ? 16 : 8;
-    constexpr int RPU = (EPI == EPI_SWIGLU) ? 2 : 1;
-    constexpr int NR = R * RPU;
-    extern __shared__ float xs[];  // [S][KC]
-    __shared__ float red[4][kMaxSeq];
-    __shared__ float inv_s[kMaxSeq];
-    __shared__ float bv[4][kMaxSeq];
-    __shared__ int bi[4][kMaxSeq];
-    __shared__ int is_last;
-    __shared__ int bad;
-
-    const int S = a.S, K = a.K;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int unit0 = (blockIdx.x * 4 + wave) * R;
-
-    if (a.norm_w) {
-        for (int s = 0; s < S; ++s) {
-            float ss = 0.f;
-            const float *xr = a.x + (size_t)s * a.ldx;
-            for (int k = tid; k < K; k += 256) {
-                float v = xr[k];
-                ss += v * v;
+    const int kblocks = a.K / 32;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            const int kk = k0 + (lane + 64 * t) * E;
+            if (ok) {
+                wv[j][t] = load_nt16((const char *)a.w + (size_t)(row[j] * (long long)a.K + kk) * (Q8 ? 1 : 2));
+                sc[j][t] = Q8 ? a.scales[row[j] * kblocks + (kk >> 5)] : 0.f;
+            } else {
+                wv[j][t] = make_uint4(0, 0, 0, 0);
+                sc[j][t] = 0.f;
             }
-            ss = wave_sum(ss);
-            if (lane == 0) red[wave][s] = ss;
         }
-        __syncthreads();
-        if (tid < S) {
-            float ss = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
-            inv_s[tid] = 1.0f / sqrtf(ss / (float)K + a.eps);
-        }
-        __syncthreads();
     }
+}
 
-    long long row[NR];
-    bool valid[R];
+// Rows of unit group g (SwiGLU: gate row u and up row u + N per unit).  Rows past the end are clamped to
+// the last unit so loads stay in bounds; their results are never stored.
+template <int R, int RPU>
+__device__ __forceinline__ void gemv_rows(const GemvArgs &a, int g, long long (&row)[R * RPU]) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int unit = unit0 + r;
-        valid[r] = unit < a.N;
+        const int unit = min(g * R + r, a.N - 1);
 #pragma unroll
-        for (int u = 0; u < RPU; ++u) row[r * RPU + u] = valid[r] ? (long long)unit + (long long)u * a.N : 0;
+        for (int u = 0; u < RPU; ++u) row[r * RPU + u] = (long long)unit + (long long)u * a.N;
     }
+}
 
-    float acc[NR][SM];
+template <int Q8, int SM, int NR, int KS>
+__device__ __forceinline__ void gemv_dot(const uint4 (&wv)[NR][KS], const float (&sc)[NR][KS], const float *xs, int KC,
+                                         int S, int lane, float (&acc)[NR][SM]) {
+    constexpr int E = Q8 ? 16 : 8;
 #pragma unroll
-    for (int j = 0; j < NR; ++j)
-#pragma unroll
-        for (int s = 0; s < SM; ++s) acc[j][s] = 0.f;
-
-    const int kblocks = K / 32;
-    for (int k0 = 0; k0 < K; k0 += KC) {
-        const int kc = min(KC, K - k0);
-        __syncthreads();
-        for (int s = 0; s < S; ++s) {
-            const float *xr = a.x + (size_t)s * a.ldx + k0;
-            for (int k = tid * 4; k < kc; k += 1024) {
-                float4 v = *(const float4 *)(xr + k);
-                if (a.norm_w) {
-                    const float4 w = *(const float4 *)(a.norm_w + k0 + k);
-                    const float inv = inv_s[s];
-                    v.x = w.x * (v.x * inv);
-                    v.y = w.y * (v.y * inv);
-                    v.z = w.z * (v.z * inv);
-                    v.w = w.w * (v.w * inv);
-                }
-                *(float4 *)(xs + s * KC + k) = v;
-            }
-        }
-        __syncthreads();
-        for (int sl = lane; sl < kc / E; sl += 64) {
-            const int kk = k0 + sl * E;
-            uint4 wv[NR];
-            float sc[NR];
-#pragma unroll
-            for (int j = 0; j < NR; ++j) {
-                if (valid[j / RPU]) {
-                    const char *base = (const char *)a.w + (size_t)(row[j] * (long long)K + kk) * (Q8 ? 1 : 2);
-                    wv[j] = load_nt16(base);
-                    if (Q8) sc[j] = a.scales[row[j] * kblocks + (kk >> 5)];
-                } else {
-                    wv[j] = make_uint4(0, 0, 0, 0);
-                    sc[j] = 0.f;
-                }
-            }
-            float wf[NR][E];
-#pragma unroll
-            for (int j = 0; j < NR; ++j) {
-                if constexpr (Q8) {
-                    unpack_i8x16(wv[j], wf[j]);
-                } else {
-                    unpack_bf16x8(wv[j], wf[j]);
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < SM; ++s) {
-                if (s < S) {
-                    float xv[E];
-                    const float4 *xp = (const float4 *)(xs + s * KC + sl * E);
-#pragma unroll
-                    for (int q = 0; q < E / 4; ++q) {
-                        float4 t = xp[q];
-                        xv[4 * q] = t.x;
-                        xv[4 * q + 1] = t.y;
-                        xv[4 * q + 2] = t.z;
-                        xv[4 * q + 3] = t.w;
-                    }
-#pragma unroll
-                    for (int j = 0; j < NR; ++j) {
-                        if constexpr (Q8) {
-                            float d = 0.f;
-#pragma unroll
-                            for (int e = 0; e < E; ++e) d += wf[j][e] * xv[e];
-                            acc[j][s] += d * sc[j];
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < E; ++e) acc[j][s] += wf[j][e] * xv[e];
-                        }
-                    }
-                }
-            }
-        }
-    }
-
-#pragma unroll
-    for (int j = 0; j < NR; ++j)
-#pragma unroll
-        for (int s = 0; s < SM; ++s) acc[j][s] = wave_sum(acc[j][s]);
-
-    if constexpr (EPI == EPI_LOGITS) {
-        // logits, then the greedy choice: greatest value, lowest index on ties ([P4] "Sampling order");
-        // a non-finite logit latches a numerical failure ([P1] section 4).
-        if (tid == 0) bad = 0;
-        __syncthreads();
-        int my_bad = 0;
+    for (int t = 0; t < KS; ++t) {
+        const int sl = lane + 64 * t;
 #pragma unroll
         for (int s = 0; s < SM; ++s) {
             if (s < S) {
-                float best = -INFINITY;
-                int besti = 0x7fffffff;
+                float xv[E];
+                const float4 *xp = (const float4 *)(xs + s * KC + sl * E);
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    if (valid[r]) {
-                        const float v = acc[r][s];
-                        if (lane == 0) a.y[(size_t)s * a.ldy + unit0 + r] = v;
-                        if (!isfinite(v)) my_bad = 1;
-                        if (v > best) {
-                            best = v;
-                            besti = unit0 + r;
-                        }
-                    }
+                for (int q = 0; q < E / 4; ++q) {
+                    const float4 v = xp[q];
+                    xv[4 * q] = v.x;
+                    xv[4 * q + 1] = v.y;
+                    xv[4 * q + 2] = v.z;
+                    xv[4 * q + 3] = v.w;
                 }
-                if (lane == 0) {
-                    bv[wave][s] = best;
-                    bi[wave][s] = besti;
-                }
-            }
-        }
-        if (lane == 0 && my_bad) bad = 1;
-        __syncthreads();
-        if (tid < S) {
-            float best = -INFINITY;
-            int besti = 0x7fffffff;
-            for (int w = 0; w < 4; ++w) {
-                const float v = bv[w][tid];
-                const int i = bi[w][tid];
-                if (v > best || (v == best && i < besti)) {
-                    best = v;
-                    besti = i;
-                }
-            }
-            float *p = a.argpart + ((size_t)tid * gridDim.x + blockIdx.x) * 2;
-            p[0] = best;
-            p[1] = __int_as_float(besti);
-        }
-        if (tid == 0 && bad) atomicOr(a.status, 1);
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) is_last = (atomicAdd(a.counter, 1u) == gridDim.x - 1);
-        __syncthreads();
-        if (!is_last) return;
-        __threadfence();
-        for (int s = 0; s < S; ++s) {
-            float best = -INFINITY;
-            int besti = 0x7fffffff;
-            for (int b = tid; b < (int)gridDim.x; b += 256) {
-                const float *p = a.argpart + ((size_t)s * gridDim.x + b) * 2;
-                const float v = __builtin_nontemporal_load(p);
-                const int i = __float_as_int(__builtin_nontemporal_load(p + 1));
-                if (v > best || (v == best && i < besti)) {
-                    best = v;
-                    besti = i;
-                }
-            }
-            // wave then block reduction of (value, index)
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const float ov = __shfl_xor(best, o, 64);
-                const int oi = __shfl_xor(besti, o, 64);
-                if (ov > best || (ov == best && oi < besti)) {
-                    best = ov;
-                    besti = oi;
-                }
-            }
-            if (lane == 0) {
-                bv[wave][s] = best;
-                bi[wave][s] = besti;
-            }
-        }
-        __syncthreads();
-        if (tid < S) {
-            float best = -INFINITY;
-            int besti = 0x7fffffff;
-            for (int w = 0; w < 4; ++w) {
-                const float v = bv[w][tid];
-                const int i = bi[w][tid];
-                if (v > best || (v == best && i < besti)) {
-                    best = v;
-                    besti = i;
-                }
-            }
-            // all logits NaN: no index qualifies; report 0 (the status word carries the failure)
-            if (a.argmax_out) a.argmax_out[tid] = besti == 0x7fffffff ? 0 : besti;
-            // commit: the appended positions become valid only now ([P4] "Cancellation")
-            if (a.len) a.len[tid] += a.commit_add;
-        }
-        if (tid == 0) *a.counter = 0u;
-    } else {
-        if (lane == 0) {
+                for (int j = 0; j < NR; ++j) {
+                    float wf[E];
+                    if constexpr (Q8) {
+                        unpack_i8x16(wv[j][t], wf);
+                        float d = 0.f;
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                if (!valid[r]) continue;
-                const int unit = unit0 + r;
-#pragma unroll
-                for (int s = 0; s < SM; ++s) {
-                    if (s >= S) continue;
-                    float *yp = a.y + (size_t)s * a.ldy + unit;
-                    if constexpr (EPI == EPI_STORE) {
-                        *yp = acc[r][s];
-                    } else if constexpr (EPI == EPI_RESID) {
-                        *yp = *yp + acc[r][s];
+                        for (int e = 0; e < E; ++e) d += wf[e] * xv[e];
+                        acc[j][s] += d * sc[j][t];
                     } else {
-                        // SwiGLU, [P1] section 5: (g * sigmoid(g)) * u with sigmoid(g) = 1 / (1 + exp(-g))
-                        const float g = acc[2 * r][s], u = acc[2 * r + 1][s];
-                        const float sig = 1.0f / (1.0f + __expf(-g));
-                        *yp = (g * sig) * u;
+                        unpack_bf16x8(wv[j][t], wf);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) acc[j][s] += wf[e] * xv[e];
                     }
                 }
             }
@@ -298,22 +119,286 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a, int KC) {
     }
 }
 
-template <int Q8, int SM, int EPI>
-hipError_t gemv_dispatch_r(int R, const GemvArgs &a, int KC, size_t lds, hipStream_t st) {
-    const int units_per_block = 4 * R;
-    const int grid = (a.N + units_per_block - 1) / units_per_block;
-    switch (R) {
-        case 1: hipLaunchKernelGGL((gemv_kernel<Q8, SM, 1, EPI>), dim3(grid), dim3(256), lds, st, a, KC); break;
-        case 2: hipLaunchKernelGGL((gemv_kernel<Q8, SM, 2, EPI>), dim3(grid), dim3(256), lds, st, a, KC); break;
-        case 4:
-            if constexpr (SM == 1 || EPI == EPI_LOGITS) {
-                hipLaunchKernelGGL((gemv_kernel<Q8, SM, 4, EPI>), dim3(grid), dim3(256), lds, st, a, KC);
+template <int Q8, int SM, int R, int EPI, int KS>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a, int KC) {
+    constexpr int RPU = (EPI == EPI_SWIGLU) ? 2 : 1;
+    constexpr int NR = R * RPU;
+    extern __shared__ float xs[];  // [S][KC]
+    __shared__ float red[4][kMaxSeq];
+    __shared__ float inv_s[kMaxSeq];
+    __shared__ float bv[4][kMaxSeq];
+    __shared__ int bi[4][kMaxSeq];
+
+    const int S = a.S, K = a.K;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n_groups = (a.N + R - 1) / R;
+    const int gstride = gridDim.x * 4;
+    int g = blockIdx.x * 4 + wave;
+    const bool single = KC >= K;
+
+    long long row[NR];
+    uint4 wv[NR][KS];
+    float sc[NR][KS];
+    gemv_rows<R, RPU>(a, g, row);
+    gemv_load<Q8, NR, KS>(a, row, g < n_groups, 0, lane, wv, sc);
+
+    // running greedy choice of this wave (logits epilogue)
+    float best[SM];
+    int besti[SM];
+    int my_bad = 0;
+#pragma unroll
+    for (int s = 0; s < SM; ++s) {
+        best[s] = -INFINITY;
+        besti[s] = 0x7fffffff;
+    }
+
+    auto epilogue = [&](int grp, float (&acc)[NR][SM]) {
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+#pragma unroll
+            for (int s = 0; s < SM; ++s) acc[j][s] = wave_sum(acc[j][s]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int unit = grp * R + r;
+            if (unit >= a.N) continue;
+#pragma unroll
+            for (int s = 0; s < SM; ++s) {
+                if (s >= S) continue;
+                float *yp = a.y + (size_t)s * a.ldy + unit;
+                if constexpr (EPI == EPI_LOGITS) {
+                    const float v = acc[r][s];
+                    if (lane == 0) *yp = v;
+                    if (!isfinite(v)) my_bad = 1;
+                    if (v > best[s]) {  // units visited in increasing order: ties keep the lowest id
+                        best[s] = v;
+                        besti[s] = unit;
+                    }
+                } else if (lane == 0) {
+                    if constexpr (EPI == EPI_STORE) {
+                        *yp = acc[r][s];
+                    } else if constexpr (EPI == EPI_RESID) {
+                        *yp = *yp + acc[r][s];
+                    } else {
+                        // SwiGLU, [P1] section 5: (g * sigmoid(g)) * u with sigmoid(g) = 1 / (1 + exp(-g))
+                        const float gt = acc[2 * r][s], up = acc[2 * r + 1][s];
+                        const float sig = 1.0f / (1.0f + __expf(-gt));
+                        *yp = (gt * sig) * up;
+                    }
+                }
+            }
+        }
+    };
+
+    if (single) {
+        // stage all inputs once: raw values to LDS while summing squares, then normalise in place
+        for (int s = 0; s < S; ++s) {
+            const float *xr = a.x + (size_t)s * a.ldx;
+            float ss = 0.f;
+            for (int k = tid * 4; k < K; k += 1024) {
+                const float4 v = *(const float4 *)(xr + k);
+                ss += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+                *(float4 *)(xs + s * KC + k) = v;
+            }
+            if (a.norm_w) {
+                ss = wave_sum(ss);
+                if (lane == 0) red[wave][s] = ss;
+            }
+        }
+        if (a.norm_w) {
+            __syncthreads();
+            if (tid < S) {
+                const float ss = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+                inv_s[tid] = 1.0f / sqrtf(ss / (float)K + a.eps);
+            }
+            __syncthreads();
+            for (int s = 0; s < S; ++s) {
+                const float inv = inv_s[s];
+                for (int k = tid * 4; k < K; k += 1024) {
+                    float4 v = *(float4 *)(xs + s * KC + k);
+                    const float4 w = *(const float4 *)(a.norm_w + k);
+                    v.x = w.x * (v.x * inv);
+                    v.y = w.y * (v.y * inv);
+                    v.z = w.z * (v.z * inv);
+                    v.w = w.w * (v.w * inv);
+                    *(float4 *)(xs + s * KC + k) = v;
+                }
+            }
+        }
+        __syncthreads();
+        while (g < n_groups) {
+            const int gn = g + gstride;
+            long long rn[NR];
+            uint4 wn[NR][KS];
+            float sn[NR][KS];
+            gemv_rows<R, RPU>(a, gn, rn);
+            gemv_load<Q8, NR, KS>(a, rn, gn < n_groups, 0, lane, wn, sn);
+            float acc[NR][SM];
+#pragma unroll
+            for (int j = 0; j < NR; ++j)
+#pragma unroll
+                for (int s = 0; s < SM; ++s) acc[j][s] = 0.f;
+            gemv_dot<Q8, SM, NR, KS>(wv, sc, xs, KC, S, lane, acc);
+            epilogue(g, acc);
+#pragma unroll
+            for (int j = 0; j < NR; ++j) {
+                row[j] = rn[j];
+#pragma unroll
+                for (int t = 0; t < KS; ++t) {
+                    wv[j][t] = wn[j][t];
+                    sc[j][t] = sn[j][t];
+                }
+            }
+            g = gn;
+        }
+    } else {
+        // inputs staged in chunks: one unit group per wave (the grid covers every group)
+        if (a.norm_w) {
+            for (int s = 0; s < S; ++s) {
+                float ss = 0.f;
+                const float *xr = a.x + (size_t)s * a.ldx;
+                for (int k = tid; k < K; k += 256) {
+                    const float v = xr[k];
+                    ss += v * v;
+                }
+                ss = wave_sum(ss);
+                if (lane == 0) red[wave][s] = ss;
+            }
+            __syncthreads();
+            if (tid < S) {
+                const float ss = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+                inv_s[tid] = 1.0f / sqrtf(ss / (float)K + a.eps);
+            }
+        }
+        float acc[NR][SM];
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+#pragma unroll
+            for (int s = 0; s < SM; ++s) acc[j][s] = 0.f;
+        for (int k0 = 0; k0 < K; k0 += KC) {
+            if (k0) gemv_load<Q8, NR, KS>(a, row, g < n_groups, k0, lane, wv, sc);
+            const int kc = min(KC, K - k0);
+            __syncthreads();
+            for (int s = 0; s < S; ++s) {
+                const float *xr = a.x + (size_t)s * a.ldx + k0;
+                for (int k = tid * 4; k < kc; k += 1024) {
+                    float4 v = *(const float4 *)(xr + k);
+                    if (a.norm_w) {
+                        const float4 w = *(const float4 *)(a.norm_w + k0 + k);
+                        const float inv = inv_s[s];
+                        v.x = w.x * (v.x * inv);
+                        v.y = w.y * (v.y * inv);
+                        v.z = w.z * (v.z * inv);
+                        v.w = w.w * (v.w * inv);
+                    }
+                    *(float4 *)(xs + s * KC + k) = v;
+                }
+            }
+            __syncthreads();
+            gemv_dot<Q8, SM, NR, KS>(wv, sc, xs, KC, S, lane, acc);
+        }
+        if (g < n_groups) epilogue(g, acc);
+    }
+
+    if constexpr (EPI == EPI_LOGITS) {
+        // per-workgroup greedy partial: greatest value, lowest index on ties ([P4] "Sampling order"); a
+        // non-finite logit latches a numerical failure ([P1] section 4).  The final choice over the
+        // workgroups is made by argmax_finalize_kernel.
+        if (lane == 0) {
+#pragma unroll
+            for (int s = 0; s < SM; ++s) {
+                if (s < S) {
+                    bv[wave][s] = best[s];
+                    bi[wave][s] = besti[s];
+                }
+            }
+        }
+        if (lane == 0 && my_bad) atomicOr(a.status, 1);
+        __syncthreads();
+        if (tid < S) {
+            float b = -INFINITY;
+            int i0 = 0x7fffffff;
+            for (int w = 0; w < 4; ++w) {
+                const float v = bv[w][tid];
+                const int i = bi[w][tid];
+                if (v > b || (v == b && i < i0)) {
+                    b = v;
+                    i0 = i;
+                }
+            }
+            float *p = a.argpart + ((size_t)tid * gridDim.x + blockIdx.x) * 2;
+            p[0] = b;
+            p[1] = __int_as_float(i0);
+        }
+    }
+}
+
+// Final greedy choice over the logits workgroups' partials (fixed order: lowest index wins ties), then the
+// commit of the appended positions ([P4] "Cancellation": positions become valid only after the step).
+__global__ __launch_bounds__(256) void argmax_finalize_kernel(const float *argpart, int nparts, int S, int *argmax_out,
+                                                              int *len, int commit_add) {
+    __shared__ float bv[4];
+    __shared__ int bi[4];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    for (int s = 0; s < S; ++s) {
+        float best = -INFINITY;
+        int besti = 0x7fffffff;
+        for (int b = tid; b < nparts; b += 256) {
+            const float *p = argpart + ((size_t)s * nparts + b) * 2;
+            const float v = p[0];
+            const int i = __float_as_int(p[1]);
+            if (v > best || (v == best && i < besti)) {
+                best = v;
+                besti = i;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float ov = __shfl_xor(best, o, 64);
+            const int oi = __shfl_xor(besti, o, 64);
+            if (ov > best || (ov == best && oi < besti)) {
+                best = ov;
+                besti = oi;
+            }
+        }
+        if (lane == 0) {
+            bv[wave] = best;
+            bi[wave] = besti;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            for (int w = 1; w < 4; ++w)
+                if (bv[w] > bv[0] || (bv[w] == bv[0] && bi[w] < bi[0])) {
+                    bv[0] = bv[w];
+                    bi[0] = bi[w];
+                }
+            // all logits NaN: no index qualifies; report 0 (the status word carries the failure)
+            if (argmax_out) argmax_out[s] = bi[0] == 0x7fffffff ? 0 : bi[0];
+            if (len) len[s] += commit_add;
+        }
+        __syncthreads();
+    }
+}
+
+template <int Q8, int SM, int R, int EPI>
+hipError_t gemv_launch_ks(int KS, int grid, const GemvArgs &a, int KC, size_t lds, hipStream_t st) {
+    switch (KS) {
+        case 1: hipLaunchKernelGGL((gemv_kernel<Q8, SM, R, EPI, 1>), dim3(grid), dim3(256), lds, st, a, KC); break;
+        case 2: hipLaunchKernelGGL((gemv_kernel<Q8, SM, R, EPI, 2>), dim3(grid), dim3(256), lds, st, a, KC); break;
+        case 3:
+            if constexpr (SM == 1) {
+                hipLaunchKernelGGL((gemv_kernel<Q8, SM, R, EPI, 3>), dim3(grid), dim3(256), lds, st, a, KC);
                 break;
             }
             return hipErrorInvalidValue;
-        case 8:
-            if constexpr (SM == 1 && EPI != EPI_SWIGLU) {
-                hipLaunchKernelGGL((gemv_kernel<Q8, SM, 8, EPI>), dim3(grid), dim3(256), lds, st, a, KC);
+        case 4:
+            if constexpr (SM == 1 && R <= 2) {
+                hipLaunchKernelGGL((gemv_kernel<Q8, SM, R, EPI, 4>), dim3(grid), dim3(256), lds, st, a, KC);
+                break;
+            }
+            return hipErrorInvalidValue;
+        case 6:
+            if constexpr (SM == 1 && R <= 2 && !Q8) {
+                hipLaunchKernelGGL((gemv_kernel<Q8, SM, R, EPI, 6>), dim3(grid), dim3(256), lds, st, a, KC);
                 break;
             }
             return hipErrorInvalidValue;
@@ -322,35 +407,57 @@ hipError_t gemv_dispatch_r(int R, const GemvArgs &a, int KC, size_t lds, hipStre
     return hipGetLastError();
 }
 
+template <int Q8, int SM, int EPI>
+hipError_t gemv_launch_r(int R, int KS, int grid, const GemvArgs &a, int KC, size_t lds, hipStream_t st) {
+    switch (R) {
+        case 1:
+            if constexpr (EPI != EPI_LOGITS) return gemv_launch_ks<Q8, SM, 1, EPI>(KS, grid, a, KC, lds, st);
+            break;
+        case 2: return gemv_launch_ks<Q8, SM, 2, EPI>(KS, grid, a, KC, lds, st);
+        case 4:
+            if constexpr (SM == 1 && (EPI == EPI_STORE || EPI == EPI_LOGITS))
+                return gemv_launch_ks<Q8, SM, 4, EPI>(KS, grid, a, KC, lds, st);
+            break;
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int Q8, int EPI>
-hipError_t gemv_dispatch_s(const GemvArgs &a, hipStream_t st) {
-    const int E = Q8 ? 16 : 8;
-    // LDS budget for the staged input vectors: whole K when it fits in 64 KB, else chunks that are
-    // multiples of one wave's slice span (64 * E columns).
-    int KC = a.K;
-    const int budget = 16384;  // floats
-    if (a.S * KC > budget) {
-        KC = (budget / a.S) / (64 * E) * (64 * E);
-        if (KC < 64 * E) KC = 64 * E;
-    }
-    const size_t lds = (size_t)a.S * KC * sizeof(float);
-    // units per wave: as many as keep >= ~2 workgroups per CU
-    int R = 1;
+hipError_t gemv_dispatch(const GemvArgs &a, hipStream_t st) {
+    constexpr int E = Q8 ? 16 : 8;
+    const int slices = a.K / (64 * E);  // 16-byte slices per lane per row over the whole K
+    // Slices per chunk: one vector keeps up to four slices per lane per row in registers (the whole row
+    // span for K <= 4*64*E); several vectors stage at most 64 KB of inputs in LDS per chunk.
+    int KS;
     if (a.S == 1) {
-        const int maxR = (EPI == EPI_SWIGLU) ? 4 : 8;
-        while (R < maxR && (a.N + 8 * R - 1) / (8 * R) >= 512) R *= 2;
-        if (EPI == EPI_LOGITS) {
-            while (R < maxR && (a.N + 4 * R - 1) / (4 * R) > kLmMaxBlocks) R *= 2;
-            if ((a.N + 4 * R - 1) / (4 * R) > kLmMaxBlocks) return hipErrorInvalidValue;
-        }
-        return gemv_dispatch_r<Q8, 1, EPI>(R, a, KC, lds, st);
+        KS = (slices <= 4 || (!Q8 && slices == 6)) ? slices
+                                                  : (slices % 4 == 0 ? 4 : slices % 3 == 0 ? 3 : slices % 2 == 0 ? 2 : 1);
+    } else {
+        KS = slices % 2 == 0 ? 2 : 1;
+        while (KS > 1 && (size_t)a.S * KS * 64 * E > 16384) KS /= 2;
     }
-    if (EPI != EPI_SWIGLU && (a.N + 7) / 8 >= 256) R = 2;
-    if (EPI == EPI_LOGITS) {
-        while (R < 4 && (a.N + 4 * R - 1) / (4 * R) > kLmMaxBlocks) R *= 2;
-        if ((a.N + 4 * R - 1) / (4 * R) > kLmMaxBlocks) return hipErrorInvalidValue;
+    int R;
+    if (a.S == 1) {
+        R = EPI == EPI_LOGITS ? 4 : EPI == EPI_STORE ? 2 : 1;
+        if (EPI == EPI_STORE && (a.N + 2 * 4 - 1) / (2 * 4) < 256) R = 1;
+    } else {
+        R = (EPI == EPI_LOGITS || (EPI != EPI_SWIGLU && (a.N + 7) / 8 >= 256)) ? 2 : 1;
     }
-    return gemv_dispatch_r<Q8, kMaxSeq, EPI>(R, a, KC, lds, st);
+    while (KS >= 4 && R > 2) R /= 2;
+    if (EPI == EPI_LOGITS && R < 2) R = 2;
+    const int KC = KS * 64 * E;
+    const bool single = KC >= a.K;
+    const size_t lds = (size_t)a.S * KC * sizeof(float);
+    const int n_groups = (a.N + R - 1) / R;
+    int grid = (n_groups + 3) / 4;
+    if (single && EPI == EPI_LOGITS && grid > 1024) grid = 1024;  // waves walk several groups
+    if (EPI == EPI_LOGITS && grid > kLmMaxBlocks) return hipErrorInvalidValue;
+    hipError_t e = a.S == 1 ? gemv_launch_r<Q8, 1, EPI>(R, KS, grid, a, KC, lds, st)
+                            : gemv_launch_r<Q8, kMaxSeq, EPI>(R, KS, grid, a, KC, lds, st);
+    if (e != hipSuccess || EPI != EPI_LOGITS) return e;
+    hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(256), 0, st, a.argpart, grid, a.S, a.argmax_out, a.len,
+                       a.commit_add);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -366,12 +473,24 @@ hipError_t gemv_dispatch_s(const GemvArgs &a, hipStream_t st) {
 // and written as the split's partial; the last workgroup to finish a (seq, kv head) merges the splits in
 // split order, so the result does not depend on completion order.
 // ---------------------------------------------------------------------------------------------------
+// K/V of the newly appended position as 8 packed bf16 pairs (the LDS copy holds the bf16 bits per dim).
+__device__ __forceinline__ void new_kv_from_lds(const float *knew, const float *vnew, int dsub, uint4 &k, uint4 &v) {
+    uint32_t kw[4], vw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        kw[q] = __float_as_uint(knew[dsub + 2 * q]) | (__float_as_uint(knew[dsub + 2 * q + 1]) << 16);
+        vw[q] = __float_as_uint(vnew[dsub + 2 * q]) | (__float_as_uint(vnew[dsub + 2 * q + 1]) << 16);
+    }
+    k = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+    v = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+}
+
 template <int G>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     __shared__ float qs[G][kHeadDim];
-    __shared__ float knew[kHeadDim];
+    __shared__ float knew[kHeadDim], vnew[kHeadDim];
     __shared__ float red[4];
     __shared__ float wm[4][G], wl[4][G];
     __shared__ float wacc[4][G][kHeadDim];
@@ -383,6 +502,30 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     chunk = (chunk + 15) & ~15;
     const int start = split * chunk;
     const int end = min(n, start + chunk);
+    const size_t head_off = (size_t)s * a.seq_stride + (size_t)kvh * a.max_ctx * kHeadDim;
+    const uint16_t *kb = a.kcache + head_off;
+    const uint16_t *vb = a.vcache + head_off;
+    const int dsub = (lane & 15) * 8;
+    const int prow = lane >> 4;
+
+    // K/V of this wave's first 16-position group, issued before the query prologue.  The new position is
+    // excluded here: it is written below and read in the loop after the append.
+    uint4 kr[4], vr[4];
+    bool val[4];
+    int j0 = start + 16 * wave;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = j0 + 4 * i + prow;
+        val[i] = p < end;
+        if (val[i] && p != pos) {
+            kr[i] = load_nt16(kb + (size_t)p * kHeadDim + dsub);
+            vr[i] = load_nt16(vb + (size_t)p * kHeadDim + dsub);
+        } else {
+            kr[i] = make_uint4(0, 0, 0, 0);
+            vr[i] = make_uint4(0, 0, 0, 0);
+        }
+    }
+
     const float *qkv = a.qkv + (size_t)s * a.ldqkv;
     const float *cosr = a.rope_cos + (size_t)pos * (kHeadDim / 2);
     const float *sinr = a.rope_sin + (size_t)pos * (kHeadDim / 2);
@@ -412,12 +555,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
         __syncthreads();
     }
 
-    const size_t head_off = (size_t)s * a.seq_stride + (size_t)kvh * a.max_ctx * kHeadDim;
-    const uint16_t *kb = a.kcache + head_off;
-    const uint16_t *vb = a.vcache + head_off;
-
     // ---- append the new key/value (only the workgroup whose split holds the new position)
-    if (pos >= start && pos < end) {
+    const bool owner = pos >= start && pos < end;
+    if (owner) {
         const int d = tid & 127;
         const bool is_k = tid < 128;
         const float v = is_k ? qkv[q_dim + kvh * kHeadDim + d] : qkv[q_dim + (a.HKV + kvh) * kHeadDim + d];
@@ -436,15 +576,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
             const float x1 = knew[i], x2 = knew[i + 64];
             out = d < 64 ? x1 * c - x2 * sn : x2 * c + x1 * sn;
         }
-        uint16_t *dst = (uint16_t *)(is_k ? kb : vb) + (size_t)pos * kHeadDim + d;
-        *dst = f32_to_bf16(out);
-        __threadfence();
+        const uint16_t b = f32_to_bf16(out);
+        *((uint16_t *)(is_k ? kb : vb) + (size_t)pos * kHeadDim + d) = b;
+        __syncthreads();  // every lane has read knew for its rotation
+        (is_k ? knew : vnew)[d] = __uint_as_float((uint32_t)b);
         __syncthreads();
+        // the new position is taken from LDS (its global store may still be in flight)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (j0 + 4 * i + prow == pos) new_kv_from_lds(knew, vnew, dsub, kr[i], vr[i]);
     }
 
     // ---- stream this split's positions
-    const int dsub = (lane & 15) * 8;
-    const int prow = lane >> 4;
     float qr[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -460,21 +603,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     }
 
-    for (int j0 = start + 16 * wave; j0 < end; j0 += 64) {
-        uint4 kr[4], vr[4];
-        bool val[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = j0 + 4 * i + prow;
-            val[i] = p < end;
-            if (val[i]) {
-                kr[i] = load_nt16(kb + (size_t)p * kHeadDim + dsub);
-                vr[i] = load_nt16(vb + (size_t)p * kHeadDim + dsub);
-            } else {
-                kr[i] = make_uint4(0, 0, 0, 0);
-                vr[i] = make_uint4(0, 0, 0, 0);
-            }
-        }
+    while (j0 < end) {
         float sc[G][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -492,6 +621,25 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
                 sc[h][i] = val[i] ? d * sl2 : -INFINITY;
             }
         }
+        float vf[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) unpack_bf16x8(vr[i], vf[i]);
+        // next group's loads go out before this group's softmax and V accumulation
+        j0 += 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = j0 + 4 * i + prow;
+            val[i] = p < end;
+            if (val[i] && p != pos) {
+                kr[i] = load_nt16(kb + (size_t)p * kHeadDim + dsub);
+                vr[i] = load_nt16(vb + (size_t)p * kHeadDim + dsub);
+            } else if (val[i]) {
+                new_kv_from_lds(knew, vnew, dsub, kr[i], vr[i]);
+            } else {
+                kr[i] = make_uint4(0, 0, 0, 0);
+                vr[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float tm = fmaxf(fmaxf(sc[h][0], sc[h][1]), fmaxf(sc[h][2], sc[h][3]));
@@ -503,17 +651,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
             m[h] = mn;
-        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float vf[8];
-            unpack_bf16x8(vr[i], vf);
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float p = exp2f(sc[h][i] - m[h]);
+            for (int i = 0; i < 4; ++i) {
+                const float p = exp2f(sc[h][i] - mn);
                 l[h] += p;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] += p * vf[e];
+                for (int e = 0; e < 8; ++e) acc[h][e] += p * vf[i][e];
             }
         }
     }
@@ -554,32 +697,51 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
         }
         float *p = a.part + (((size_t)s * a.HQ + kvh * G + h) * kMaxSplit + split) * kPartStride;
         if (d == 0) {
-            p[0] = M;
-            p[1] = L;
+            store_coherent(p, M);
+            store_coherent(p + 1, L);
         }
-        p[2 + d] = O;
+        store_coherent(p + 2 + d, O);
     }
-    __threadfence();
+    wait_memory();
     __syncthreads();
-    if (tid == 0) is_last = (atomicAdd(a.counters + s * a.HKV + kvh, 1u) == gridDim.x - 1);
+    if (tid == 0) is_last = arrive_last(a.counters + s * a.HKV + kvh, gridDim.x);
     __syncthreads();
     if (!is_last) return;
-    __threadfence();
-    for (int t = tid; t < G * kHeadDim; t += 256) {
+    // ---- last workgroup of this (seq, kv head): merge the splits in split order.  Every load of the merge
+    // (running max, running sum and the output slice of each split) is issued in one round.
+    __shared__ float fw[G][kMaxSplit], lw[G][kMaxSplit];
+    static_assert(kMaxSplit == 64, "one split per lane of a wave");
+    const float *pbase = a.part + (((size_t)s * a.HQ + kvh * G) * kMaxSplit) * kPartStride;
+    float ov[G > 2 ? 2 : 1][kMaxSplit];
+    for (int t = tid, k = 0; t < G * kHeadDim; t += 256, ++k) {
         const int h = t >> 7, d = t & 127;
-        const float *p0 = a.part + (((size_t)s * a.HQ + kvh * G + h) * kMaxSplit) * kPartStride;
-        float M = -INFINITY;
-        for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, __builtin_nontemporal_load(p0 + sp * kPartStride));
-        float L = 0.f, O = 0.f;
-        for (int sp = 0; sp < a.n_split; ++sp) {
-            const float *p = p0 + sp * kPartStride;
-            const float f = exp2f(__builtin_nontemporal_load(p) - M);
-            L += f * __builtin_nontemporal_load(p + 1);
-            O += f * __builtin_nontemporal_load(p + 2 + d);
-        }
-        a.out[(size_t)s * a.ldo + (kvh * G + h) * kHeadDim + d] = O / L;
+        const float *p0 = pbase + (size_t)h * kMaxSplit * kPartStride + 2 + d;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplit; ++sp) ov[k][sp] = sp < a.n_split ? load_coherent(p0 + sp * kPartStride) : 0.f;
     }
-    if (tid == 0) a.counters[s * a.HKV + kvh] = 0u;
+    for (int t = tid; t < G * kMaxSplit; t += 256) {
+        const int h = t / kMaxSplit, sp = t % kMaxSplit;
+        const float *p = pbase + ((size_t)h * kMaxSplit + sp) * kPartStride;
+        fw[h][sp] = sp < a.n_split ? load_coherent(p) : -INFINITY;
+        lw[h][sp] = sp < a.n_split ? load_coherent(p + 1) : 0.f;
+    }
+    __syncthreads();
+    if (wave < G) {  // one wave per head, one split per lane
+        const float mv = fw[wave][lane];
+        const float M = wave_max(mv);
+        const float f = mv == -INFINITY ? 0.f : exp2f(mv - M);
+        const float L = wave_sum(f * lw[wave][lane]);
+        fw[wave][lane] = f / L;
+    }
+    __syncthreads();
+    for (int t = tid, k = 0; t < G * kHeadDim; t += 256, ++k) {
+        const int h = t >> 7, d = t & 127;
+        float O = 0.f;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplit; ++sp) O += fw[h][sp] * ov[k][sp];
+        a.out[(size_t)s * a.ldo + (kvh * G + h) * kHeadDim + d] = O;
+    }
+    if (tid == 0) reset_counter(a.counters + s * a.HKV + kvh);
 }
 
 // Embedding: x[s] = row tokens[s] of the table, widened (bf16) or dequantised (code * scale).
@@ -632,12 +794,12 @@ __global__ void dequant_kernel(const void *w, const float *scales, long long tot
 
 hipError_t launch_gemv(bool q8, GemvEpi epi, const GemvArgs &a, hipStream_t st) {
     if (a.S < 1 || a.S > kMaxSeq || a.K % (q8 ? 1024 : 512)) return hipErrorInvalidValue;
-#define QW3_GEMV_EPI(Q)                                                       \
-    switch (epi) {                                                            \
-        case EPI_STORE: return gemv_dispatch_s<Q, EPI_STORE>(a, st);          \
-        case EPI_RESID: return gemv_dispatch_s<Q, EPI_RESID>(a, st);          \
-        case EPI_SWIGLU: return gemv_dispatch_s<Q, EPI_SWIGLU>(a, st);        \
-        case EPI_LOGITS: return gemv_dispatch_s<Q, EPI_LOGITS>(a, st);        \
+#define QW3_GEMV_EPI(Q)                                                     \
+    switch (epi) {                                                          \
+        case EPI_STORE: return gemv_dispatch<Q, EPI_STORE>(a, st);          \
+        case EPI_RESID: return gemv_dispatch<Q, EPI_RESID>(a, st);          \
+        case EPI_SWIGLU: return gemv_dispatch<Q, EPI_SWIGLU>(a, st);        \
+        case EPI_LOGITS: return gemv_dispatch<Q, EPI_LOGITS>(a, st);        \
     }
     if (q8) {
         QW3_GEMV_EPI(1)
