@@ -241,14 +241,15 @@ class Model:
     def __del__(self):
         self.close()
 
-    def step(self, seq=0, tok=-1, hidden_in=None, want_logits=True, want_hidden=False):
-        """Returns (rc, argmax, logits or None, hidden_out or None)."""
+    def step(self, seq=0, tok=-1, hidden_in=None, want_logits=True, want_hidden=False, want_argmax=True):
+        """Returns (rc, argmax, logits or None, hidden_out or None).  With neither logits nor argmax
+        requested the final norm and logits are skipped (a prefill position that is not the last)."""
         hin = f32(hidden_in) if hidden_in is not None else None
         hout = np.empty(self.shape.hidden, np.float32) if want_hidden else None
         lg = np.empty(self.shape.vocab, np.float32) if (want_logits and self.shape.input_mode == 0) else None
         am = ctypes.c_int32(-1)
         rc = lib().orc_step(self.h, seq, int(tok), _p(hin), _p(hout), _p(lg),
-                            ctypes.byref(am) if self.shape.input_mode == 0 else None)
+                            ctypes.byref(am) if (self.shape.input_mode == 0 and want_argmax) else None)
         return rc, am.value, lg, hout
 
     def prefill(self, tokens, seq=0):
@@ -256,7 +257,7 @@ class Model:
         rc, am, lg = ORC_OK, -1, None
         for i, t in enumerate(tokens):
             last = i == len(tokens) - 1
-            rc, am, lg, _ = self.step(seq, int(t), want_logits=last)
+            rc, am, lg, _ = self.step(seq, int(t), want_logits=last, want_argmax=last)
             if rc != ORC_OK:
                 break
         return rc, am, lg

@@ -1,7 +1,498 @@
+// Tiled bf16 prefill on gfx950 MFMA: RMSNorm rows -> bf16, Q/K/V GEMM, QK-Norm + RoPE + KV append, causal
+// GQA flash attention, o_proj GEMM + residual, RMSNorm rows, gate/up GEMM + SwiGLU, down GEMM + residual.
+// Activations enter the MFMA as bf16 with f32 accumulation; the residual stream stays f32.
+//
+// MFMA v_mfma_f32_16x16x32_bf16 lane layout (wave64): lane l supplies A[l%16][8*(l/16)+e] and
+// B[8*(l/16)+e][l%16] (e = 0..7) and receives C[4*(l/16)+r][l%16] (r = 0..3).
+//
+// Page titles used in citations:
+//   [P1] "Scalar-Native Qwen3 Reference Runtime As The Numerical Authority"
+//   [P4] "Portable WebAssembly Runtime Architecture for TinyRustLM"
+#include <math.h>
+
 #include "prefill.h"
 
 namespace qw3 {
-int32_t prefill_layers(uint8_t *, const Layout &, const Dims &, int, int, int, hipStream_t) {
-    return QW3_UNSUPPORTED_SHAPE;
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ f32x4_t mfma16(const uint4 &a, const uint4 &b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
+
+// ---------------------------------------------------------------------------------------------------
+// RMSNorm of T rows ([P1] section 2 items 1 and 6), written as bf16 MFMA operands.
+// ---------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float *x, int H, const float *w, float eps,
+                                                           uint16_t *out) {
+    __shared__ float red[4];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const float *xr = x + (size_t)t * H;
+    float ss = 0.f;
+    for (int k = tid * 4; k < H; k += 1024) {
+        const float4 v = *(const float4 *)(xr + k);
+        ss += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)H + eps);
+    for (int k = tid * 4; k < H; k += 1024) {
+        const float4 v = *(const float4 *)(xr + k);
+        const float4 g = *(const float4 *)(w + k);
+        ushort4 o;
+        o.x = f32_to_bf16(g.x * (v.x * inv));
+        o.y = f32_to_bf16(g.y * (v.y * inv));
+        o.z = f32_to_bf16(g.z * (v.z * inv));
+        o.w = f32_to_bf16(g.w * (v.w * inv));
+        *(ushort4 *)(out + (size_t)t * H + k) = o;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------------
+// C[M, N] = A[M, K] * W[N, K]^T on bf16 MFMA with f32 accumulation.
+// Workgroup tile BM x BN, K in steps of 64 staged through LDS (next step prefetched into registers while
+// the current one is multiplied); WM x WN waves, each owning a (BM/WM) x (BN/WN) block of 16x16 tiles.
+// Epilogues: f32 store, f32 residual add (in place), or SwiGLU into bf16: with GLU, each wave's columns
+// are half gate rows and half the matching up rows (up rows start at W row `up_off`), so gate and up of
+// one output element meet in the same lane.
+// ---------------------------------------------------------------------------------------------------
+enum GemmEpi { G_STORE = 0, G_RESID = 1, G_SWIGLU = 2 };
+
+struct GemmArgs {
+    const uint16_t *A;  // [M][K]
+    const uint16_t *W;  // weight rows [*][K]
+    int M, N, K;        // N = columns of C (SwiGLU: 2 x output columns)
+    int up_off;         // SwiGLU: first up row of W
+    float *outf;        // G_STORE / G_RESID: [M][ldo]
+    uint16_t *out16;    // G_SWIGLU: [M][ldo]
+    int ldo;
+};
+
+constexpr int kBK = 64;
+constexpr int kLdsPad = 8;  // bf16 elements of padding per LDS row
+
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+    static_assert(WM * WN == 4, "four waves");
+    constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+    constexpr int TM = WTM / 16, TN = WTN / 16;
+    constexpr int LDR = kBK + kLdsPad;
+    constexpr int ACH = BM * kBK / 8 / 256;  // 16-byte chunks per thread per A step
+    constexpr int BCH = BN * kBK / 8 / 256;
+    static_assert(ACH >= 1 && BCH >= 1, "tile too small for 256 threads");
+    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDR];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDR];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / WN, wn = wave % WN;
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+
+    // weight row of tile row r
+    auto wrow = [&](int r) -> long long {
+        if constexpr (EPI == G_SWIGLU) {
+            const int wv = r / WTN, q = r % WTN, half = WTN / 2;
+            const int col = n0 / 2 + wv * half + (q % half);
+            return q < half ? (long long)col : (long long)g.up_off + col;
+        } else {
+            return (long long)n0 + r;
+        }
+    };
+
+    uint4 ra[ACH], rb[BCH];
+    auto load_tiles = [&](int k0) {
+#pragma unroll
+        for (int c = 0; c < ACH; ++c) {
+            const int ch = tid + 256 * c, r = ch >> 3, kc = (ch & 7) * 8;
+            const int m = m0 + r;
+            ra[c] = m < g.M ? *(const uint4 *)(g.A + (size_t)m * g.K + k0 + kc) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int c = 0; c < BCH; ++c) {
+            const int ch = tid + 256 * c, r = ch >> 3, kc = (ch & 7) * 8;
+            rb[c] = load_nt16(g.W + (size_t)wrow(r) * g.K + k0 + kc);
+        }
+    };
+    auto store_tiles = [&]() {
+#pragma unroll
+        for (int c = 0; c < ACH; ++c) {
+            const int ch = tid + 256 * c, r = ch >> 3, kc = (ch & 7) * 8;
+            *(uint4 *)(As + r * LDR + kc) = ra[c];
+        }
+#pragma unroll
+        for (int c = 0; c < BCH; ++c) {
+            const int ch = tid + 256 * c, r = ch >> 3, kc = (ch & 7) * 8;
+            *(uint4 *)(Bs + r * LDR + kc) = rb[c];
+        }
+    };
+
+    f32x4_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    load_tiles(0);
+    store_tiles();
+    __syncthreads();
+    const int ksub = 8 * (lane >> 4), lrow = lane & 15;
+    for (int k0 = 0; k0 < g.K; k0 += kBK) {
+        const bool more = k0 + kBK < g.K;
+        if (more) load_tiles(k0 + kBK);
+#pragma unroll
+        for (int kk = 0; kk < kBK; kk += 32) {
+            uint4 af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) af[i] = *(const uint4 *)(As + (wm * WTM + i * 16 + lrow) * LDR + kk + ksub);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) bfr[j] = *(const uint4 *)(Bs + (wn * WTN + j * 16 + lrow) * LDR + kk + ksub);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+        }
+        __syncthreads();
+        if (more) {
+            store_tiles();
+            __syncthreads();
+        }
+    }
+
+    // epilogue: lane holds C[4*(lane/16) + r][lane%16] of each 16x16 tile
+    const int crow = 4 * (lane >> 4), ccol = lane & 15;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = m0 + wm * WTM + i * 16 + crow + r;
+            if (m >= g.M) continue;
+            if constexpr (EPI == G_SWIGLU) {
+#pragma unroll
+                for (int j = 0; j < TN / 2; ++j) {
+                    const int col = n0 / 2 + wn * (WTN / 2) + j * 16 + ccol;
+                    const float gt = acc[i][j][r], up = acc[i][j + TN / 2][r];
+                    // SwiGLU, [P1] section 5: (g * sigmoid(g)) * u
+                    const float sig = 1.0f / (1.0f + __expf(-gt));
+                    g.out16[(size_t)m * g.ldo + col] = f32_to_bf16((gt * sig) * up);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int n = n0 + wn * WTN + j * 16 + ccol;
+                    float *p = g.outf + (size_t)m * g.ldo + n;
+                    if constexpr (EPI == G_STORE)
+                        *p = acc[i][j][r];
+                    else
+                        *p = *p + acc[i][j][r];
+                }
+            }
+        }
+    }
+}
+
+template <int EPI>
+hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
+    if (g.K % kBK || g.N % 128) return hipErrorInvalidValue;
+    const int mt128 = (g.M + 127) / 128;
+    if (g.M <= 64) {
+        // short prompts: weight-streaming bound; many narrow column tiles, all rows in one tile
+        const dim3 grid(g.N / 32, (g.M + 63) / 64);
+        hipLaunchKernelGGL((gemm_bf16_kernel<64, 32, 4, 1, EPI>), grid, dim3(256), 0, st, g);
+    } else if (mt128 * (g.N / 128) < 512) {
+        const dim3 grid(g.N / 64, (g.M + 127) / 128);
+        hipLaunchKernelGGL((gemm_bf16_kernel<128, 64, 2, 2, EPI>), grid, dim3(256), 0, st, g);
+    } else {
+        const dim3 grid(g.N / 128, mt128);
+        hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, EPI>), grid, dim3(256), 0, st, g);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------------
+// QK-Norm + RoPE of every query/key head of T tokens ([P1] section 2 items 3-4) and the KV append
+// ([P1] section 6): query heads go to q16 (bf16, [T][HQ][128]); keys (normalised, rotated) and values are
+// rounded to bf16 into the cache at positions pos0..pos0+T-1.  Grid (T, HQ + HKV), 128 threads.
+// ---------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void qknorm_rope_append_kernel(const float *qkv, int ldqkv, int HQ, int HKV,
+                                                                 const float *q_norm, const float *k_norm,
+                                                                 const float *rope_cos, const float *rope_sin,
+                                                                 int pos0, float eps, uint16_t *q16, uint16_t *kc,
+                                                                 uint16_t *vc, int max_ctx) {
+    __shared__ float red[2];
+    __shared__ float nv[kHeadDim];
+    const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+    const int pos = pos0 + t;
+    const float *row = qkv + (size_t)t * ldqkv;
+    const bool is_q = h < HQ;
+    const int hk = h - HQ;
+    const float v = is_q ? row[h * kHeadDim + d] : row[(HQ + hk) * kHeadDim + d];
+    const float ss = wave_sum(v * v);
+    if ((d & 63) == 0) red[d >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((red[0] + red[1]) / (float)kHeadDim + eps);
+    nv[d] = (is_q ? q_norm[d] : k_norm[d]) * (v * inv);
+    __syncthreads();
+    const int i = d & 63;
+    const float c = rope_cos[(size_t)pos * 64 + i], sn = rope_sin[(size_t)pos * 64 + i];
+    const float x1 = nv[i], x2 = nv[i + 64];
+    const float r = d < 64 ? x1 * c - x2 * sn : x2 * c + x1 * sn;
+    if (is_q) {
+        q16[((size_t)t * HQ + h) * kHeadDim + d] = f32_to_bf16(r);
+    } else {
+        const size_t at = ((size_t)hk * max_ctx + pos) * kHeadDim + d;
+        kc[at] = f32_to_bf16(r);
+        vc[at] = f32_to_bf16(row[(HQ + HKV + hk) * kHeadDim + d]);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Causal GQA flash attention for T queries at positions pos0..pos0+T-1 over cache positions 0..pos0+T-1
+// ([P1] section 2 item 5: query head h reads KV head floor(h / G); keys j <= the query's position).
+//
+// Workgroup = (query block, KV head); its four waves cover the G query heads of that KV head, 16 queries
+// per wave.  Each 64-key tile of K ([key][dim]) and V (transposed to [dim][key]) is staged in LDS once for
+// all waves.  Scores are computed transposed, S^T = K Q^T, so each lane holds four keys of one query
+// (query = lane%16): the row max/sum need only two cross-lane steps, and the probabilities already sit in
+// the B-operand layout of O^T = V^T P^T (the k index of both operands runs over the same key set), so no
+// transpose of P is needed.  Online softmax in log2 units; P enters the MFMA as bf16.
+// ---------------------------------------------------------------------------------------------------
+struct AttnPrefillArgs {
+    const uint16_t *q16;  // [T][HQ][128]
+    const uint16_t *kc, *vc;  // head 0 of (seq, layer): [HKV][max_ctx][128]
+    int T, pos0, HQ, HKV, max_ctx;
+    uint16_t *out16;  // [T][HQ*128]
+};
+
+constexpr int kKT = 64;                  // keys per tile
+constexpr int kKsLd = kHeadDim + 8;      // K tile row stride (bf16)
+constexpr int kVtLd = kKT + 8;           // V^T tile row stride (bf16)
+
+template <int G>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
+    constexpr int WPH = 4 / G;    // waves per query head
+    constexpr int QB = 16 * WPH;  // queries per workgroup
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[kKT * kKsLd];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * kVtLd];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int nqb = (a.T + QB - 1) / QB;
+    const int qb = nqb - 1 - blockIdx.x;  // longest causal rows first
+    const int kvh = blockIdx.y;
+    const int t0 = qb * QB;
+    const int hq = kvh * G + wave / WPH;
+    const int tq = t0 + (wave % WPH) * 16 + (lane & 15);  // this lane's query (C column)
+    const int qpos = a.pos0 + tq;
+    const int t_last = min(a.T - 1, t0 + QB - 1);
+    const int n_keys = a.pos0 + t_last + 1;
+    const int g4 = lane >> 4;
+    const size_t head_off = (size_t)kvh * a.max_ctx * kHeadDim;
+    const uint16_t *kb = a.kc + head_off;
+    const uint16_t *vb = a.vc + head_off;
+
+    // Q^T fragments (B operand of S^T): lane holds Q[tq][32*ks + 8*g4 .. +8]
+    uint4 qf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        qf[ks] = tq < a.T ? *(const uint4 *)(a.q16 + ((size_t)tq * a.HQ + hq) * kHeadDim + 32 * ks + 8 * g4)
+                          : make_uint4(0, 0, 0, 0);
+
+    f32x4_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+    const float sl2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
+
+    for (int k0 = 0; k0 < n_keys; k0 += kKT) {
+        __syncthreads();  // previous tile fully consumed
+        // stage K [64][128] and V^T [128][64]; positions past n_keys are zero
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int ch = tid + 256 * c, key = ch >> 4, dc = (ch & 15) * 8;
+            const int p = k0 + key;
+            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+            if (p < n_keys) {
+                kv = *(const uint4 *)(kb + (size_t)p * kHeadDim + dc);
+                vv = *(const uint4 *)(vb + (size_t)p * kHeadDim + dc);
+            }
+            *(uint4 *)(Ks + key * kKsLd + dc) = kv;
+            const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                Vt[(dc + 2 * q) * kVtLd + key] = (uint16_t)(w[q] & 0xffffu);
+                Vt[(dc + 2 * q + 1) * kVtLd + key] = (uint16_t)(w[q] >> 16);
+            }
+        }
+        __syncthreads();
+
+        // S^T tiles: lane holds scores of keys k0 + 16*kt + 4*g4 + r for its query
+        float sc[4][4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const uint4 kf = *(const uint4 *)(Ks + (16 * kt + (lane & 15)) * kKsLd + 32 * ks + 8 * g4);
+                s = mfma16(kf, qf[ks], s);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int kp = k0 + 16 * kt + 4 * g4 + r;
+                sc[kt][r] = kp <= qpos && kp < n_keys ? s[r] * sl2 : -INFINITY;
+            }
+        }
+        float tm = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tm = fmaxf(tm, sc[kt][r]);
+        tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+        tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+        const float mn = fmaxf(m, tm);
+        const float alpha = exp2f(m - mn);
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] *= alpha;
+        // probabilities as bf16 pairs: P^T fragments for the two 32-key halves of the tile
+        uint32_t pw[2][4];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const int kt0 = 2 * kb2 + (e >> 2), r0 = e & 3;
+                const float p0 = exp2f(sc[kt0][r0] - mn), p1 = exp2f(sc[kt0][r0 + 1] - mn);
+                l += p0 + p1;
+                pw[kb2][e >> 1] = (uint32_t)f32_to_bf16(p0) | ((uint32_t)f32_to_bf16(p1) << 16);
+            }
+        }
+        // O^T += V^T P^T: A = V^T[16 dims][32 keys] with the key set {4*g4 + 0..3, 16 + 4*g4 + 0..3}
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const uint4 pb = make_uint4(pw[kb2][0], pw[kb2][1], pw[kb2][2], pw[kb2][3]);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const uint16_t *vr = Vt + (16 * dt + (lane & 15)) * kVtLd + 32 * kb2 + 4 * g4;
+                const uint2 lo = *(const uint2 *)vr;
+                const uint2 hi = *(const uint2 *)(vr + 16);
+                o[dt] = mfma16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[dt]);
+            }
+        }
+    }
+
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (tq < a.T) {
+        const float inv = 1.0f / l;
+        uint16_t *orow = a.out16 + (size_t)tq * a.HQ * kHeadDim + hq * kHeadDim;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) orow[16 * dt + 4 * g4 + r] = f32_to_bf16(o[dt][r] * inv);
+    }
+}
+
+hipError_t launch_attn_prefill(int G, const AttnPrefillArgs &a, hipStream_t st) {
+    const int QB = 16 * (4 / G);
+    const dim3 grid((a.T + QB - 1) / QB, a.HKV);
+    switch (G) {
+        case 1: hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(256), 0, st, a); break;
+        case 2: hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, dim3(256), 0, st, a); break;
+        case 4: hipLaunchKernelGGL(attn_prefill_kernel<4>, grid, dim3(256), 0, st, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+inline int32_t dev_rc(hipError_t e) { return e == hipSuccess ? QW3_OK : QW3_DEVICE_ERROR; }
+#define QW3_PF_TRY(expr)                                  \
+    do {                                                  \
+        if ((expr) != hipSuccess) return QW3_DEVICE_ERROR; \
+    } while (0)
+
+}  // namespace
+
+// Layer stack of the tiled prefill ([P4] "Prefill versus decode": project Q/K/V for the tile, RoPE and
+// publish K/V, causal attention, output and FFN projections).
+int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, int pos0, int T, hipStream_t st) {
+    if (d.q8 || T < 1 || T > d.max_prefill || pos0 + T > d.max_ctx) return QW3_INVALID_ARGUMENT;
+    float *x = (float *)(arena + L.x);
+    uint16_t *xn16 = (uint16_t *)(arena + L.xn16);
+    float *qkv = (float *)(arena + L.qkv);
+    uint16_t *q16 = (uint16_t *)(arena + L.q16);
+    uint16_t *attn16 = (uint16_t *)(arena + L.attn16);
+    uint16_t *act16 = (uint16_t *)(arena + L.act16);
+    const float *rc = (const float *)(arena + L.rope_cos), *rs = (const float *)(arena + L.rope_sin);
+    const size_t seq_stride = (size_t)d.L * d.HKV * d.max_ctx * kHeadDim;
+    for (int l = 0; l < d.L; ++l) {
+        const uint64_t b = L.layer0 + (uint64_t)l * L.layer_stride;
+        const uint16_t *wqkv = (const uint16_t *)(arena + b + L.l_wqkv);
+        const uint16_t *wo = (const uint16_t *)(arena + b + L.l_wo);
+        const uint16_t *wgu = (const uint16_t *)(arena + b + L.l_wgu);
+        const uint16_t *wd = (const uint16_t *)(arena + b + L.l_wd);
+        const size_t layer_off = (size_t)seq * seq_stride + (size_t)l * d.HKV * d.max_ctx * kHeadDim;
+        uint16_t *kc = (uint16_t *)(arena + L.kcache) + layer_off;
+        uint16_t *vc = (uint16_t *)(arena + L.vcache) + layer_off;
+
+        hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(T), dim3(256), 0, st, x, d.H,
+                           (const float *)(arena + b + L.l_attn_norm), d.eps, xn16);
+        GemmArgs g{};
+        g.A = xn16;
+        g.W = wqkv;
+        g.M = T;
+        g.N = d.Nqkv;
+        g.K = d.H;
+        g.outf = qkv;
+        g.ldo = d.Nqkv;
+        QW3_PF_TRY(launch_gemm<G_STORE>(g, st));
+        hipLaunchKernelGGL(qknorm_rope_append_kernel, dim3(T, d.HQ + d.HKV), dim3(128), 0, st, qkv, d.Nqkv, d.HQ,
+                           d.HKV, (const float *)(arena + b + L.l_q_norm), (const float *)(arena + b + L.l_k_norm), rc,
+                           rs, pos0, d.eps, q16, kc, vc, d.max_ctx);
+        AttnPrefillArgs at{};
+        at.q16 = q16;
+        at.kc = kc;
+        at.vc = vc;
+        at.T = T;
+        at.pos0 = pos0;
+        at.HQ = d.HQ;
+        at.HKV = d.HKV;
+        at.max_ctx = d.max_ctx;
+        at.out16 = attn16;
+        QW3_PF_TRY(launch_attn_prefill(d.G, at, st));
+        g.A = attn16;
+        g.W = wo;
+        g.N = d.H;
+        g.K = d.q_dim;
+        g.outf = x;
+        g.ldo = d.H;
+        QW3_PF_TRY(launch_gemm<G_RESID>(g, st));
+        hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(T), dim3(256), 0, st, x, d.H,
+                           (const float *)(arena + b + L.l_mlp_norm), d.eps, xn16);
+        g.A = xn16;
+        g.W = wgu;
+        g.N = 2 * d.I;
+        g.K = d.H;
+        g.up_off = d.I;
+        g.outf = nullptr;
+        g.out16 = act16;
+        g.ldo = d.I;
+        QW3_PF_TRY(launch_gemm<G_SWIGLU>(g, st));
+        g.A = act16;
+        g.W = wd;
+        g.N = d.H;
+        g.K = d.I;
+        g.out16 = nullptr;
+        g.outf = x;
+        g.ldo = d.H;
+        QW3_PF_TRY(launch_gemm<G_RESID>(g, st));
+    }
+    return dev_rc(hipGetLastError());
+}
+
 }  // namespace qw3
