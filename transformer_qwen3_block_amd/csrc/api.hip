@@ -117,6 +117,7 @@ int32_t validate(const qw3_config_t *c, Dims *d) {
     d->Nqkv = (c->n_q_heads + 2 * c->n_kv_heads) * kHeadDim;
     d->q8 = q8;
     d->hidden_mode = c->input_mode == QW3_INPUT_HIDDEN;
+    d->mfma_prefill = !q8 && c->max_prefill > 1;
     d->eps = c->rms_eps;
     return QW3_OK;
 }
@@ -153,6 +154,12 @@ int32_t plan(const Dims &d, Layout *lay, qw3_sizes_t *sz) {
         L.l_mlp_norm = take(c.mul(d.H, 4));
         L.l_q_norm = take(kHeadDim * 4);
         L.l_k_norm = take(kHeadDim * 4);
+        if (d.mfma_prefill) {
+            L.l_wqkv16 = take(c.mul(c.mul(d.Nqkv, d.H), 2));
+            L.l_wo16 = take(c.mul(c.mul(d.H, d.q_dim), 2));
+            L.l_wgu16 = take(c.mul(c.mul(c.mul(2, d.I), d.H), 2));
+            L.l_wd16 = take(c.mul(c.mul(d.H, d.I), 2));
+        }
         L.layer_stride = off;
         off = save;
     }
@@ -386,6 +393,13 @@ int32_t qw3_load_weights(uint64_t h, const qw3_tensor_t *t, int32_t n, void *str
         QW3_TRY(upload_norm(m, t[sl[QW3_T_MLP_NORM]], b + L.l_mlp_norm, st, keep));
         QW3_TRY(upload_norm(m, t[sl[QW3_T_Q_NORM]], b + L.l_q_norm, st, keep));
         QW3_TRY(upload_norm(m, t[sl[QW3_T_K_NORM]], b + L.l_k_norm, st, keep));
+        if (d.mfma_prefill) {
+            // f16 copies for the MFMA prefill: exact for |w| >= 2^-14, smaller magnitudes keep 2^-24 steps
+            QW3_HIP(launch_bf16_to_f16(m->arena + b + L.l_wqkv, m->arena + b + L.l_wqkv16, (size_t)d.Nqkv * d.H, st));
+            QW3_HIP(launch_bf16_to_f16(m->arena + b + L.l_wo, m->arena + b + L.l_wo16, (size_t)d.H * d.q_dim, st));
+            QW3_HIP(launch_bf16_to_f16(m->arena + b + L.l_wgu, m->arena + b + L.l_wgu16, (size_t)2 * d.I * d.H, st));
+            QW3_HIP(launch_bf16_to_f16(m->arena + b + L.l_wd, m->arena + b + L.l_wd16, (size_t)d.H * d.I, st));
+        }
     }
     // RoPE table: angle pos * theta^(-2i/d) for pair i, cos and sin in double rounded to f32
     // ([P1] section 2 item 4; [P4] recommends packed RoPE tables over platform libm).

@@ -21,6 +21,7 @@ struct Layout {
     uint64_t layer0, layer_stride;
     uint64_t l_wqkv, l_sqkv, l_wo, l_so, l_wgu, l_sgu, l_wd, l_sd;  // relative to the layer block
     uint64_t l_attn_norm, l_mlp_norm, l_q_norm, l_k_norm;           // f32 vectors
+    uint64_t l_wqkv16, l_wo16, l_wgu16, l_wd16;  // f16 copies of the bf16 projections (MFMA prefill), or 0
     uint64_t rope_cos, rope_sin;                                     // f32 [max_ctx][head_dim/2]
     // KV cache, bf16 [seq][layer][kv_head][pos][head_dim]
     uint64_t kcache, vcache;
@@ -38,6 +39,7 @@ struct Dims {
     int q_dim;       // HQ * 128
     bool q8;
     bool hidden_mode;
+    bool mfma_prefill;  // bf16 weights and multi-token tiles: f16 weight copies exist
     float eps;
 };
 

@@ -8,4 +8,7 @@ namespace qw3 {
 // at positions pos0..pos0+T-1, appending their K/V to the cache.  On return x holds the layer-stack output.
 int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, int pos0, int T, hipStream_t st);
 
+// Widens n bf16 values to f16 (round to nearest even; exact unless |v| < 2^-14 or |v| > 65504).
+hipError_t launch_bf16_to_f16(const void *in, void *out, size_t n, hipStream_t st);
+
 }  // namespace qw3

@@ -1,8 +1,12 @@
-// Tiled bf16 prefill on gfx950 MFMA: RMSNorm rows -> bf16, Q/K/V GEMM, QK-Norm + RoPE + KV append, causal
-// GQA flash attention, o_proj GEMM + residual, RMSNorm rows, gate/up GEMM + SwiGLU, down GEMM + residual.
-// Activations enter the MFMA as bf16 with f32 accumulation; the residual stream stays f32.
+// Tiled prefill of bf16-weight models on gfx950 MFMA: RMSNorm rows, Q/K/V GEMM, QK-Norm + RoPE + KV append,
+// causal GQA flash attention, o_proj GEMM + residual, RMSNorm rows, gate/up GEMM + SwiGLU, down GEMM +
+// residual.  MFMA operands are f16 with f32 accumulation: the packer keeps an f16 copy of each bf16
+// projection (bf16 -> f16 is exact for |w| >= 2^-14), activations are rounded to f16 (11-bit significand,
+// eight times finer than bf16), and the bf16 K/V cache is widened to f16 while it is staged in LDS.  The
+// residual stream stays f32.  An activation beyond the f16 range becomes infinite and reaches the logits,
+// where the non-finite check latches a numerical failure.
 //
-// MFMA v_mfma_f32_16x16x32_bf16 lane layout (wave64): lane l supplies A[l%16][8*(l/16)+e] and
+// MFMA v_mfma_f32_16x16x32_f16 lane layout (wave64): lane l supplies A[l%16][8*(l/16)+e] and
 // B[8*(l/16)+e][l%16] (e = 0..7) and receives C[4*(l/16)+r][l%16] (r = 0..3).
 //
 // Page titles used in citations:
@@ -16,19 +20,31 @@ namespace qw3 {
 
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ f16x8_t as_f16x8(const uint4 &v) { return __builtin_bit_cast(f16x8_t, v); }
 
 __device__ __forceinline__ f32x4_t mfma16(const uint4 &a, const uint4 &b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
+}
+
+// f32 -> f16 bits, round to nearest even
+__device__ __forceinline__ uint16_t f32_to_h16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+// bf16 bits -> f16 bits
+__device__ __forceinline__ uint32_t bf16x2_to_h16x2(uint32_t w) {
+    return (uint32_t)f32_to_h16(bf16_lo(w)) | ((uint32_t)f32_to_h16(bf16_hi(w)) << 16);
+}
+
+__global__ void bf16_to_f16_kernel(const uint16_t *in, uint16_t *out, size_t n) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = f32_to_h16(bf16_to_f32(in[i]));
 }
 
 // ---------------------------------------------------------------------------------------------------
-// RMSNorm of T rows ([P1] section 2 items 1 and 6), written as bf16 MFMA operands.
+// RMSNorm of T rows ([P1] section 2 items 1 and 6), written as f16 MFMA operands.
 // ---------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float *x, int H, const float *w, float eps,
                                                            uint16_t *out) {
@@ -48,39 +64,39 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float *x, int H
         const float4 v = *(const float4 *)(xr + k);
         const float4 g = *(const float4 *)(w + k);
         ushort4 o;
-        o.x = f32_to_bf16(g.x * (v.x * inv));
-        o.y = f32_to_bf16(g.y * (v.y * inv));
-        o.z = f32_to_bf16(g.z * (v.z * inv));
-        o.w = f32_to_bf16(g.w * (v.w * inv));
+        o.x = f32_to_h16(g.x * (v.x * inv));
+        o.y = f32_to_h16(g.y * (v.y * inv));
+        o.z = f32_to_h16(g.z * (v.z * inv));
+        o.w = f32_to_h16(g.w * (v.w * inv));
         *(ushort4 *)(out + (size_t)t * H + k) = o;
     }
 }
 
 // ---------------------------------------------------------------------------------------------------
-// C[M, N] = A[M, K] * W[N, K]^T on bf16 MFMA with f32 accumulation.
+// C[M, N] = A[M, K] * W[N, K]^T on f16 MFMA with f32 accumulation.
 // Workgroup tile BM x BN, K in steps of 64 staged through LDS (next step prefetched into registers while
 // the current one is multiplied); WM x WN waves, each owning a (BM/WM) x (BN/WN) block of 16x16 tiles.
-// Epilogues: f32 store, f32 residual add (in place), or SwiGLU into bf16: with GLU, each wave's columns
+// Epilogues: f32 store, f32 residual add (in place), or SwiGLU into f16: with GLU, each wave's columns
 // are half gate rows and half the matching up rows (up rows start at W row `up_off`), so gate and up of
 // one output element meet in the same lane.
 // ---------------------------------------------------------------------------------------------------
 enum GemmEpi { G_STORE = 0, G_RESID = 1, G_SWIGLU = 2 };
 
 struct GemmArgs {
-    const uint16_t *A;  // [M][K]
-    const uint16_t *W;  // weight rows [*][K]
+    const uint16_t *A;  // f16 [M][K]
+    const uint16_t *W;  // f16 weight rows [*][K]
     int M, N, K;        // N = columns of C (SwiGLU: 2 x output columns)
     int up_off;         // SwiGLU: first up row of W
     float *outf;        // G_STORE / G_RESID: [M][ldo]
-    uint16_t *out16;    // G_SWIGLU: [M][ldo]
+    uint16_t *out16;    // G_SWIGLU: f16 [M][ldo]
     int ldo;
 };
 
 constexpr int kBK = 64;
-constexpr int kLdsPad = 8;  // bf16 elements of padding per LDS row
+constexpr int kLdsPad = 8;  // 16-bit elements of padding per LDS row
 
 template <int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs g) {
     static_assert(WM * WN == 4, "four waves");
     constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
     constexpr int TM = WTM / 16, TN = WTN / 16;
@@ -180,7 +196,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
                     const float gt = acc[i][j][r], up = acc[i][j + TN / 2][r];
                     // SwiGLU, [P1] section 5: (g * sigmoid(g)) * u
                     const float sig = 1.0f / (1.0f + __expf(-gt));
-                    g.out16[(size_t)m * g.ldo + col] = f32_to_bf16((gt * sig) * up);
+                    g.out16[(size_t)m * g.ldo + col] = f32_to_h16((gt * sig) * up);
                 }
             } else {
 #pragma unroll
@@ -204,20 +220,20 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
     if (g.M <= 64) {
         // short prompts: weight-streaming bound; many narrow column tiles, all rows in one tile
         const dim3 grid(g.N / 32, (g.M + 63) / 64);
-        hipLaunchKernelGGL((gemm_bf16_kernel<64, 32, 4, 1, EPI>), grid, dim3(256), 0, st, g);
+        hipLaunchKernelGGL((gemm_f16_kernel<64, 32, 4, 1, EPI>), grid, dim3(256), 0, st, g);
     } else if (mt128 * (g.N / 128) < 512) {
         const dim3 grid(g.N / 64, (g.M + 127) / 128);
-        hipLaunchKernelGGL((gemm_bf16_kernel<128, 64, 2, 2, EPI>), grid, dim3(256), 0, st, g);
+        hipLaunchKernelGGL((gemm_f16_kernel<128, 64, 2, 2, EPI>), grid, dim3(256), 0, st, g);
     } else {
         const dim3 grid(g.N / 128, mt128);
-        hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, EPI>), grid, dim3(256), 0, st, g);
+        hipLaunchKernelGGL((gemm_f16_kernel<128, 128, 2, 2, EPI>), grid, dim3(256), 0, st, g);
     }
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------------
 // QK-Norm + RoPE of every query/key head of T tokens ([P1] section 2 items 3-4) and the KV append
-// ([P1] section 6): query heads go to q16 (bf16, [T][HQ][128]); keys (normalised, rotated) and values are
+// ([P1] section 6): query heads go to q16 (f16, [T][HQ][128]); keys (normalised, rotated) and values are
 // rounded to bf16 into the cache at positions pos0..pos0+T-1.  Grid (T, HQ + HKV), 128 threads.
 // ---------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void qknorm_rope_append_kernel(const float *qkv, int ldqkv, int HQ, int HKV,
@@ -244,7 +260,7 @@ __global__ __launch_bounds__(128) void qknorm_rope_append_kernel(const float *qk
     const float x1 = nv[i], x2 = nv[i + 64];
     const float r = d < 64 ? x1 * c - x2 * sn : x2 * c + x1 * sn;
     if (is_q) {
-        q16[((size_t)t * HQ + h) * kHeadDim + d] = f32_to_bf16(r);
+        q16[((size_t)t * HQ + h) * kHeadDim + d] = f32_to_h16(r);
     } else {
         const size_t at = ((size_t)hk * max_ctx + pos) * kHeadDim + d;
         kc[at] = f32_to_bf16(r);
@@ -261,18 +277,18 @@ __global__ __launch_bounds__(128) void qknorm_rope_append_kernel(const float *qk
 // all waves.  Scores are computed transposed, S^T = K Q^T, so each lane holds four keys of one query
 // (query = lane%16): the row max/sum need only two cross-lane steps, and the probabilities already sit in
 // the B-operand layout of O^T = V^T P^T (the k index of both operands runs over the same key set), so no
-// transpose of P is needed.  Online softmax in log2 units; P enters the MFMA as bf16.
+// transpose of P is needed.  Online softmax in log2 units; Q, K, V and P enter the MFMA as f16.
 // ---------------------------------------------------------------------------------------------------
 struct AttnPrefillArgs {
-    const uint16_t *q16;  // [T][HQ][128]
-    const uint16_t *kc, *vc;  // head 0 of (seq, layer): [HKV][max_ctx][128]
+    const uint16_t *q16;      // f16 [T][HQ][128]
+    const uint16_t *kc, *vc;  // bf16 cache, head 0 of (seq, layer): [HKV][max_ctx][128]
     int T, pos0, HQ, HKV, max_ctx;
-    uint16_t *out16;  // [T][HQ*128]
+    uint16_t *out16;          // f16 [T][HQ*128]
 };
 
 constexpr int kKT = 64;                  // keys per tile
-constexpr int kKsLd = kHeadDim + 8;      // K tile row stride (bf16)
-constexpr int kVtLd = kKT + 8;           // V^T tile row stride (bf16)
+constexpr int kKsLd = kHeadDim + 8;      // K tile row stride (f16 elements)
+constexpr int kVtLd = kKT + 8;           // V^T tile row stride (f16 elements)
 
 template <int G>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
@@ -320,6 +336,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
             if (p < n_keys) {
                 kv = *(const uint4 *)(kb + (size_t)p * kHeadDim + dc);
                 vv = *(const uint4 *)(vb + (size_t)p * kHeadDim + dc);
+                kv = make_uint4(bf16x2_to_h16x2(kv.x), bf16x2_to_h16x2(kv.y), bf16x2_to_h16x2(kv.z),
+                                bf16x2_to_h16x2(kv.w));
+                vv = make_uint4(bf16x2_to_h16x2(vv.x), bf16x2_to_h16x2(vv.y), bf16x2_to_h16x2(vv.z),
+                                bf16x2_to_h16x2(vv.w));
             }
             *(uint4 *)(Ks + key * kKsLd + dc) = kv;
             const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
@@ -369,7 +389,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
                 const int kt0 = 2 * kb2 + (e >> 2), r0 = e & 3;
                 const float p0 = exp2f(sc[kt0][r0] - mn), p1 = exp2f(sc[kt0][r0 + 1] - mn);
                 l += p0 + p1;
-                pw[kb2][e >> 1] = (uint32_t)f32_to_bf16(p0) | ((uint32_t)f32_to_bf16(p1) << 16);
+                pw[kb2][e >> 1] = (uint32_t)f32_to_h16(p0) | ((uint32_t)f32_to_h16(p1) << 16);
             }
         }
         // O^T += V^T P^T: A = V^T[16 dims][32 keys] with the key set {4*g4 + 0..3, 16 + 4*g4 + 0..3}
@@ -394,7 +414,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) orow[16 * dt + 4 * g4 + r] = f32_to_bf16(o[dt][r] * inv);
+            for (int r = 0; r < 4; ++r) orow[16 * dt + 4 * g4 + r] = f32_to_h16(o[dt][r] * inv);
     }
 }
 
@@ -418,10 +438,16 @@ inline int32_t dev_rc(hipError_t e) { return e == hipSuccess ? QW3_OK : QW3_DEVI
 
 }  // namespace
 
+hipError_t launch_bf16_to_f16(const void *in, void *out, size_t n, hipStream_t st) {
+    hipLaunchKernelGGL(bf16_to_f16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const uint16_t *)in,
+                       (uint16_t *)out, n);
+    return hipGetLastError();
+}
+
 // Layer stack of the tiled prefill ([P4] "Prefill versus decode": project Q/K/V for the tile, RoPE and
 // publish K/V, causal attention, output and FFN projections).
 int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, int pos0, int T, hipStream_t st) {
-    if (d.q8 || T < 1 || T > d.max_prefill || pos0 + T > d.max_ctx) return QW3_INVALID_ARGUMENT;
+    if (!d.mfma_prefill || T < 1 || T > d.max_prefill || pos0 + T > d.max_ctx) return QW3_INVALID_ARGUMENT;
     float *x = (float *)(arena + L.x);
     uint16_t *xn16 = (uint16_t *)(arena + L.xn16);
     float *qkv = (float *)(arena + L.qkv);
@@ -432,10 +458,10 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
     const size_t seq_stride = (size_t)d.L * d.HKV * d.max_ctx * kHeadDim;
     for (int l = 0; l < d.L; ++l) {
         const uint64_t b = L.layer0 + (uint64_t)l * L.layer_stride;
-        const uint16_t *wqkv = (const uint16_t *)(arena + b + L.l_wqkv);
-        const uint16_t *wo = (const uint16_t *)(arena + b + L.l_wo);
-        const uint16_t *wgu = (const uint16_t *)(arena + b + L.l_wgu);
-        const uint16_t *wd = (const uint16_t *)(arena + b + L.l_wd);
+        const uint16_t *wqkv = (const uint16_t *)(arena + b + L.l_wqkv16);
+        const uint16_t *wo = (const uint16_t *)(arena + b + L.l_wo16);
+        const uint16_t *wgu = (const uint16_t *)(arena + b + L.l_wgu16);
+        const uint16_t *wd = (const uint16_t *)(arena + b + L.l_wd16);
         const size_t layer_off = (size_t)seq * seq_stride + (size_t)l * d.HKV * d.max_ctx * kHeadDim;
         uint16_t *kc = (uint16_t *)(arena + L.kcache) + layer_off;
         uint16_t *vc = (uint16_t *)(arena + L.vcache) + layer_off;
