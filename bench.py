@@ -92,12 +92,10 @@ def run_decode(args, torch, q, synth):
     kernels = {}
     reps = args.kernel_reps
     for name, kid in ids.items():
-        for r in range(3):
-            m.bench_kernel(kid, r % shp.n_layers)
+        m.bench_kernel(kid, 0, 3)
         torch.cuda.synchronize()
         e0.record(stream)
-        for r in range(reps):
-            m.bench_kernel(kid, r % shp.n_layers)
+        m.bench_kernel(kid, 0, reps)   # enqueued back to back from C++, layers cycling
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
@@ -183,6 +181,8 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle decode (0 = skip)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the sequence-parallel "
@@ -201,6 +201,14 @@ def main():
     side = torch.cuda.Stream(device="cuda:0")
     with torch.cuda.stream(side):
         res = run_decode(args, torch, q, synth)
+    if args.copy_probe:
+        with torch.cuda.stream(side):
+            src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
     pre = None
     if not args.no_prefill:
         try:

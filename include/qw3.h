@@ -214,12 +214,12 @@ int32_t qw3_set_len(uint64_t handle, int32_t seq, int32_t len, void *stream);
  * layer) or QW3_T_EMBED; out_dev f32 [rows, cols].  For Q8 each element is one f32 multiply code*scale. */
 int32_t qw3_dequant(uint64_t handle, int32_t kind, int32_t layer, float *out_dev, void *stream);
 
-/* Launches one kernel of the decode step on the current state, for timing: kernel 1 = RMSNorm+QKV GEMV,
- * 2 = attention (re-appends the current position's K/V), 3 = o_proj+residual, 4 = RMSNorm+gate/up+SwiGLU,
- * 5 = down+residual (for `layer`), 6 = final norm + logits + argmax (no commit).  Lengths do not advance;
- * the residual-updating kernels change the scratch hidden state, so a step after this hook is not a
- * continuation of the previous one. */
-int32_t qw3_bench_kernel(uint64_t handle, int32_t kernel, int32_t layer, void *stream);
+/* Launches one kernel of the decode step `reps` times back to back on the current state, for timing:
+ * kernel 1 = RMSNorm+QKV GEMV, 2 = attention (re-appends the current position's K/V), 3 = o_proj+residual,
+ * 4 = RMSNorm+gate/up+SwiGLU, 5 = down+residual (layers layer, layer+1, ... cyclically), 6 = final norm +
+ * logits + argmax (no commit).  Lengths do not advance; the residual-updating kernels change the scratch
+ * hidden state, so a step after this hook is not a continuation of the previous one. */
+int32_t qw3_bench_kernel(uint64_t handle, int32_t kernel, int32_t layer, int32_t reps, void *stream);
 
 #ifdef __cplusplus
 }

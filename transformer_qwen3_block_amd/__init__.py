@@ -103,7 +103,7 @@ def lib():
             "qw3_kv_read": (I32, [U64, I32, I32, I32, I32, P, P, V]),
             "qw3_set_len": (I32, [U64, I32, I32, V]),
             "qw3_dequant": (I32, [U64, I32, I32, P, V]),
-            "qw3_bench_kernel": (I32, [U64, I32, I32, V]),
+            "qw3_bench_kernel": (I32, [U64, I32, I32, I32, V]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -223,8 +223,8 @@ class Model:
         check(lib().qw3_dequant(self.handle, KIND[kind], layer, _ptr(out), _stream(stream)), "qw3_dequant")
         return out
 
-    def bench_kernel(self, kernel, layer=0, stream=None):
-        check(lib().qw3_bench_kernel(self.handle, kernel, layer, _stream(stream)), "qw3_bench_kernel")
+    def bench_kernel(self, kernel, layer=0, reps=1, stream=None):
+        check(lib().qw3_bench_kernel(self.handle, kernel, layer, reps, _stream(stream)), "qw3_bench_kernel")
 
     def close(self):
         if getattr(self, "handle", None) and _lib is not None:

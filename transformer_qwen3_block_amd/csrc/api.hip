@@ -809,21 +809,25 @@ int32_t qw3_dequant(uint64_t h, int32_t kind, int32_t layer, float *out_dev, voi
                               out_dev, (hipStream_t)stream));
 }
 
-int32_t qw3_bench_kernel(uint64_t h, int32_t kernel, int32_t layer, void *stream) {
+int32_t qw3_bench_kernel(uint64_t h, int32_t kernel, int32_t layer, int32_t reps, void *stream) {
     Model *m;
     QW3_TRY(lookup(h, &m));
     QW3_TRY(check_ready(m));
     const Dims &d = m->d;
-    if (layer < 0 || layer >= d.L) return QW3_INVALID_ARGUMENT;
+    if (layer < 0 || layer >= d.L || reps < 1) return QW3_INVALID_ARGUMENT;
+    if (kernel < DK_QKV || kernel > 6 || (kernel == 6 && d.hidden_mode)) return QW3_INVALID_ARGUMENT;
     for (int s = 0; s < d.S; ++s)
         if (m->len[s] >= d.max_ctx) return QW3_CONTEXT_EXCEEDED;
     hipStream_t st = (hipStream_t)stream;
     QW3_TRY(sync_state(m, st));
-    if (kernel >= DK_QKV && kernel <= DK_DOWN) return launch_decode_kernel(m, kernel, layer, 0, d.S, st);
-    if (kernel == 6 && !d.hidden_mode)
-        return run_logits(m, 0, d.S, at<float>(m, m->lay.x), at<float>(m, m->lay.logits), at<int>(m, m->lay.tokens), 0,
-                          st);
-    return QW3_INVALID_ARGUMENT;
+    for (int r = 0; r < reps; ++r) {
+        if (kernel <= DK_DOWN)
+            QW3_TRY(launch_decode_kernel(m, kernel, (layer + r) % d.L, 0, d.S, st));
+        else
+            QW3_TRY(run_logits(m, 0, d.S, at<float>(m, m->lay.x), at<float>(m, m->lay.logits), at<int>(m, m->lay.tokens),
+                               0, st));
+    }
+    return QW3_OK;
 }
 
 }  // extern "C"
