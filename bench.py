@@ -24,6 +24,24 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_q8_b1_ctx2048_hbm_traffic.json")
+
+
+def counted_traffic(role):
+    """HBM bytes per launch of `role` from the committed rocprofv3 counter summary, or None when the kernel
+    source changed since the counters were taken."""
+    import hashlib
+    try:
+        prof = json.load(open(TRAFFIC_PROFILE))
+    except (OSError, ValueError):
+        return None
+    for rel, h in prof.get("source_sha256_16", {}).items():
+        if hashlib.sha256(open(os.path.join(ROOT, rel), "rb").read()).hexdigest()[:16] != h:
+            return None
+    k = prof.get("kernels", {}).get(role)
+    return k["traffic_bytes"] if k else None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -247,7 +265,7 @@ def main():
         "hbm_GBps": round(res["step_bytes"] / ms / 1e6, 1),
         "step_bytes": res["step_bytes"],
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dk["GBps"] / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(dk["GBps"] / HBM_PEAK_GBS, 4), "traffic": counted_traffic(dom)},
         "kernels": res["kernels"],
         "cpu_baseline": cpu,
     }
