@@ -164,6 +164,56 @@ def run_prefill(args, torch, q, synth):
     return dict(tokens=T, ms=ms, tok_s=T / ms * 1e3, flops=flops, tflops=flops / ms / 1e9)
 
 
+def run_batched(args, torch, q, synth):
+    """16 sequences x 8192-position caches, Q8: one greedy step per sequence per iteration."""
+    wl = synth.Q8_BATCHED
+    shp = wl.shape
+    t0 = time.time()
+    W = synth.make_weights(shp, seed=wl.seed)
+    m = q.Model(q.make_config(**synth.abi_config_kwargs(shp)), device="cuda:0")
+    m.load_weights(synth.abi_tensors(W))
+    del W
+    for s in range(shp.n_seq):
+        for l in range(shp.n_layers):
+            k, v = synth.kv_fill(wl.seed, s, l, shp.n_kv_heads, wl.kv_prefill, shp.head_dim)
+            m.kv_write(s, l, 0, torch.from_numpy(k.view("int16")).cuda(), torch.from_numpy(v.view("int16")).cuda())
+        m.set_len(s, wl.kv_prefill)
+    torch.cuda.synchronize()
+    log(f"batched workload ready in {time.time() - t0:.1f}s")
+    stream = torch.cuda.current_stream()
+    am = torch.from_numpy(synth.tokens(wl.seed, 1, shp.n_seq, shp.vocab)).cuda()
+    warm, iters = 4, args.batched_iters
+    for _ in range(warm):
+        m.decode_step(am, am)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        m.decode_step(am, am)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    assert m.status() == 0
+    ms = e0.elapsed_time(e1) / iters
+    ctx_mid = wl.kv_prefill + warm + iters // 2
+    H, I, Q, KV, V, L = shp.hidden, shp.inter, shp.q_dim, shp.kv_dim, shp.vocab, shp.n_layers
+    mats = Q * H + 2 * KV * H + H * Q + 3 * I * H
+    wbytes = (L * mats + V * H) * (1 + 4 / 32)
+    kvbytes = shp.n_seq * L * shp.n_kv_heads * shp.head_dim * 2 * 2 * (ctx_mid + 1)
+    # attention kernel alone (the dominant kernel of this workload)
+    m.bench_kernel(2, 0, 3)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    m.bench_kernel(2, 0, 28)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    attn_us = e0.elapsed_time(e1) * 1e3 / 28
+    attn_bytes = kvbytes / L
+    del m
+    torch.cuda.empty_cache()
+    return dict(ms=ms, tok_s=shp.n_seq / ms * 1e3, bytes=wbytes + kvbytes, GBps=(wbytes + kvbytes) / ms / 1e6,
+                attn_us=attn_us, attn_GBps=attn_bytes / attn_us / 1e3, iters=iters)
+
+
 def cpu_baseline(res, oracle, budget_s):
     """The oracle as it stands, on the host cores, decoding greedy tokens of the same Q8 workload."""
     import numpy as np
@@ -198,6 +248,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=56)
     ap.add_argument("--prefill-reps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-batched", action="store_true")
+    ap.add_argument("--batched-iters", type=int, default=16)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle decode (0 = skip)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM counter scaling)")
@@ -235,6 +287,12 @@ def main():
             log(f"prefill 2048: {pre['ms']:.3f} ms, {pre['tok_s']:.0f} tok/s, {pre['tflops']:.1f} TFLOP/s")
         except q.Qw3Error as e:
             log(f"prefill unavailable: {e}")
+    bat = None
+    if not args.no_batched:
+        with torch.cuda.stream(side):
+            bat = run_batched(args, torch, q, synth)
+        log(f"batched 16x8192: {bat['ms']:.3f} ms/iteration, {bat['tok_s']:.0f} tok/s, {bat['GBps']:.0f} GB/s; "
+            f"attention {bat['attn_us']:.1f} us/layer = {bat['attn_GBps']:.0f} GB/s")
     cpu = None
     if args.cpu_budget > 0:
         import oracle
@@ -274,6 +332,11 @@ def main():
                           "tok_s": round(pre["tok_s"], 1), "ms": round(pre["ms"], 4),
                           "TFLOPs": round(pre["tflops"], 2), "flop": pre["flops"],
                           "frac_bf16_mfma_peak": round(pre["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)}
+    if bat is not None:
+        out["batched"] = {"workload": "28-layer Qwen3-0.6B-shape Q8 decode, 16 sequences x KV context 8192",
+                          "tok_s": round(bat["tok_s"], 1), "ms_per_iteration": round(bat["ms"], 4),
+                          "hbm_GBps": round(bat["GBps"], 1), "attn_us_per_layer": round(bat["attn_us"], 2),
+                          "attn_GBps": round(bat["attn_GBps"], 1), "iterations": bat["iters"]}
     print(json.dumps(out), flush=True)
 
 

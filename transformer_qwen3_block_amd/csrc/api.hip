@@ -52,6 +52,7 @@ struct Model {
     };
     std::vector<StepGraph> graphs;
     bool graphs_enabled = true;
+    int b1_splits = kMaxSplit / 2;  // batch-1 decode attention context splits (measured best of 16/32/64)
     ~Model() {
         for (auto &g : graphs) hipGraphExecDestroy(g.exec);
     }
@@ -173,8 +174,6 @@ int32_t plan(const Dims &d, Layout *lay, qw3_sizes_t *sz) {
     L.kv_end = off;
     L.len = take(kMaxSeq * 4);
     L.status = take(4);
-    L.att_counters = take(c.mul(c.mul(kMaxSeq, d.HKV), 4));
-    L.lm_counter = take(4);
     L.state_end = off;
     const uint64_t M = (uint64_t)(d.max_prefill > d.S ? d.max_prefill : d.S);
     L.x = take(c.mul(c.mul(M, d.H), 4));
@@ -316,6 +315,8 @@ int32_t qw3_create(const qw3_config_t *cfg, void *arena_dev, uint64_t arena_byte
     m->len.assign(d.S, 0);
     const char *ng = getenv("QW3_NO_GRAPH");
     m->graphs_enabled = !(ng && ng[0] == '1');
+    const char *sp = getenv("QW3_B1_SPLITS");  // tuning override, 1..64
+    if (sp && atoi(sp) >= 1 && atoi(sp) <= kMaxSplit) m->b1_splits = atoi(sp);
     std::lock_guard<std::mutex> lk(g_mu);
     for (int i = 0; i < kSlots; ++i) {
         if (!g_slots[i].m) {
@@ -506,7 +507,7 @@ static int32_t launch_decode_kernel(Model *m, int which, int l, int seq0, int S,
             return dev(launch_gemv(d.q8, EPI_STORE, g, st));
         case DK_ATTN: {
             const long long seq_stride = (long long)d.L * d.HKV * d.max_ctx * kHeadDim;
-            int n_split = kMaxSplit / S;
+            int n_split = (S == 1 && m->b1_splits > 0) ? m->b1_splits : kMaxSplit / S;
             if (n_split < 1) n_split = 1;
             AttnDecodeArgs a{};
             a.qkv = qkv;
@@ -526,7 +527,6 @@ static int32_t launch_decode_kernel(Model *m, int which, int l, int seq0, int S,
             a.n_split = n_split;
             a.len = at<int>(m, L.len) + seq0;
             a.part = at<float>(m, L.part);
-            a.counters = at<unsigned>(m, L.att_counters);
             a.out = attn;
             a.ldo = d.q_dim;
             a.eps = d.eps;
@@ -590,7 +590,6 @@ static int32_t run_logits(Model *m, int seq0, int S, const float *xin, float *lo
     g.y = logits;
     g.ldy = d.V;
     g.argpart = at<float>(m, L.argpart);
-    g.counter = at<unsigned>(m, L.lm_counter);
     g.len = at<int>(m, L.len) + seq0;
     g.commit_add = commit_add;
     g.argmax_out = argmax;

@@ -26,7 +26,7 @@ struct Layout {
     // KV cache, bf16 [seq][layer][kv_head][pos][head_dim]
     uint64_t kcache, vcache;
     // state
-    uint64_t len, status, att_counters, lm_counter;
+    uint64_t len, status;
     // scratch
     uint64_t x, xn16, qkv, q16, attn, attn16, act, act16, part, argpart, logits, tokens;
     uint64_t weights_end, kv_end, state_end, scratch_end;
@@ -64,26 +64,6 @@ __device__ __forceinline__ uint4 load_nt16(const void *p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Cross-workgroup exchange without an L2 writeback: values are stored and loaded as relaxed agent-scope
-// atomics (device-coherent "sc1" accesses), and a writer waits for its stores to complete before it
-// increments the arrival counter.  (A plain __threadfence() writes back the whole L2 of the XCD.)
-__device__ __forceinline__ void store_coherent(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float *p) {
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Waits until every memory operation this thread issued has completed.
-__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
-// Arrival ticket of a workgroup on `counter`; returns true for the last of `n` arrivals.  Call after
-// __syncthreads() from one thread, once every thread of the workgroup has called wait_memory().
-__device__ __forceinline__ bool arrive_last(unsigned *counter, unsigned n) {
-    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
-}
-__device__ __forceinline__ void reset_counter(unsigned *counter) {
-    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -112,7 +92,6 @@ struct GemvArgs {
     int ldy;
     // EPI_LOGITS only
     float *argpart;         // [S][gridDim.x][2]
-    unsigned *counter;
     int *len;               // committed lengths of the S sequences (indexed from seq0)
     int commit_add;
     int *argmax_out;        // [S]
@@ -131,7 +110,6 @@ struct AttnDecodeArgs {
     int max_ctx, HQ, HKV, S, n_split;
     const int *len;                 // [S] (already offset to seq0)
     float *part;                    // [S][HQ][kMaxSplit][kPartStride]
-    unsigned *counters;             // [S][HKV]
     float *out;                     // [S][ldo]
     int ldo;
     float eps;

@@ -470,8 +470,8 @@ hipError_t gemv_dispatch(const GemvArgs &a, hipStream_t st) {
 // value to bf16 and appends them to the cache ([P1] section 6).  Each wave then streams 16-position
 // groups of K and V (1 KB per load instruction, 16 lanes per position, 8 dims per lane), keeping an online
 // softmax (running max, running sum, rescaled accumulator) in log2 units.  Wave states are merged in LDS
-// and written as the split's partial; the last workgroup to finish a (seq, kv head) merges the splits in
-// split order, so the result does not depend on completion order.
+// and written as the split's partial (running max, running sum, unnormalised output); attn_merge_kernel
+// combines the splits.
 // ---------------------------------------------------------------------------------------------------
 // K/V of the newly appended position as 8 packed bf16 pairs (the LDS copy holds the bf16 bits per dim).
 __device__ __forceinline__ void new_kv_from_lds(const float *knew, const float *vnew, int dsub, uint4 &k, uint4 &v) {
@@ -494,7 +494,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     __shared__ float red[4];
     __shared__ float wm[4][G], wl[4][G];
     __shared__ float wacc[4][G][kHeadDim];
-    __shared__ int is_last;
 
     const int pos = a.len[s];
     const int n = pos + 1;
@@ -697,51 +696,44 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
         }
         float *p = a.part + (((size_t)s * a.HQ + kvh * G + h) * kMaxSplit + split) * kPartStride;
         if (d == 0) {
-            store_coherent(p, M);
-            store_coherent(p + 1, L);
+            p[0] = M;
+            p[1] = L;
         }
-        store_coherent(p + 2 + d, O);
+        p[2 + d] = O;
     }
-    wait_memory();
-    __syncthreads();
-    if (tid == 0) is_last = arrive_last(a.counters + s * a.HKV + kvh, gridDim.x);
-    __syncthreads();
-    if (!is_last) return;
-    // ---- last workgroup of this (seq, kv head): merge the splits in split order.  Every load of the merge
-    // (running max, running sum and the output slice of each split) is issued in one round.
-    __shared__ float fw[G][kMaxSplit], lw[G][kMaxSplit];
+}
+
+// Merge of one (sequence, query head)'s context splits, in split order (the result does not depend on
+// which split finished first): M = max m_s, f_s = 2^(m_s - M) / sum_s 2^(m_s - M) l_s, o = sum_s f_s o_s.
+// Grid (HQ, S), one thread per head dimension.  Runs as its own kernel: the partials of every split are
+// visible after the attention kernel's boundary, which is cheaper on this chip than an in-kernel arrival
+// ticket (device-coherent stores, their completion and an atomic).
+__global__ __launch_bounds__(kHeadDim) void attn_merge_kernel(const float *part, int HQ, int n_split, float *out,
+                                                              int ldo) {
     static_assert(kMaxSplit == 64, "one split per lane of a wave");
-    const float *pbase = a.part + (((size_t)s * a.HQ + kvh * G) * kMaxSplit) * kPartStride;
-    float ov[G > 2 ? 2 : 1][kMaxSplit];
-    for (int t = tid, k = 0; t < G * kHeadDim; t += 256, ++k) {
-        const int h = t >> 7, d = t & 127;
-        const float *p0 = pbase + (size_t)h * kMaxSplit * kPartStride + 2 + d;
+    __shared__ float fm[kMaxSplit], fl[kMaxSplit];
+    const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+    const float *p0 = part + (((size_t)s * HQ + h) * kMaxSplit) * kPartStride;
+    float ov[kMaxSplit];
 #pragma unroll
-        for (int sp = 0; sp < kMaxSplit; ++sp) ov[k][sp] = sp < a.n_split ? load_coherent(p0 + sp * kPartStride) : 0.f;
-    }
-    for (int t = tid; t < G * kMaxSplit; t += 256) {
-        const int h = t / kMaxSplit, sp = t % kMaxSplit;
-        const float *p = pbase + ((size_t)h * kMaxSplit + sp) * kPartStride;
-        fw[h][sp] = sp < a.n_split ? load_coherent(p) : -INFINITY;
-        lw[h][sp] = sp < a.n_split ? load_coherent(p + 1) : 0.f;
+    for (int sp = 0; sp < kMaxSplit; ++sp) ov[sp] = sp < n_split ? p0[sp * kPartStride + 2 + d] : 0.f;
+    if (d < kMaxSplit) {
+        fm[d] = d < n_split ? p0[d * kPartStride] : -INFINITY;
+        fl[d] = d < n_split ? p0[d * kPartStride + 1] : 0.f;
     }
     __syncthreads();
-    if (wave < G) {  // one wave per head, one split per lane
-        const float mv = fw[wave][lane];
+    if (d < 64) {
+        const float mv = fm[d];
         const float M = wave_max(mv);
         const float f = mv == -INFINITY ? 0.f : exp2f(mv - M);
-        const float L = wave_sum(f * lw[wave][lane]);
-        fw[wave][lane] = f / L;
+        const float L = wave_sum(f * fl[d]);
+        fm[d] = f / L;
     }
     __syncthreads();
-    for (int t = tid, k = 0; t < G * kHeadDim; t += 256, ++k) {
-        const int h = t >> 7, d = t & 127;
-        float O = 0.f;
+    float o = 0.f;
 #pragma unroll
-        for (int sp = 0; sp < kMaxSplit; ++sp) O += fw[h][sp] * ov[k][sp];
-        a.out[(size_t)s * a.ldo + (kvh * G + h) * kHeadDim + d] = O;
-    }
-    if (tid == 0) reset_counter(a.counters + s * a.HKV + kvh);
+    for (int sp = 0; sp < kMaxSplit; ++sp) o += fm[sp] * ov[sp];
+    out[(size_t)s * ldo + h * kHeadDim + d] = o;
 }
 
 // Embedding: x[s] = row tokens[s] of the table, widened (bf16) or dequantised (code * scale).
@@ -819,6 +811,8 @@ hipError_t launch_attn_decode(int G, const AttnDecodeArgs &a, hipStream_t st) {
         case 4: hipLaunchKernelGGL(attn_decode_kernel<4>, grid, dim3(256), 0, st, a); break;
         default: return hipErrorInvalidValue;
     }
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.HQ, a.S), dim3(kHeadDim), 0, st, a.part, a.HQ, a.n_split, a.out,
+                       a.ldo);
     return hipGetLastError();
 }
 
