@@ -96,14 +96,14 @@ constexpr int kBK = 64;
 constexpr int kLdsPad = 8;  // 16-bit elements of padding per LDS row
 
 template <int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs g) {
-    static_assert(WM * WN == 4, "four waves");
+__global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
+    constexpr int NT = 64 * WM * WN;             // threads
     constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
     constexpr int TM = WTM / 16, TN = WTN / 16;
     constexpr int LDR = kBK + kLdsPad;
-    constexpr int ACH = BM * kBK / 8 / 256;  // 16-byte chunks per thread per A step
-    constexpr int BCH = BN * kBK / 8 / 256;
-    static_assert(ACH >= 1 && BCH >= 1, "tile too small for 256 threads");
+    constexpr int ACH = BM * kBK / 8 / NT;  // 16-byte chunks per thread per A step
+    constexpr int BCH = BN * kBK / 8 / NT;
+    static_assert(ACH >= 1 && BCH >= 1 && TM >= 1 && TN >= 1, "tile too small for the wave layout");
     __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDR];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDR];
 
@@ -126,25 +126,25 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs g) {
     auto load_tiles = [&](int k0) {
 #pragma unroll
         for (int c = 0; c < ACH; ++c) {
-            const int ch = tid + 256 * c, r = ch >> 3, kc = (ch & 7) * 8;
+            const int ch = tid + NT * c, r = ch >> 3, kc = (ch & 7) * 8;
             const int m = m0 + r;
             ra[c] = m < g.M ? *(const uint4 *)(g.A + (size_t)m * g.K + k0 + kc) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int c = 0; c < BCH; ++c) {
-            const int ch = tid + 256 * c, r = ch >> 3, kc = (ch & 7) * 8;
+            const int ch = tid + NT * c, r = ch >> 3, kc = (ch & 7) * 8;
             rb[c] = load_nt16(g.W + (size_t)wrow(r) * g.K + k0 + kc);
         }
     };
     auto store_tiles = [&]() {
 #pragma unroll
         for (int c = 0; c < ACH; ++c) {
-            const int ch = tid + 256 * c, r = ch >> 3, kc = (ch & 7) * 8;
+            const int ch = tid + NT * c, r = ch >> 3, kc = (ch & 7) * 8;
             *(uint4 *)(As + r * LDR + kc) = ra[c];
         }
 #pragma unroll
         for (int c = 0; c < BCH; ++c) {
-            const int ch = tid + 256 * c, r = ch >> 3, kc = (ch & 7) * 8;
+            const int ch = tid + NT * c, r = ch >> 3, kc = (ch & 7) * 8;
             *(uint4 *)(Bs + r * LDR + kc) = rb[c];
         }
     };
@@ -222,11 +222,12 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
         const dim3 grid(g.N / 32, (g.M + 63) / 64);
         hipLaunchKernelGGL((gemm_f16_kernel<64, 32, 4, 1, EPI>), grid, dim3(256), 0, st, g);
     } else if (mt128 * (g.N / 128) < 512) {
-        const dim3 grid(g.N / 64, (g.M + 127) / 128);
-        hipLaunchKernelGGL((gemm_f16_kernel<128, 64, 2, 2, EPI>), grid, dim3(256), 0, st, g);
+        // narrow outputs (o_proj, down): 64x64 tiles so every CU gets at least two workgroups
+        const dim3 grid(g.N / 64, (g.M + 63) / 64);
+        hipLaunchKernelGGL((gemm_f16_kernel<64, 64, 2, 2, EPI>), grid, dim3(256), 0, st, g);
     } else {
         const dim3 grid(g.N / 128, mt128);
-        hipLaunchKernelGGL((gemm_f16_kernel<128, 128, 2, 2, EPI>), grid, dim3(256), 0, st, g);
+        hipLaunchKernelGGL((gemm_f16_kernel<128, 128, 4, 2, EPI>), grid, dim3(512), 0, st, g);
     }
     return hipGetLastError();
 }
@@ -234,37 +235,39 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
 // ---------------------------------------------------------------------------------------------------
 // QK-Norm + RoPE of every query/key head of T tokens ([P1] section 2 items 3-4) and the KV append
 // ([P1] section 6): query heads go to q16 (f16, [T][HQ][128]); keys (normalised, rotated) and values are
-// rounded to bf16 into the cache at positions pos0..pos0+T-1.  Grid (T, HQ + HKV), 128 threads.
+// rounded to bf16 into the cache at positions pos0..pos0+T-1.  One workgroup per token, one wave per head
+// at a time; lane i holds dims i and i+64, which is exactly a RoPE pair.
 // ---------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void qknorm_rope_append_kernel(const float *qkv, int ldqkv, int HQ, int HKV,
+__global__ __launch_bounds__(256) void qknorm_rope_append_kernel(const float *qkv, int ldqkv, int HQ, int HKV,
                                                                  const float *q_norm, const float *k_norm,
                                                                  const float *rope_cos, const float *rope_sin,
                                                                  int pos0, float eps, uint16_t *q16, uint16_t *kc,
                                                                  uint16_t *vc, int max_ctx) {
-    __shared__ float red[2];
-    __shared__ float nv[kHeadDim];
-    const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+    const int t = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int pos = pos0 + t;
     const float *row = qkv + (size_t)t * ldqkv;
-    const bool is_q = h < HQ;
-    const int hk = h - HQ;
-    const float v = is_q ? row[h * kHeadDim + d] : row[(HQ + hk) * kHeadDim + d];
-    const float ss = wave_sum(v * v);
-    if ((d & 63) == 0) red[d >> 6] = ss;
-    __syncthreads();
-    const float inv = 1.0f / sqrtf((red[0] + red[1]) / (float)kHeadDim + eps);
-    nv[d] = (is_q ? q_norm[d] : k_norm[d]) * (v * inv);
-    __syncthreads();
-    const int i = d & 63;
-    const float c = rope_cos[(size_t)pos * 64 + i], sn = rope_sin[(size_t)pos * 64 + i];
-    const float x1 = nv[i], x2 = nv[i + 64];
-    const float r = d < 64 ? x1 * c - x2 * sn : x2 * c + x1 * sn;
-    if (is_q) {
-        q16[((size_t)t * HQ + h) * kHeadDim + d] = f32_to_h16(r);
-    } else {
-        const size_t at = ((size_t)hk * max_ctx + pos) * kHeadDim + d;
-        kc[at] = f32_to_bf16(r);
-        vc[at] = f32_to_bf16(row[(HQ + HKV + hk) * kHeadDim + d]);
+    const float c = rope_cos[(size_t)pos * 64 + lane], sn = rope_sin[(size_t)pos * 64 + lane];
+    for (int h = wave; h < HQ + HKV; h += 4) {
+        const bool is_q = h < HQ;
+        const float *src = row + (size_t)h * kHeadDim;  // query heads, then key heads
+        const float v0 = src[lane], v1 = src[lane + 64];
+        const float inv = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) / (float)kHeadDim + eps);
+        const float *w = is_q ? q_norm : k_norm;
+        const float n0 = w[lane] * (v0 * inv), n1 = w[lane + 64] * (v1 * inv);
+        const float r0 = n0 * c - n1 * sn, r1 = n1 * c + n0 * sn;
+        if (is_q) {
+            uint16_t *dst = q16 + ((size_t)t * HQ + h) * kHeadDim;
+            dst[lane] = f32_to_h16(r0);
+            dst[lane + 64] = f32_to_h16(r1);
+        } else {
+            const int hk = h - HQ;
+            const size_t at = ((size_t)hk * max_ctx + pos) * kHeadDim;
+            kc[at + lane] = f32_to_bf16(r0);
+            kc[at + lane + 64] = f32_to_bf16(r1);
+            const float *vs = row + (size_t)(HQ + HKV + hk) * kHeadDim;
+            vc[at + lane] = f32_to_bf16(vs[lane]);
+            vc[at + lane + 64] = f32_to_bf16(vs[lane + 64]);
+        }
     }
 }
 
@@ -291,9 +294,11 @@ constexpr int kKsLd = kHeadDim + 8;      // K tile row stride (f16 elements)
 constexpr int kVtLd = kKT + 8;           // V^T tile row stride (f16 elements)
 
 template <int G>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
-    constexpr int WPH = 4 / G;    // waves per query head
+__global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
+    constexpr int NW = 8;         // waves per workgroup
+    constexpr int WPH = NW / G;   // waves per query head
     constexpr int QB = 16 * WPH;  // queries per workgroup
+    constexpr int KPW = kKT / NW; // keys of a tile whose V this wave stages
     __shared__ __attribute__((aligned(16))) uint16_t Ks[kKT * kKsLd];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * kVtLd];
 
@@ -312,6 +317,48 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
     const uint16_t *kb = a.kc + head_off;
     const uint16_t *vb = a.vc + head_off;
 
+    // Tile loads (registers): K as 16-byte chunks [key][8 dims]; V as 4-byte pairs so that each lane holds
+    // two dims of four consecutive keys and can write V^T rows with 8-byte stores.
+    constexpr int KCH = kKT * kHeadDim / 8 / (64 * NW);  // 16-byte K chunks per thread
+    uint4 kreg[KCH];
+    uint32_t vreg[KPW / 4][4];  // [key batch][key]: dims (2*lane, 2*lane+1) of key KPW*wave + 4*batch + k
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            const int ch = tid + 64 * NW * c, key = ch >> 4, dc = (ch & 15) * 8;
+            const int p = k0 + key;
+            kreg[c] = p < n_keys ? *(const uint4 *)(kb + (size_t)p * kHeadDim + dc) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int bt = 0; bt < KPW / 4; ++bt)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int p = k0 + KPW * wave + 4 * bt + k;
+                vreg[bt][k] = p < n_keys ? *(const uint32_t *)(vb + (size_t)p * kHeadDim + 2 * lane) : 0u;
+            }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            const int ch = tid + 64 * NW * c, key = ch >> 4, dc = (ch & 15) * 8;
+            const uint4 kv = kreg[c];
+            *(uint4 *)(Ks + key * kKsLd + dc) =
+                make_uint4(bf16x2_to_h16x2(kv.x), bf16x2_to_h16x2(kv.y), bf16x2_to_h16x2(kv.z), bf16x2_to_h16x2(kv.w));
+        }
+#pragma unroll
+        for (int bt = 0; bt < KPW / 4; ++bt) {
+            uint32_t h[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) h[k] = bf16x2_to_h16x2(vreg[bt][k]);
+            // dim 2*lane: low halves of the four keys; dim 2*lane+1: high halves
+            const uint2 lo = make_uint2((h[0] & 0xffffu) | (h[1] << 16), (h[2] & 0xffffu) | (h[3] << 16));
+            const uint2 hi = make_uint2((h[0] >> 16) | (h[1] & 0xffff0000u), (h[2] >> 16) | (h[3] & 0xffff0000u));
+            const int key0 = KPW * wave + 4 * bt;
+            *(uint2 *)(Vt + (2 * lane) * kVtLd + key0) = lo;
+            *(uint2 *)(Vt + (2 * lane + 1) * kVtLd + key0) = hi;
+        }
+    };
+
     // Q^T fragments (B operand of S^T): lane holds Q[tq][32*ks + 8*g4 .. +8]
     uint4 qf[4];
 #pragma unroll
@@ -325,46 +372,27 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
     float m = -INFINITY, l = 0.f;
     const float sl2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
 
+    load_tile(0);
     for (int k0 = 0; k0 < n_keys; k0 += kKT) {
         __syncthreads();  // previous tile fully consumed
-        // stage K [64][128] and V^T [128][64]; positions past n_keys are zero
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int ch = tid + 256 * c, key = ch >> 4, dc = (ch & 15) * 8;
-            const int p = k0 + key;
-            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-            if (p < n_keys) {
-                kv = *(const uint4 *)(kb + (size_t)p * kHeadDim + dc);
-                vv = *(const uint4 *)(vb + (size_t)p * kHeadDim + dc);
-                kv = make_uint4(bf16x2_to_h16x2(kv.x), bf16x2_to_h16x2(kv.y), bf16x2_to_h16x2(kv.z),
-                                bf16x2_to_h16x2(kv.w));
-                vv = make_uint4(bf16x2_to_h16x2(vv.x), bf16x2_to_h16x2(vv.y), bf16x2_to_h16x2(vv.z),
-                                bf16x2_to_h16x2(vv.w));
-            }
-            *(uint4 *)(Ks + key * kKsLd + dc) = kv;
-            const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                Vt[(dc + 2 * q) * kVtLd + key] = (uint16_t)(w[q] & 0xffffu);
-                Vt[(dc + 2 * q + 1) * kVtLd + key] = (uint16_t)(w[q] >> 16);
-            }
-        }
+        store_tile();
         __syncthreads();
+        if (k0 + kKT < n_keys) load_tile(k0 + kKT);  // next tile in flight during this one
 
         // S^T tiles: lane holds scores of keys k0 + 16*kt + 4*g4 + r for its query
         float sc[4][4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-            f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            f32x4_t sv = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const uint4 kf = *(const uint4 *)(Ks + (16 * kt + (lane & 15)) * kKsLd + 32 * ks + 8 * g4);
-                s = mfma16(kf, qf[ks], s);
+                sv = mfma16(kf, qf[ks], sv);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int kp = k0 + 16 * kt + 4 * g4 + r;
-                sc[kt][r] = kp <= qpos && kp < n_keys ? s[r] * sl2 : -INFINITY;
+                sc[kt][r] = kp <= qpos && kp < n_keys ? sv[r] * sl2 : -INFINITY;
             }
         }
         float tm = -INFINITY;
@@ -380,7 +408,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
         l *= alpha;
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[i] *= alpha;
-        // probabilities as bf16 pairs: P^T fragments for the two 32-key halves of the tile
+        // probabilities as f16 pairs: P^T fragments for the two 32-key halves of the tile
         uint32_t pw[2][4];
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -419,12 +447,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
 }
 
 hipError_t launch_attn_prefill(int G, const AttnPrefillArgs &a, hipStream_t st) {
-    const int QB = 16 * (4 / G);
+    const int QB = 16 * (8 / G);
     const dim3 grid((a.T + QB - 1) / QB, a.HKV);
     switch (G) {
-        case 1: hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(256), 0, st, a); break;
-        case 2: hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, dim3(256), 0, st, a); break;
-        case 4: hipLaunchKernelGGL(attn_prefill_kernel<4>, grid, dim3(256), 0, st, a); break;
+        case 1: hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(512), 0, st, a); break;
+        case 2: hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, dim3(512), 0, st, a); break;
+        case 4: hipLaunchKernelGGL(attn_prefill_kernel<4>, grid, dim3(512), 0, st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -477,7 +505,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         g.outf = qkv;
         g.ldo = d.Nqkv;
         QW3_PF_TRY(launch_gemm<G_STORE>(g, st));
-        hipLaunchKernelGGL(qknorm_rope_append_kernel, dim3(T, d.HQ + d.HKV), dim3(128), 0, st, qkv, d.Nqkv, d.HQ,
+        hipLaunchKernelGGL(qknorm_rope_append_kernel, dim3(T), dim3(256), 0, st, qkv, d.Nqkv, d.HQ,
                            d.HKV, (const float *)(arena + b + L.l_q_norm), (const float *)(arena + b + L.l_k_norm), rc,
                            rs, pos0, d.eps, q16, kc, vc, d.max_ctx);
         AttnPrefillArgs at{};
