@@ -56,7 +56,9 @@ def decode_kernel_bytes(shp, ctx):
         return rows * cols + rows * (cols // 32) * 4 if q8 else rows * cols * 2
 
     nqkv = Q + 2 * KV
+    layer_w = w(nqkv, H) + w(H, Q) + w(2 * I, H) + w(H, I)
     return {
+        "decode_layers": shp.n_layers * (layer_w + ctx * shp.n_kv_heads * shp.head_dim * 2 * 2) + 8 * H,
         "qkv_gemv": w(nqkv, H) + 4 * H + 4 * nqkv,
         "attn_decode": ctx * shp.n_kv_heads * shp.head_dim * 2 * 2 + 4 * nqkv + 4 * Q,
         "o_gemv": w(H, Q) + 4 * Q + 8 * H,
@@ -105,8 +107,11 @@ def run_decode(args, torch, q, synth):
     # per-kernel timing: back-to-back launches of one kernel bracketed by HIP events on the launch stream
     ctx_now = m.get_len(0)
     kb = decode_kernel_bytes(shp, ctx_now + 1)
-    ids = {"qkv_gemv": 1, "attn_decode": 2, "o_gemv": 3, "gateup_gemv": 4, "down_gemv": 5, "lm_head_argmax": 6}
-    per_step = {k: (1 if k == "lm_head_argmax" else shp.n_layers) for k in ids}
+    if args.kernel_path:
+        ids = {"qkv_gemv": 1, "attn_decode": 2, "o_gemv": 3, "gateup_gemv": 4, "down_gemv": 5, "lm_head_argmax": 6}
+    else:  # the layer stack is one persistent launch per token
+        ids = {"decode_layers": 7, "lm_head_argmax": 6}
+    per_step = {k: (1 if k in ("lm_head_argmax", "decode_layers") else shp.n_layers) for k in ids}
     kernels = {}
     reps = args.kernel_reps
     for name, kid in ids.items():
@@ -251,6 +256,8 @@ def main():
     ap.add_argument("--no-batched", action="store_true")
     ap.add_argument("--batched-iters", type=int, default=16)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle decode (0 = skip)")
+    ap.add_argument("--kernel-path", action="store_true",
+                    help="decode kernel by kernel (one launch per step of a layer) instead of one persistent launch")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM counter scaling)")
     args = ap.parse_args()
@@ -261,6 +268,8 @@ def main():
     if args.warmup < 1 or args.steps < 1:
         sys.exit("--warmup and --steps must be >= 1")
 
+    if args.kernel_path:
+        os.environ["QW3_NO_MEGA"] = "1"
     import torch
 
     import synth

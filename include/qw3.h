@@ -181,7 +181,10 @@ int32_t qw3_decode_step(uint64_t handle, const int32_t *tokens_dev, float *logit
  * length ("Scalar-Native ...", section 6 "Cancellation and Reset").  Host-side only. */
 int32_t qw3_reset_kv(uint64_t handle, int32_t seq);
 
-/* Waits for `stream` and returns the latched device status (QW3_OK or QW3_NUMERICAL_FAILURE). */
+/* Waits for `stream` and returns the latched device status: QW3_OK, QW3_NUMERICAL_FAILURE, or
+ * QW3_DEVICE_ERROR when a wait inside the single-launch decode kernel timed out (its workgroups could not
+ * all be resident at once, e.g. because other work held the compute units).  Both poison the handle until
+ * qw3_reset_kv. */
 int32_t qw3_status_poll(uint64_t handle, void *stream);
 
 /* Host copy of a sequence's committed KV length. */
@@ -217,8 +220,10 @@ int32_t qw3_dequant(uint64_t handle, int32_t kind, int32_t layer, float *out_dev
 /* Launches one kernel of the decode step `reps` times back to back on the current state, for timing:
  * kernel 1 = RMSNorm+QKV GEMV, 2 = attention (re-appends the current position's K/V), 3 = o_proj+residual,
  * 4 = RMSNorm+gate/up+SwiGLU, 5 = down+residual (layers layer, layer+1, ... cyclically), 6 = final norm +
- * logits + argmax (no commit).  Lengths do not advance; the residual-updating kernels change the scratch
- * hidden state, so a step after this hook is not a continuation of the previous one. */
+ * logits + argmax (no commit), 7 = the whole layer stack of sequence 0 as one persistent launch (only for
+ * single-sequence models whose shape that kernel covers; QW3_INVALID_ARGUMENT otherwise).  Lengths do not
+ * advance; the residual-updating kernels change the scratch hidden state, so a step after this hook is not a
+ * continuation of the previous one. */
 int32_t qw3_bench_kernel(uint64_t handle, int32_t kernel, int32_t layer, int32_t reps, void *stream);
 
 #ifdef __cplusplus

@@ -6,6 +6,10 @@ L2 (||gpu - ref|| / ||ref||) <= 1e-2 against the oracle.  Integer results (dequa
 contents, argmax ids) are compared bit for bit; an argmax may differ from the oracle's only when the
 oracle's own top-1/top-2 margin is smaller than twice the observed max-abs logit difference of that step
 (then both ids are correct within the tolerance), and exact ties must pick the lowest id.
+
+Decode trajectories are compared with the KV cache teacher-forced (sync_appended_kv): the appended bf16 K/V
+of every step must be within the relative-L2 tolerance of the oracle's, and the oracle continues from the
+GPU's cache.
 """
 import numpy as np
 
@@ -42,6 +46,34 @@ def argmax_ok(gpu_id, ref_logits, gpu_logits=None):
     top = np.sort(ref_logits)[::-1]
     margin = float(top[0] - ref_logits[gpu_id])
     return margin < 2 * diff
+
+
+def bf16_to_f32(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def sync_appended_kv(gpu_model, orc, seq, pos, n_layers, orc_seq=None):
+    """KV teacher forcing.  Both sides round the appended K and V to bf16; two correct f32 evaluations in
+    different summation orders can land on opposite sides of a bf16 rounding boundary (one ulp, 0.4 %), a flip
+    in one layer moves the later layers' K/V of the same position, and a free-running comparison then drifts
+    for every later step.  So after a step each layer's appended K and V are checked against the oracle's
+    (relative L2 within the hidden-state tolerance: an index, head or position error is an O(1) difference)
+    and the oracle's copy is replaced by the GPU's: every step is compared from the same cache.  Returns the
+    number of appended elements that differ."""
+    oseq = seq if orc_seq is None else orc_seq
+    differ = 0
+    for l in range(n_layers):
+        gk, gv = gpu_model.kv_read(seq, l, pos, 1)
+        gk = gk.cpu().numpy().view(np.uint16)
+        gv = gv.cpu().numpy().view(np.uint16)
+        rc, ok_, ov = orc.kv_read(oseq, l, pos, 1)
+        assert rc == 0
+        for g_, o_, nm in ((gk, ok_, "K"), (gv, ov, "V")):
+            r = rel_l2(bf16_to_f32(g_), bf16_to_f32(o_))
+            assert r <= REL_L2, f"appended {nm} of layer {l} at position {pos}: rel-L2 {r:.3e}"
+            differ += int(np.count_nonzero(g_ != o_))
+        assert orc.kv_write(oseq, l, pos, gk, gv) == 0
+    return differ
 
 
 def build_gpu_model(W, device="cuda:0", with_lm_head=False):

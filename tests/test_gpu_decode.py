@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from parity import argmax_ok, assert_close, build_gpu_model
+from parity import argmax_ok, assert_close, build_gpu_model, sync_appended_kv
 
 pytestmark = pytest.mark.gpu
 
@@ -64,11 +64,23 @@ def test_kv_write_read_roundtrip_and_bounds():
     assert e.value.code == 6
 
 
-def _greedy_vs_oracle(shp, seed, steps, prefill_tokens=0, kv_fill_len=0, seqs_checked=None):
+def _build(W, path):
+    """path "mega": single-sequence steps as one persistent launch (the default where the shape allows);
+    "kernels": one launch per step of the layer (QW3_NO_MEGA=1 at creation)."""
+    import os
+    if path == "kernels":
+        os.environ["QW3_NO_MEGA"] = "1"
+    try:
+        return build_gpu_model(W)
+    finally:
+        os.environ.pop("QW3_NO_MEGA", None)
+
+
+def _greedy_vs_oracle(shp, seed, steps, prefill_tokens=0, kv_fill_len=0, seqs_checked=None, path="mega"):
     """Free-running GPU greedy decode, replayed through the oracle (teacher forcing)."""
     torch = _torch()
     W = synth.make_weights(shp, seed=seed)
-    m = build_gpu_model(W)
+    m = _build(W, path)
     S = shp.n_seq
     orc = oracle.Model(W)
     if kv_fill_len:
@@ -91,11 +103,13 @@ def _greedy_vs_oracle(shp, seed, steps, prefill_tokens=0, kv_fill_len=0, seqs_ch
         g_logits = logits.cpu().numpy()
         g_am = am.cpu().numpy()
         for s in (seqs_checked if seqs_checked is not None else range(S)):
+            pos = orc.get_len(s)
             rc, o_am, o_logits, _ = orc.step(s, int(cur[s].item()))
             assert rc == 0
             mab, r = assert_close(g_logits[s], o_logits, f"step {step} seq {s}")
             worst = (max(worst[0], mab), max(worst[1], r))
             assert argmax_ok(int(g_am[s]), o_logits, g_logits[s]), (step, s, int(g_am[s]), o_am)
+            sync_appended_kv(m, orc, s, pos, shp.n_layers)
         cur = am.clone()
     assert m.status() == 0
     for s in range(S):
@@ -103,25 +117,29 @@ def _greedy_vs_oracle(shp, seed, steps, prefill_tokens=0, kv_fill_len=0, seqs_ch
     return worst
 
 
+@pytest.mark.parametrize("path", ["mega", "kernels"])
 @pytest.mark.parametrize("fmt", [synth.FMT_BF16, synth.FMT_Q8])
-def test_decode_small_vs_oracle(fmt):
+def test_decode_small_vs_oracle(fmt, path):
     shp = replace(SMALL, fmt=fmt)
-    _say("decode small", shp)
-    worst = _greedy_vs_oracle(shp, seed=23, steps=12)
+    _say("decode small", shp, path)
+    worst = _greedy_vs_oracle(shp, seed=23, steps=12, path=path)
     _say("worst max-abs / rel-L2", worst)
 
 
-@pytest.mark.parametrize("heads", [(8, 8), (8, 2)])
-def test_decode_gqa_group_sizes(heads):
+@pytest.mark.parametrize("path", ["mega", "kernels"])
+@pytest.mark.parametrize("heads", [(8, 8), (8, 2), (16, 4)])
+def test_decode_gqa_group_sizes(heads, path):
     shp = replace(SMALL, n_q_heads=heads[0], n_kv_heads=heads[1], n_layers=1)
-    _say("gqa", heads)
-    _greedy_vs_oracle(shp, seed=24, steps=6)
+    _say("gqa", heads, path)
+    _greedy_vs_oracle(shp, seed=24, steps=6, path=path)
 
 
-def test_decode_over_prefilled_cache_ragged_context():
+@pytest.mark.parametrize("path", ["mega", "kernels"])
+def test_decode_over_prefilled_cache_ragged_context(path):
     """Context lengths that are not multiples of the 16-position groups or of the split count."""
     shp = replace(SMALL, fmt=synth.FMT_Q8, max_ctx=400)
-    _greedy_vs_oracle(shp, seed=25, steps=4, kv_fill_len=333)
+    _say("ragged context", path)
+    _greedy_vs_oracle(shp, seed=25, steps=4, kv_fill_len=333, path=path)
 
 
 def test_decode_batched_sequences():

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import synth
-from parity import argmax_ok, assert_close, build_gpu_model
+from parity import argmax_ok, assert_close, build_gpu_model, sync_appended_kv
 
 pytestmark = pytest.mark.gpu
 
@@ -62,12 +62,15 @@ def test_q8_decode_context_2048_full():
         with torch.cuda.stream(side):   # the graph-replayed launch configuration of bench.py
             m.decode_step(cur, am, lg)
         side.synchronize()
+        pos = orc.get_len(0)
         rc, _, o_lg, _ = orc.step(0, int(cur.item()))
         assert rc == 0
         g = lg.cpu().numpy()[0]
         mab, r = assert_close(g, o_lg, f"step {step}")
         _say(f"  step {step}: max-abs {mab:.3e} rel-L2 {r:.3e} (logit rms {np.sqrt(np.mean(o_lg ** 2)):.2f})")
         assert argmax_ok(int(am.item()), o_lg, g)
+        flips = sync_appended_kv(m, orc, 0, pos, shp.n_layers)
+        _say(f"  appended KV elements that differ from the oracle's: {flips}")
         cur = am.clone()
     assert m.get_len(0) == wl.kv_prefill + 4 and m.status() == 0
 
@@ -96,11 +99,13 @@ def test_batched_16_sequences_context_8192_full():
         side.synchronize()
         g_all = lg.cpu().numpy()
         for s in check:
+            pos = orcs[s].get_len(0)
             rc, _, o_lg, _ = orcs[s].step(0, int(cur[s].item()))
             assert rc == 0
             mab, r = assert_close(g_all[s], o_lg, f"iteration {it} seq {s}")
             _say(f"  it {it} seq {s}: max-abs {mab:.3e} rel-L2 {r:.3e}")
             assert argmax_ok(int(am[s].item()), o_lg, g_all[s])
+            sync_appended_kv(m, orcs[s], s, pos, shp.n_layers, orc_seq=0)
         cur = am.clone()
     assert m.status() == 0
     for s in range(shp.n_seq):

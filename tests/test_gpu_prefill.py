@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from parity import argmax_ok, assert_close, build_gpu_model, rel_l2
+from parity import argmax_ok, assert_close, build_gpu_model, sync_appended_kv, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -56,10 +56,12 @@ def _prefill_vs_oracle(shp, seed, T, decode_steps=0):
     for step in range(decode_steps):
         m.decode_step(cur, am, lg)
         torch.cuda.synchronize()
+        pos = orc.get_len(0)
         rc, _, o_lg, _ = orc.step(0, int(cur.item()))
         assert rc == 0
         assert_close(lg.cpu().numpy()[0], o_lg, f"decode {step} after prefill {T}")
         assert argmax_ok(int(am.item()), o_lg, lg.cpu().numpy()[0])
+        sync_appended_kv(m, orc, 0, pos, shp.n_layers)
         cur = am.clone()
     assert m.status() == 0
     return m, W

@@ -52,6 +52,7 @@ struct Model {
     };
     std::vector<StepGraph> graphs;
     bool graphs_enabled = true;
+    bool mega = false;  // single-sequence steps run as one persistent launch (decode_mega_kernel)
     int b1_splits = kMaxSplit / 2;  // batch-1 decode attention context splits (measured best of 16/32/64)
     ~Model() {
         for (auto &g : graphs) hipGraphExecDestroy(g.exec);
@@ -174,6 +175,14 @@ int32_t plan(const Dims &d, Layout *lay, qw3_sizes_t *sz) {
     L.kv_end = off;
     L.len = take(kMaxSeq * 4);
     L.status = take(4);
+    // single-launch decode: epoch word and tagged exchange words (8 bytes each), zeroed at load
+    L.epoch = take(4);
+    L.x_o = take(c.mul(d.H, 8));
+    L.x_d = take(c.mul(d.H, 8));
+    L.qkv_x = take(c.mul(d.Nqkv, 8));
+    L.part_x = take(c.mul(c.mul((uint64_t)kMegaGrid * d.G, kPartStride), 8));  // one partial per workgroup
+    L.attn_x = take(c.mul(d.q_dim, 8));
+    L.act_x = take(c.mul(d.I, 8));
     L.state_end = off;
     const uint64_t M = (uint64_t)(d.max_prefill > d.S ? d.max_prefill : d.S);
     L.x = take(c.mul(c.mul(M, d.H), 4));
@@ -218,7 +227,7 @@ inline int32_t dev(hipError_t e) { return e == hipSuccess ? QW3_OK : QW3_DEVICE_
 int32_t sync_state(Model *m, hipStream_t st) {
     if (!m->lens_dirty && !m->status_dirty) return QW3_OK;
     QW3_HIP(launch_set_lens(at<int>(m, m->lay.len), m->d.S, m->len.data(), (1 << m->d.S) - 1, at<int>(m, m->lay.status),
-                            m->status_dirty ? 1 : 0, st));
+                            m->status_dirty ? 1 : 0, at<uint32_t>(m, m->lay.epoch), st));
     m->lens_dirty = m->status_dirty = false;
     return QW3_OK;
 }
@@ -315,6 +324,8 @@ int32_t qw3_create(const qw3_config_t *cfg, void *arena_dev, uint64_t arena_byte
     m->len.assign(d.S, 0);
     const char *ng = getenv("QW3_NO_GRAPH");
     m->graphs_enabled = !(ng && ng[0] == '1');
+    const char *nm = getenv("QW3_NO_MEGA");  // run single-sequence steps kernel by kernel
+    m->mega = mega_supported(d) && !(nm && nm[0] == '1');
     const char *sp = getenv("QW3_B1_SPLITS");  // tuning override, 1..64
     if (sp && atoi(sp) >= 1 && atoi(sp) <= kMaxSplit) m->b1_splits = atoi(sp);
     std::lock_guard<std::mutex> lk(g_mu);
@@ -469,6 +480,10 @@ int32_t qw3_status_poll(uint64_t h, void *stream) {
     QW3_HIP(hipMemcpyAsync(&status, m->arena + m->lay.status, 4, hipMemcpyDeviceToHost, st));
     QW3_HIP(hipStreamSynchronize(st));
     if (status & 1) m->poisoned = true;
+    if (status & 4) {  // a wait of the single-launch decode timed out (its workgroups were not all resident)
+        m->poisoned = true;
+        return QW3_DEVICE_ERROR;
+    }
     if (status & 2) return QW3_INVALID_ARGUMENT;  // a token id outside [0, vocab) reached the device
     return m->poisoned ? QW3_NUMERICAL_FAILURE : QW3_OK;
 }
@@ -573,6 +588,57 @@ static int32_t run_layers_decode(Model *m, int seq0, int S, hipStream_t st) {
     return QW3_OK;
 }
 
+// Layer stack for one token of sequence `seq` in one persistent launch: input = embedding row of *token
+// (token mode) or hidden_in (f32 [H]); output = x_out (f32 [H]).  Needs m->mega.
+static int32_t run_layers_mega(Model *m, int seq, const int *token, const float *hidden_in, float *x_out,
+                               hipStream_t st) {
+    const Dims &d = m->d;
+    const Layout &L = m->lay;
+    MegaArgs a{};
+    a.layer0 = m->arena + L.layer0;
+    a.layer_stride = L.layer_stride;
+    a.wqkv = L.l_wqkv;
+    a.sqkv = L.l_sqkv;
+    a.wo = L.l_wo;
+    a.so = L.l_so;
+    a.wgu = L.l_wgu;
+    a.sgu = L.l_sgu;
+    a.wd = L.l_wd;
+    a.sd = L.l_sd;
+    a.attn_norm = L.l_attn_norm;
+    a.mlp_norm = L.l_mlp_norm;
+    a.q_norm = L.l_q_norm;
+    a.k_norm = L.l_k_norm;
+    a.embed = d.hidden_mode ? nullptr : m->arena + L.embed;
+    a.embed_scales = d.q8 && !d.hidden_mode ? at<float>(m, L.embed_scales) : nullptr;
+    a.rope_cos = at<float>(m, L.rope_cos);
+    a.rope_sin = at<float>(m, L.rope_sin);
+    const size_t seq_stride = (size_t)d.L * d.HKV * d.max_ctx * kHeadDim;
+    a.kcache = at<uint16_t>(m, L.kcache) + (size_t)seq * seq_stride;
+    a.vcache = at<uint16_t>(m, L.vcache) + (size_t)seq * seq_stride;
+    a.kv_layer_stride = (long long)d.HKV * d.max_ctx * kHeadDim;
+    a.max_ctx = d.max_ctx;
+    a.len = at<int>(m, L.len) + seq;
+    a.token = token;
+    a.hidden_in = hidden_in;
+    a.x_out = x_out;
+    a.status = at<int>(m, L.status);
+    a.epoch = at<uint32_t>(m, L.epoch);
+    a.xo = at<uint64_t>(m, L.x_o);
+    a.xd = at<uint64_t>(m, L.x_d);
+    a.qkv = at<uint64_t>(m, L.qkv_x);
+    a.part = at<uint64_t>(m, L.part_x);
+    a.attn = at<uint64_t>(m, L.attn_x);
+    a.act = at<uint64_t>(m, L.act_x);
+    a.L = d.L;
+    a.HQ = d.HQ;
+    a.HKV = d.HKV;
+    a.I = d.I;
+    a.V = d.V;
+    a.eps = d.eps;
+    return dev(launch_decode_mega(d.q8, d.G, a, st));
+}
+
 static int32_t run_logits(Model *m, int seq0, int S, const float *xin, float *logits, int *argmax, int commit_add,
                           hipStream_t st) {
     const Dims &d = m->d;
@@ -607,9 +673,13 @@ static int32_t enqueue_decode_step(Model *m, const int32_t *tokens_dev, float *l
                                    hipStream_t st) {
     const Dims &d = m->d;
     const Layout &L = m->lay;
-    QW3_HIP(launch_embed(d.q8, m->arena + L.embed, d.q8 ? at<float>(m, L.embed_scales) : nullptr, d.H, tokens_dev, d.S,
-                         at<float>(m, L.x), at<int>(m, L.status), d.V, st));
-    QW3_TRY(run_layers_decode(m, 0, d.S, st));
+    if (m->mega && d.S == 1) {
+        QW3_TRY(run_layers_mega(m, 0, tokens_dev, nullptr, at<float>(m, L.x), st));
+    } else {
+        QW3_HIP(launch_embed(d.q8, m->arena + L.embed, d.q8 ? at<float>(m, L.embed_scales) : nullptr, d.H, tokens_dev,
+                             d.S, at<float>(m, L.x), at<int>(m, L.status), d.V, st));
+        QW3_TRY(run_layers_decode(m, 0, d.S, st));
+    }
     return run_logits(m, 0, d.S, at<float>(m, L.x), logits_dev ? logits_dev : at<float>(m, L.logits), argmax_dev, 1,
                       st);
 }
@@ -688,9 +758,13 @@ int32_t qw3_prefill(uint64_t h, int32_t seq, const int32_t *tokens_dev, int32_t 
     } else {
         // Q8: token by token through the decode kernels (only the last position computes logits)
         for (int t = 0; t < n_tokens; ++t) {
-            QW3_HIP(launch_embed(true, m->arena + L.embed, at<float>(m, L.embed_scales), d.H, tokens_dev + t, 1,
-                                 at<float>(m, L.x), at<int>(m, L.status), d.V, st));
-            QW3_TRY(run_layers_decode(m, seq, 1, st));
+            if (m->mega) {
+                QW3_TRY(run_layers_mega(m, seq, tokens_dev + t, nullptr, at<float>(m, L.x), st));
+            } else {
+                QW3_HIP(launch_embed(true, m->arena + L.embed, at<float>(m, L.embed_scales), d.H, tokens_dev + t, 1,
+                                     at<float>(m, L.x), at<int>(m, L.status), d.V, st));
+                QW3_TRY(run_layers_decode(m, seq, 1, st));
+            }
             if (t == n_tokens - 1)
                 QW3_TRY(run_logits(m, seq, 1, at<float>(m, L.x), logits, argmax, 1, st));
             else
@@ -715,8 +789,16 @@ int32_t qw3_block_forward(uint64_t h, const float *hidden_in_dev, int32_t n_toke
     float *x = at<float>(m, L.x);
     for (int t0 = 0; t0 < n_tokens; t0 += d.max_prefill) {
         const int T = n_tokens - t0 < d.max_prefill ? n_tokens - t0 : d.max_prefill;
-        QW3_HIP(hipMemcpyAsync(x, hidden_in_dev + (size_t)t0 * d.H, (size_t)T * d.H * 4, hipMemcpyDeviceToDevice, st));
-        if (T == 1 || d.q8) {
+        if (!(m->mega && (T == 1 || d.q8)))
+            QW3_HIP(hipMemcpyAsync(x, hidden_in_dev + (size_t)t0 * d.H, (size_t)T * d.H * 4, hipMemcpyDeviceToDevice,
+                                   st));
+        if (m->mega && (T == 1 || d.q8)) {
+            for (int t = 0; t < T; ++t) {
+                QW3_TRY(run_layers_mega(m, 0, nullptr, hidden_in_dev + (size_t)(t0 + t) * d.H,
+                                        hidden_out_dev + (size_t)(t0 + t) * d.H, st));
+                QW3_HIP(launch_commit(at<int>(m, L.len), 1, 1, st));
+            }
+        } else if (T == 1 || d.q8) {
             for (int t = 0; t < T; ++t) {
                 if (t) QW3_HIP(hipMemcpyAsync(x, hidden_in_dev + (size_t)(t0 + t) * d.H, (size_t)d.H * 4,
                                               hipMemcpyDeviceToDevice, st));
@@ -814,7 +896,8 @@ int32_t qw3_bench_kernel(uint64_t h, int32_t kernel, int32_t layer, int32_t reps
     QW3_TRY(check_ready(m));
     const Dims &d = m->d;
     if (layer < 0 || layer >= d.L || reps < 1) return QW3_INVALID_ARGUMENT;
-    if (kernel < DK_QKV || kernel > 6 || (kernel == 6 && d.hidden_mode)) return QW3_INVALID_ARGUMENT;
+    if (kernel < DK_QKV || kernel > 7 || (kernel == 6 && d.hidden_mode)) return QW3_INVALID_ARGUMENT;
+    if (kernel == 7 && !(m->mega && d.S == 1)) return QW3_INVALID_ARGUMENT;
     for (int s = 0; s < d.S; ++s)
         if (m->len[s] >= d.max_ctx) return QW3_CONTEXT_EXCEEDED;
     hipStream_t st = (hipStream_t)stream;
@@ -822,6 +905,8 @@ int32_t qw3_bench_kernel(uint64_t h, int32_t kernel, int32_t layer, int32_t reps
     for (int r = 0; r < reps; ++r) {
         if (kernel <= DK_DOWN)
             QW3_TRY(launch_decode_kernel(m, kernel, (layer + r) % d.L, 0, d.S, st));
+        else if (kernel == 7)  // whole layer stack, in place on the scratch hidden state
+            QW3_TRY(run_layers_mega(m, 0, nullptr, at<float>(m, m->lay.x), at<float>(m, m->lay.x), st));
         else
             QW3_TRY(run_logits(m, 0, d.S, at<float>(m, m->lay.x), at<float>(m, m->lay.logits), at<int>(m, m->lay.tokens),
                                0, st));

@@ -12,6 +12,8 @@ constexpr int kMaxSeq = 16;
 constexpr int kMaxSplit = 64;          // decode attention splits of the context per (seq, kv head)
 constexpr int kPartStride = 2 + kHeadDim;  // per split partial: running max, running sum, o[128]
 constexpr int kLmMaxBlocks = 16384;    // upper bound on lm_head workgroups (argmax partials)
+constexpr int kMegaGrid = 256;         // resident workgroups of the single-launch decode kernel
+constexpr int kMegaWaves = 4;          // its waves per workgroup
 
 // Byte offsets of every region inside the caller's arena.  Per-layer weight blocks repeat with a fixed
 // stride, so layer l's block starts at layer0 + l * layer_stride.
@@ -27,6 +29,8 @@ struct Layout {
     uint64_t kcache, vcache;
     // state
     uint64_t len, status;
+    // single-launch decode: epoch tag base and the tagged exchange words (f32 value | tag << 32)
+    uint64_t epoch, x_o, x_d, qkv_x, part_x, attn_x, act_x;
     // scratch
     uint64_t x, xn16, qkv, q16, attn, attn16, act, act16, part, argpart, logits, tokens;
     uint64_t weights_end, kv_end, state_end, scratch_end;
@@ -62,6 +66,40 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_nt16(const void *p) {
     const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)p);
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// DPP lane moves (VALU; no LDS round trip).  Controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
+// row_half_mirror = 0x141, row_mirror = 0x140 (a row is 16 lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+// Sum over the 16 lanes of each row, in every lane of the row.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    v += dpp_mov<0x140>(v);
+    return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    v = fmaxf(v, dpp_mov<0x140>(v));
+    return v;
+}
+__device__ __forceinline__ float lane_get(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+// Whole-wave sum / max, wave-uniform result: row reductions on DPP, then the four row results.
+__device__ __forceinline__ float wave_sum_fast(float v) {
+    v = row16_sum(v);
+    return (lane_get(v, 0) + lane_get(v, 16)) + (lane_get(v, 32) + lane_get(v, 48));
+}
+__device__ __forceinline__ float wave_max_fast(float v) {
+    v = row16_max(v);
+    return fmaxf(fmaxf(lane_get(v, 0), lane_get(v, 16)), fmaxf(lane_get(v, 32), lane_get(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -116,10 +154,35 @@ struct AttnDecodeArgs {
 };
 hipError_t launch_attn_decode(int G, const AttnDecodeArgs &a, hipStream_t st);
 
+// Single-launch decode of one token of one sequence (hidden size 1024): the whole layer stack in one
+// persistent grid of kMegaGrid workgroups (see mega.hip).
+struct MegaArgs {
+    const uint8_t *layer0;  // first layer block; layer l at layer0 + l * layer_stride
+    uint64_t layer_stride;
+    uint64_t wqkv, sqkv, wo, so, wgu, sgu, wd, sd, attn_norm, mlp_norm, q_norm, k_norm;  // offsets in a block
+    const void *embed;
+    const float *embed_scales;
+    const float *rope_cos, *rope_sin;
+    uint16_t *kcache, *vcache;   // (sequence, layer 0, KV head 0)
+    long long kv_layer_stride;   // elements between consecutive layers of the sequence
+    int max_ctx;
+    const int *len;              // committed length of the sequence (= position of the new token)
+    const int *token;            // token id (token mode) or nullptr
+    const float *hidden_in;      // f32 [1024] input (hidden mode) or nullptr
+    float *x_out;                // f32 [1024] output of the layer stack
+    int *status;
+    uint32_t *epoch;             // tag base; advanced by the launch for the next one
+    uint64_t *xo, *xd, *qkv, *part, *attn, *act;  // tagged exchange words
+    int L, HQ, HKV, I, V;
+    float eps;
+};
+bool mega_supported(const Dims &d);
+hipError_t launch_decode_mega(bool q8, int G, const MegaArgs &a, hipStream_t st);
+
 hipError_t launch_embed(bool q8, const void *table, const float *scales, int H, const int *tokens, int S, float *x,
                         int *status, int vocab, hipStream_t st);
 hipError_t launch_set_lens(int *len_dev, int n, const int *vals, int mask, int *status, int clear_status,
-                           hipStream_t st);
+                           uint32_t *epoch, hipStream_t st);
 hipError_t launch_commit(int *len_dev, int n, int add, hipStream_t st);
 hipError_t launch_dequant(bool q8, const void *w, const float *scales, long long rows, int cols, float *out,
                           hipStream_t st);

@@ -761,10 +761,16 @@ struct LenVals {
     int v[kMaxSeq];
 };
 
-__global__ void set_lens_kernel(int *len, int n, LenVals vals, int mask, int *status, int clear_status) {
+__global__ void set_lens_kernel(int *len, int n, LenVals vals, int mask, int *status, int clear_status,
+                                uint32_t *epoch) {
     const int t = threadIdx.x;
     if (t < n && (mask >> t) & 1) len[t] = vals.v[t];
-    if (t == 0 && clear_status) *status = 0;
+    if (t == 0 && clear_status) {
+        *status = 0;
+        // a launch of the single-launch decode that gave up did not advance the tag base: move it past any
+        // word that launch may have written
+        *epoch += 1u << 20;
+    }
 }
 
 __global__ void commit_kernel(int *len, int n, int add) {
@@ -827,10 +833,10 @@ hipError_t launch_embed(bool q8, const void *table, const float *scales, int H, 
 }
 
 hipError_t launch_set_lens(int *len_dev, int n, const int *vals, int mask, int *status, int clear_status,
-                           hipStream_t st) {
+                           uint32_t *epoch, hipStream_t st) {
     LenVals v{};
     for (int i = 0; i < n && i < kMaxSeq; ++i) v.v[i] = vals[i];
-    hipLaunchKernelGGL(set_lens_kernel, dim3(1), dim3(64), 0, st, len_dev, n, v, mask, status, clear_status);
+    hipLaunchKernelGGL(set_lens_kernel, dim3(1), dim3(64), 0, st, len_dev, n, v, mask, status, clear_status, epoch);
     return hipGetLastError();
 }
 

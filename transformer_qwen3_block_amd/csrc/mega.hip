@@ -1,0 +1,703 @@
+// Persistent single-launch decode of one token of one sequence for gfx950 (hidden size 1024, head_dim 128).
+//
+// One launch runs the whole layer stack of [P1] section 5 ("Transformer Layer Execution Loop") for one token:
+// 256 workgroups stay resident and walk six dependent phases per layer,
+//   Q  RMSNorm + Q/K/V rows                 ([P1] section 2 items 1-2)
+//   A  QK-Norm, RoPE, KV append, attention   (items 3-5; one workgroup per (KV head, context split))
+//   M  merge of the context splits           (item 5, exact online-softmax combination)
+//   O  o_proj + residual                     (item 6)
+//   U  RMSNorm + gate/up + SwiGLU            (items 6-7)
+//   D  down + residual                       (item 7)
+// Every phase is spread over all 1024 waves of the grid; phase outputs travel between workgroups as 8-byte
+// words (f32 value, 32-bit epoch tag) written and polled with device-coherent relaxed atomics, so a consumer
+// needs no separate flag: a word is ready when its tag equals the tag of (layer, phase) in this launch.
+// While a workgroup waits for a phase's inputs, that phase's weights (and, for attention, the cached K/V of
+// the old positions) are already in flight into registers: weight streaming from HBM overlaps the exchange
+// latency instead of following it.  Hidden row r (r < 1024) is owned by global wave r in the o_proj and down
+// phases, which keeps the residual stream of that row in a register.
+//
+// Every wait is bounded (a fixed number of polling rounds, tens of milliseconds).  A workgroup that times out sets bit 4 of
+// the status word; every poll also watches that bit, so the whole grid leaves promptly and the status word
+// reports a device error instead of a hang.
+//
+// Page titles used in citations:
+//   [P1] "Scalar-Native Qwen3 Reference Runtime As The Numerical Authority"
+//   [P4] "Portable WebAssembly Runtime Architecture for TinyRustLM"
+#include <math.h>
+
+#include "common.h"
+
+namespace qw3 {
+
+namespace {
+
+constexpr int kWaves = kMegaWaves;
+constexpr int kNW = kMegaGrid * kWaves;  // waves in the grid
+constexpr int kHid = 1024;               // hidden size of this kernel (= kNW: one owned row per wave)
+// Poll bound: rounds of device-coherent loads (each at least one memory round trip, well over 0.25 us), so
+// 2^18 rounds outlast 50 ms while a legitimate wait lasts microseconds.
+constexpr int kPollRounds = 1 << 18;
+constexpr int kStatusTimeout = 4;
+constexpr int kMegaBuf = 3072;  // floats per LDS input buffer (largest phase input: intermediate <= 3072)
+
+static_assert(kHid == kNW, "one hidden row per wave");
+
+__device__ __forceinline__ void put(uint64_t *p, float v, uint32_t tag) {
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t get(const uint64_t *p) {
+    return __hip_atomic_load((uint64_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool timed_out(int *status) {
+    return (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusTimeout) != 0;
+}
+
+__device__ __forceinline__ void unpack_i8x16(const uint4 &w, float (&o)[16]) {
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) o[4 * j + b] = (float)(int8_t)(d[j] >> (8 * b));
+}
+__device__ __forceinline__ void unpack_bf16x8(const uint4 &w, float (&o)[8]) {
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        o[2 * j] = bf16_lo(d[j]);
+        o[2 * j + 1] = bf16_hi(d[j]);
+    }
+}
+
+// Waits until the n tagged words src(i), i < n, all carry `tag` and writes their values to dst[i] (LDS).
+// Thread t polls words t, t + 256, ...; words already seen are not loaded again.  Starts with a workgroup
+// barrier, so earlier readers of dst have finished.  Returns false on timeout or when another workgroup has
+// reported one.
+template <int NPT, typename Addr>
+__device__ __forceinline__ bool poll(Addr src, int n, uint32_t tag, float *dst, int *status) {
+    const int tid = threadIdx.x;
+    uint32_t pending = 0;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j)
+        if (tid + 256 * j < n) pending |= 1u << j;
+    __syncthreads();  // earlier readers of dst are done
+    for (int round = 0; pending; ++round) {
+        uint64_t v[NPT];
+#pragma unroll
+        for (int j = 0; j < NPT; ++j)
+            if ((pending >> j) & 1u) v[j] = get(src(tid + 256 * j));
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) {
+            if (((pending >> j) & 1u) && (uint32_t)(v[j] >> 32) == tag) {
+                dst[tid + 256 * j] = __uint_as_float((uint32_t)v[j]);
+                pending &= ~(1u << j);
+            }
+        }
+        // another workgroup's timeout is checked now and then; this one's after the round bound
+        if (pending && (round >= kPollRounds || ((round & 31) == 31 && timed_out(status)))) return false;
+    }
+    return true;
+}
+
+// Workgroup-wide agreement after a poll: true when every thread's poll succeeded.
+__device__ __forceinline__ bool all_ok(bool ok, int *s_fail, int *status) {
+    if (!ok) *(volatile int *)s_fail = 1;
+    __syncthreads();
+    if (*(volatile int *)s_fail) {
+        if (threadIdx.x == 0) atomicOr(status, kStatusTimeout);
+        return false;
+    }
+    return true;
+}
+
+// Weight rows -> registers.  Lane `lane` holds, for chunk c of a row, the 16-byte slice starting at element
+// c*64*E + lane*E (E = 16 int8 codes or 8 bf16 values), and for Q8 the scale of that slice's 32-block.
+// Every slot is loaded, unconditionally: slots of absent rows or chunks read row 0 / chunk 0 and are never
+// used.  A fixed number of loads per call lets the compiler wait for exactly the loads a computation needs
+// (the vector memory counter drains in issue order), instead of for everything in flight.
+template <int Q8, int R, int C>
+__device__ __forceinline__ void load_rows(const uint8_t *w, const float *s, int K, const int (&row)[R],
+                                          const bool (&rv)[R], int nch, int lane, uint4 (&wv)[R][C],
+                                          float (&sc)[R][C]) {
+    constexpr int E = Q8 ? 16 : 8;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const size_t rr = rv[r] ? (size_t)row[r] : 0;
+            const int k = (c < nch ? c : 0) * 64 * E + lane * E;
+            wv[r][c] = load_nt16(w + (rr * K + k) * (Q8 ? 1 : 2));
+            if constexpr (Q8) sc[r][c] = s[rr * (K / 32) + (k >> 5)];
+            else sc[r][c] = 0.f;
+        }
+}
+
+// Lane's share of one row's dot product with the input vector xl (LDS), chunks c < nch.
+template <int Q8, int C>
+__device__ __forceinline__ float dot_lds(const uint4 (&wv)[C], const float (&sc)[C], const float *xl, int nch,
+                                         int lane) {
+    constexpr int E = Q8 ? 16 : 8;
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        if (c < nch) {
+            const float4 *xp = (const float4 *)(xl + c * 64 * E + lane * E);
+            float xv[E];
+#pragma unroll
+            for (int q = 0; q < E / 4; ++q) {
+                const float4 v = xp[q];
+                xv[4 * q] = v.x;
+                xv[4 * q + 1] = v.y;
+                xv[4 * q + 2] = v.z;
+                xv[4 * q + 3] = v.w;
+            }
+            if constexpr (Q8) {
+                float wf[16];
+                unpack_i8x16(wv[c], wf);
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) d += wf[e] * xv[e];
+                acc += d * sc[c];
+            } else {
+                float wf[8];
+                unpack_bf16x8(wv[c], wf);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc += wf[e] * xv[e];
+            }
+        }
+    }
+    return acc;
+}
+
+// Lane's share of a row's dot product with inputs held in registers (K = 1024: CH chunks of E values).
+template <int Q8, int CH>
+__device__ __forceinline__ float dot_reg(const uint4 (&wv)[CH], const float (&sc)[CH], const float (&xr)[CH][Q8 ? 16 : 8]) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        if constexpr (Q8) {
+            float wf[16];
+            unpack_i8x16(wv[c], wf);
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) d += wf[e] * xr[c][e];
+            acc += d * sc[c];
+        } else {
+            float wf[8];
+            unpack_bf16x8(wv[c], wf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc += wf[e] * xr[c][e];
+        }
+    }
+    return acc;
+}
+
+// Lane's slice of a 1024-long f32 vector (the elements that lane's weight chunks multiply).
+template <int Q8, int CH>
+__device__ __forceinline__ void load_slice(const float *v, int lane, float (&out)[CH][Q8 ? 16 : 8]) {
+    constexpr int E = Q8 ? 16 : 8;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+            const float4 t = *(const float4 *)(v + c * 64 * E + lane * E + 4 * q);
+            out[c][4 * q] = t.x;
+            out[c][4 * q + 1] = t.y;
+            out[c][4 * q + 2] = t.z;
+            out[c][4 * q + 3] = t.w;
+        }
+}
+
+// RMSNorm of the 1024-vector xs (LDS) with weight slice w ([P1] section 2 items 1 and 6: w * (x / sqrt(mean(x^2)
+// + eps))), returning the lane's slice in registers.  Every wave reduces the whole vector itself.
+template <int Q8, int CH>
+__device__ __forceinline__ void rms_slice(const float *xs, const float (&w)[CH][Q8 ? 16 : 8], float eps, int lane,
+                                          float (&xr)[CH][Q8 ? 16 : 8]) {
+    constexpr int E = Q8 ? 16 : 8;
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < kHid / 64; ++k) {
+        const float v = xs[lane + 64 * k];
+        ss += v * v;
+    }
+    ss = wave_sum_fast(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)kHid + eps);
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int e = 0; e < E; ++e) xr[c][e] = w[c][e] * (xs[c * 64 * E + lane * E + e] * inv);
+}
+
+// Cached K/V of one 16-position group for this lane (positions 16*gi + 4*i + lane/16, dims (lane%16)*8..+8).
+// Always eight loads: slots of positions at or after `pos` (the new position is written in this launch and
+// taken from LDS) or of groups past the split read position 0 and are replaced before use.
+__device__ __forceinline__ void load_group(const uint16_t *kb, const uint16_t *vb, int gi, int gend, int pos,
+                                           int lane, uint4 (&kr)[4], uint4 (&vr)[4]) {
+    const int dsub = (lane & 15) * 8, prow = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = 16 * gi + 4 * i + prow;
+        const size_t pc = (gi < gend && p < pos) ? (size_t)p : 0;
+        kr[i] = load_nt16(kb + pc * kHeadDim + dsub);
+        vr[i] = load_nt16(vb + pc * kHeadDim + dsub);
+    }
+}
+
+// Online-softmax update with one 16-position group of cached positions ([P1] section 2 item 5; running max m,
+// running sum l, unnormalised accumulator acc; each lane row keeps its own l and acc).
+template <int G>
+__device__ __forceinline__ void attend_group(uint4 (&kr)[4], uint4 (&vr)[4], int gi, int pos, int lane,
+                                             const float (&qr)[G][8], float sl2, float (&m)[G], float (&l)[G],
+                                             float (&acc)[G][8]) {
+    const int prow = lane >> 4;
+    bool val[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = 16 * gi + 4 * i + prow;
+        val[i] = p < pos;
+        if (!val[i]) {  // placeholder slot: keep stale cache bits out of the sums
+            kr[i] = make_uint4(0, 0, 0, 0);
+            vr[i] = make_uint4(0, 0, 0, 0);
+        }
+    }
+    float sc[G][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float kf[8];
+        unpack_bf16x8(kr[i], kf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d += qr[h][e] * kf[e];
+            d = row16_sum(d);  // the 16 lanes of a row hold one position's dims
+            sc[h][i] = val[i] ? d * sl2 : -INFINITY;
+        }
+    }
+    float vf[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unpack_bf16x8(vr[i], vf[i]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float tm = fmaxf(fmaxf(sc[h][0], sc[h][1]), fmaxf(sc[h][2], sc[h][3]));  // uniform within a row
+        tm = fmaxf(fmaxf(lane_get(tm, 0), lane_get(tm, 16)), fmaxf(lane_get(tm, 32), lane_get(tm, 48)));
+        const float mn = fmaxf(m[h], tm);
+        if (mn == -INFINITY) continue;  // nothing valid yet in this lane row set
+        const float alpha = expf(m[h] - mn);
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+        m[h] = mn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = expf(sc[h][i] - mn);
+            l[h] += p;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] += p * vf[i][e];
+        }
+    }
+}
+
+// Online-softmax update with the new position (key kn, value vn in LDS, already rounded to bf16); lane row 0
+// carries its weight.
+template <int G>
+__device__ __forceinline__ void attend_new(const float *kn, const float *vn, int lane, const float (&qr)[G][8],
+                                           float sl2, float (&m)[G], float (&l)[G], float (&acc)[G][8]) {
+    const int dsub = (lane & 15) * 8;
+    const bool row0 = lane < 16;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d += qr[h][e] * kn[dsub + e];
+        const float sc = row16_sum(d) * sl2;  // every row computes the same full dot product
+        const float mn = fmaxf(m[h], sc);
+        const float alpha = expf(m[h] - mn), p = expf(sc - mn);
+        l[h] = l[h] * alpha + (row0 ? p : 0.f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] * alpha + (row0 ? p * vn[dsub + e] : 0.f);
+        m[h] = mn;
+    }
+}
+
+}  // namespace
+
+template <int Q8, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_mega_kernel(MegaArgs a) {
+    constexpr int E = Q8 ? 16 : 8;
+    constexpr int CH = kHid / (64 * E);  // chunks per lane of a 1024-long row
+    constexpr int KO_MAX = Q8 ? 2 : 4;   // q_dim <= 2048
+    constexpr int KD_MAX = Q8 ? 3 : 6;   // intermediate <= 3072
+    constexpr int RQ_MAX = 4;            // Q/K/V rows per wave (<= 4096 rows)
+    constexpr int RU_MAX = 3;            // gate/up units per wave (<= 3072 units)
+    constexpr int PW = 2 + kHeadDim;     // words of one attention partial (max, sum, o[128])
+
+    __shared__ __attribute__((aligned(16))) float xs[kHid];
+    __shared__ __attribute__((aligned(16))) float big[4096];
+    __shared__ float wm[kWaves][G], wl[kWaves][G];
+    __shared__ int s_fail;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int b = blockIdx.x;
+    const int gw = b * kWaves + wave;  // global wave id = owned hidden row
+    const int HQ = a.HQ, HKV = a.HKV, I = a.I;
+    const int q_dim = HQ * kHeadDim, kv_dim = HKV * kHeadDim, Nqkv = q_dim + 2 * kv_dim;
+    const int KO = q_dim / (64 * E), KD = I / (64 * E);
+    const int SP = kMegaGrid / HKV;  // context splits per KV head
+    const uint32_t ep = a.epoch[0];
+    const int pos = a.len[0];
+    if (tid == 0) s_fail = 0;
+
+    // this workgroup's attention share: KV head g, split sp.  The cached positions [0, pos) form 16-position
+    // groups dealt round-robin to the 4 * SP waves of the head (wave slot ws takes groups ws, ws + 4 SP, ...);
+    // the new position goes to wave slot ngroups mod 4 SP, whose workgroup also appends it to the cache.
+    const int g = b % HKV, sp = b / HKV;
+    const int nslot = kWaves * SP, ws = sp * kWaves + wave;
+    const int ngroups = (pos + 15) / 16;
+    const int ws_new = ngroups % nslot;
+    const size_t kv_head_off = (size_t)g * a.max_ctx * kHeadDim;
+
+    auto lblock = [&](int l) { return a.layer0 + (size_t)l * a.layer_stride; };
+    // tags of this launch: ep + 1 .. ep + 8L + 6 (the zeroed words of a fresh arena never match)
+    auto tag = [&](int l, int ph) { return ep + 8u * (uint32_t)l + (uint32_t)ph + 1u; };
+
+    // ---- register prefetch state.  Each phase first waits for its inputs, then issues the next phase's
+    // weight loads, then computes: a wait never covers loads issued less than a phase earlier (the vector
+    // memory counter drains in issue order, so a poll also waits for every older load).
+    int rq[RQ_MAX];
+    bool rqv[RQ_MAX];
+#pragma unroll
+    for (int j = 0; j < RQ_MAX; ++j) {
+        rq[j] = gw + kNW * j;
+        rqv[j] = rq[j] < Nqkv;
+    }
+    int ru[2 * RU_MAX];
+    bool ruv[2 * RU_MAX];
+#pragma unroll
+    for (int j = 0; j < RU_MAX; ++j) {
+        const int u = gw + kNW * j;
+        ru[2 * j] = u;
+        ru[2 * j + 1] = I + u;
+        ruv[2 * j] = ruv[2 * j + 1] = u < I;
+    }
+    const int ro[1] = {gw};
+    const bool rov[1] = {true};
+
+    uint4 wq[RQ_MAX][CH];
+    float sq[RQ_MAX][CH];
+    uint4 wo[1][KO_MAX];
+    float so[1][KO_MAX];
+    uint4 wu[2 * RU_MAX][CH];
+    float su[2 * RU_MAX][CH];
+    uint4 wd[1][KD_MAX];
+    float sd[1][KD_MAX];
+    uint4 kA[4], vA[4], kB[4], vB[4];
+    float nq[CH][E], nu[CH][E];  // RMSNorm weight slices of the Q and U phases
+    float qkn[4], rcs[2];        // QK-Norm weights (q: lane, lane + 64; k: same) and this position's cos/sin
+
+    // ---- prologue: layer-0 Q/K/V weights in flight, then the input vector (every workgroup builds it all)
+    load_rows<Q8, RQ_MAX, CH>(a.layer0 + a.wqkv, (const float *)(a.layer0 + a.sqkv), kHid, rq, rqv, CH, lane, wq, sq);
+    load_slice<Q8, CH>((const float *)(a.layer0 + a.attn_norm), lane, nq);
+    if (a.token) {
+        int tok = a.token[0];
+        if (tok < 0 || tok >= a.V) {
+            if (b == 0 && tid == 0) atomicOr(a.status, 2);
+            tok = 0;
+        }
+        for (int k = tid; k < kHid; k += 256) {
+            const size_t i = (size_t)tok * kHid + k;
+            xs[k] = Q8 ? (float)((const int8_t *)a.embed)[i] * a.embed_scales[i >> 5]
+                       : bf16_to_f32(((const uint16_t *)a.embed)[i]);
+        }
+    } else {
+        for (int k = tid; k < kHid; k += 256) xs[k] = a.hidden_in[k];
+    }
+    __syncthreads();
+    float x_own = xs[gw];  // residual stream of the owned row
+
+    const int dsub = (lane & 15) * 8;
+    // score scale f32(1/sqrt(128)) applied to the finished dot product, natural-exponent softmax with the
+    // full-precision expf: the same rounding points as the sequential definition
+    const float sl2 = 1.0f / sqrtf((float)kHeadDim);
+
+    for (int l = 0; l < a.L; ++l) {
+        const uint8_t *lb = lblock(l);
+        const uint16_t *kb = a.kcache + (size_t)l * a.kv_layer_stride + kv_head_off;
+        const uint16_t *vb = a.vcache + (size_t)l * a.kv_layer_stride + kv_head_off;
+        // ================= Q: RMSNorm + Q/K/V rows
+        if (l > 0) {
+            const uint64_t *src = a.xd;
+            const bool ok = poll<4>([&](int i) { return src + i; }, kHid, tag(l - 1, 5), xs, a.status);
+            if (!all_ok(ok, &s_fail, a.status)) return;
+        }
+        {
+            const float *qnw = (const float *)(lb + a.q_norm), *knw = (const float *)(lb + a.k_norm);
+            qkn[0] = qnw[lane];
+            qkn[1] = qnw[lane + 64];
+            qkn[2] = knw[lane];
+            qkn[3] = knw[lane + 64];
+            rcs[0] = a.rope_cos[(size_t)pos * (kHeadDim / 2) + lane];
+            rcs[1] = a.rope_sin[(size_t)pos * (kHeadDim / 2) + lane];
+        }
+        load_group(kb, vb, ws, ngroups, pos, lane, kA, vA);
+        load_group(kb, vb, ws + nslot, ngroups, pos, lane, kB, vB);
+        {
+            float xr[CH][E];
+            rms_slice<Q8, CH>(xs, nq, a.eps, lane, xr);
+            float d[RQ_MAX];
+#pragma unroll
+            for (int j = 0; j < RQ_MAX; ++j) d[j] = wave_sum_fast(dot_reg<Q8, CH>(wq[j], sq[j], xr));
+#pragma unroll
+            for (int j = 0; j < RQ_MAX; ++j)
+                if (lane == j && rqv[j]) put(a.qkv + rq[j], d[j], tag(l, 0));
+        }
+
+        // ================= A: QK-Norm + RoPE + append + attention over this split
+        {
+            float *raw = big;       // [(G + 2) * 128]: q heads, k, v
+            float *qs = big + 768;  // [G][128] normalised, rotated queries
+            float *kn = big + 1280; // new key (bf16 value)
+            float *vn = big + 1408; // new value (bf16 value)
+            float *wacc = big + 1536;  // [4][G][128]
+            const uint64_t *qkv = a.qkv;
+            const int hq0 = g * G;
+            auto src = [&](int i) {
+                const int h = i >> 7, d = i & 127;
+                const int row = h < G ? (hq0 + h) * kHeadDim + d
+                                      : (h == G ? q_dim + g * kHeadDim + d : q_dim + kv_dim + g * kHeadDim + d);
+                return qkv + row;
+            };
+            const bool ok = poll<3>(src, (G + 2) * kHeadDim, tag(l, 0), raw, a.status);
+            if (!all_ok(ok, &s_fail, a.status)) return;
+            load_rows<Q8, 1, KO_MAX>(lb + a.wo, (const float *)(lb + a.so), q_dim, ro, rov, KO, lane, wo, so);
+
+            // QK-Norm ([P1] item 3, one 128-weight vector per projection) then RoPE on pairs (i, i + 64) at
+            // `pos` (item 4)
+            const float c = rcs[0], s = rcs[1];
+            for (int h = wave; h <= G; h += kWaves) {
+                const float v0 = raw[h * kHeadDim + lane], v1 = raw[h * kHeadDim + lane + 64];
+                const float inv = 1.0f / sqrtf(wave_sum_fast(v0 * v0 + v1 * v1) / (float)kHeadDim + a.eps);
+                const float w0 = h < G ? qkn[0] : qkn[2], w1 = h < G ? qkn[1] : qkn[3];
+                const float n0 = w0 * (v0 * inv), n1 = w1 * (v1 * inv);
+                const float r0 = n0 * c - n1 * s, r1 = n1 * c + n0 * s;
+                if (h < G) {
+                    qs[h * kHeadDim + lane] = r0;
+                    qs[h * kHeadDim + lane + 64] = r1;
+                } else {
+                    // key and value rounded to the cache's bf16 ([P1] section 6 append); the split holding `pos`
+                    // writes them
+                    const uint16_t k0 = f32_to_bf16(r0), k1 = f32_to_bf16(r1);
+                    const uint16_t v0b = f32_to_bf16(raw[(G + 1) * kHeadDim + lane]);
+                    const uint16_t v1b = f32_to_bf16(raw[(G + 1) * kHeadDim + lane + 64]);
+                    kn[lane] = bf16_to_f32(k0);
+                    kn[lane + 64] = bf16_to_f32(k1);
+                    vn[lane] = bf16_to_f32(v0b);
+                    vn[lane + 64] = bf16_to_f32(v1b);
+                    if (sp == ws_new / kWaves) {
+                        uint16_t *kc = (uint16_t *)kb + (size_t)pos * kHeadDim;
+                        uint16_t *vc = (uint16_t *)vb + (size_t)pos * kHeadDim;
+                        kc[lane] = k0;
+                        kc[lane + 64] = k1;
+                        vc[lane] = v0b;
+                        vc[lane + 64] = v1b;
+                    }
+                }
+            }
+            __syncthreads();
+
+            float qr[G][8];
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qr[h][e] = qs[h * kHeadDim + dsub + e];
+            float m[G], lsum[G], acc[G][8];
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                m[h] = -INFINITY;
+                lsum[h] = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+            }
+            // two register slots, each refilled once consumed
+            for (int gi = ws; gi < ngroups; gi += 2 * nslot) {
+                attend_group<G>(kA, vA, gi, pos, lane, qr, sl2, m, lsum, acc);
+                load_group(kb, vb, gi + 2 * nslot, ngroups, pos, lane, kA, vA);
+                if (gi + nslot >= ngroups) break;
+                attend_group<G>(kB, vB, gi + nslot, pos, lane, qr, sl2, m, lsum, acc);
+                load_group(kb, vb, gi + 3 * nslot, ngroups, pos, lane, kB, vB);
+            }
+            if (ws == ws_new) attend_new<G>(kn, vn, lane, qr, sl2, m, lsum, acc);
+            // merge the wave's four position rows (the running max is wave-uniform), then the four waves
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float lv = lsum[h];
+                lv += __shfl_xor(lv, 16, 64);
+                lv += __shfl_xor(lv, 32, 64);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float av = acc[h][e];
+                    av += __shfl_xor(av, 16, 64);
+                    av += __shfl_xor(av, 32, 64);
+                    acc[h][e] = av;
+                }
+                if (lane < 16) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) wacc[(wave * G + h) * kHeadDim + dsub + e] = acc[h][e];
+                }
+                if (lane == 0) {
+                    wm[wave][h] = m[h];
+                    wl[wave][h] = lv;
+                }
+            }
+            __syncthreads();
+            uint64_t *pp = a.part + ((size_t)(g * SP + sp) * G) * PW;
+            for (int t = tid; t < G * kHeadDim; t += 256) {
+                const int h = t >> 7, d = t & 127;
+                float M = -INFINITY;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w][h]);
+                float Ls = 0.f, O = 0.f;
+                if (M != -INFINITY) {
+#pragma unroll
+                    for (int w = 0; w < kWaves; ++w) {
+                        const float f = expf(wm[w][h] - M);
+                        Ls += f * wl[w][h];
+                        O += f * wacc[(w * G + h) * kHeadDim + d];
+                    }
+                }
+                uint64_t *ph = pp + (size_t)h * PW;
+                if (d == 0) {
+                    put(ph, M, tag(l, 1));
+                    put(ph + 1, Ls, tag(l, 1));
+                }
+                put(ph + 2 + d, O, tag(l, 1));
+            }
+        }
+
+        // ================= M: merge of the context splits of one query head, dpw output dims per workgroup
+        {
+            const int wph = kMegaGrid / HQ;  // workgroups per query head
+            const int dpw = kHeadDim / wph;  // dims per workgroup
+            const int h = b / wph, dc = b % wph;
+            const int gh = h / G, hh = h % G;
+            const int per = 2 + dpw;
+            const uint64_t *part = a.part;
+            auto src = [&](int i) {
+                const int s = i / per, j = i % per;
+                const size_t base = ((size_t)(gh * SP + s) * G + hh) * PW;
+                return part + base + (j < 2 ? j : 2 + dc * dpw + (j - 2));
+            };
+            const bool ok = poll<kMegaBuf / 256>(src, SP * per, tag(l, 1), big, a.status);
+            if (!all_ok(ok, &s_fail, a.status)) return;
+            load_rows<Q8, 2 * RU_MAX, CH>(lb + a.wgu, (const float *)(lb + a.sgu), kHid, ru, ruv, CH, lane, wu, su);
+            load_slice<Q8, CH>((const float *)(lb + a.mlp_norm), lane, nu);
+            // exact combination in fixed split order: M = max m_s, o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s
+            for (int e = wave; e < dpw; e += kWaves) {
+                float M = -INFINITY;
+                for (int s = lane; s < SP; s += 64) M = fmaxf(M, big[s * per]);
+                M = wave_max_fast(M);
+                float Ls = 0.f, O = 0.f;
+                for (int s = lane; s < SP; s += 64) {
+                    const float ms = big[s * per];
+                    const float f = ms == -INFINITY ? 0.f : expf(ms - M);
+                    Ls += f * big[s * per + 1];
+                    O += f * big[s * per + 2 + e];
+                }
+                Ls = wave_sum_fast(Ls);
+                O = wave_sum_fast(O);
+                if (lane == 0) put(a.attn + h * kHeadDim + dc * dpw + e, O / Ls, tag(l, 2));
+            }
+        }
+
+        // ================= O: o_proj + residual on the owned row
+        {
+            const uint64_t *src = a.attn;
+            const bool ok = poll<8>([&](int i) { return src + i; }, q_dim, tag(l, 2), big, a.status);
+            if (!all_ok(ok, &s_fail, a.status)) return;
+            load_rows<Q8, 1, KD_MAX>(lb + a.wd, (const float *)(lb + a.sd), I, ro, rov, KD, lane, wd, sd);
+            const float d = wave_sum_fast(dot_lds<Q8, KO_MAX>(wo[0], so[0], big, KO, lane));
+            x_own = x_own + d;
+            if (lane == 0) put(a.xo + gw, x_own, tag(l, 3));
+        }
+
+        // ================= U: RMSNorm + gate/up + SwiGLU
+        {
+            const uint64_t *src = a.xo;
+            const bool ok = poll<4>([&](int i) { return src + i; }, kHid, tag(l, 3), xs, a.status);
+            if (!all_ok(ok, &s_fail, a.status)) return;
+            float xr[CH][E];
+            rms_slice<Q8, CH>(xs, nu, a.eps, lane, xr);
+            if (l + 1 < a.L) {
+                const uint8_t *nb = lblock(l + 1);
+                load_rows<Q8, RQ_MAX, CH>(nb + a.wqkv, (const float *)(nb + a.sqkv), kHid, rq, rqv, CH, lane, wq, sq);
+                load_slice<Q8, CH>((const float *)(nb + a.attn_norm), lane, nq);
+            }
+            float av[RU_MAX];
+#pragma unroll
+            for (int j = 0; j < RU_MAX; ++j) {
+                const float gt = wave_sum_fast(dot_reg<Q8, CH>(wu[2 * j], su[2 * j], xr));
+                const float up = wave_sum_fast(dot_reg<Q8, CH>(wu[2 * j + 1], su[2 * j + 1], xr));
+                // SwiGLU, [P1] section 5: (g * sigmoid(g)) * u with sigmoid(g) = 1 / (1 + exp(-g))
+                const float sig = 1.0f / (1.0f + expf(-gt));
+                av[j] = (gt * sig) * up;
+            }
+#pragma unroll
+            for (int j = 0; j < RU_MAX; ++j)
+                if (lane == j && ruv[2 * j]) put(a.act + ru[2 * j], av[j], tag(l, 4));
+        }
+
+        // ================= D: down + residual on the owned row
+        {
+            const uint64_t *src = a.act;
+            const bool ok = poll<kMegaBuf / 256>([&](int i) { return src + i; }, I, tag(l, 4), big, a.status);
+            if (!all_ok(ok, &s_fail, a.status)) return;
+            const float d = wave_sum_fast(dot_lds<Q8, KD_MAX>(wd[0], sd[0], big, KD, lane));
+            x_own = x_own + d;
+            if (lane == 0) {
+                if (l + 1 < a.L)
+                    put(a.xd + gw, x_own, tag(l, 5));
+                else
+                    a.x_out[gw] = x_own;
+            }
+        }
+    }
+    // Every workgroup read the epoch before its first phase, and workgroup 0 has consumed every workgroup's
+    // output since, so the next launch's tag base can be published now.
+    if (b == 0 && tid == 0) a.epoch[0] = ep + (uint32_t)(8 * a.L + 8);
+}
+
+bool mega_supported(const Dims &d) {
+    if (d.H != kHid || d.S < 1) return false;
+    if (d.HKV < 2 || kMegaGrid % d.HKV || d.HQ > 16 || kMegaGrid % d.HQ) return false;
+    // merge phase inputs: every split partial of a KV head, (2 + dims per workgroup) words each
+    const int npart = kMegaGrid / d.HKV, dpw = kHeadDim / (kMegaGrid / d.HQ);
+    if (npart * (2 + dpw) > kMegaBuf) return false;
+    if (d.q_dim + 2 * d.HKV * kHeadDim > 4 * kNW) return false;
+    if (d.I > 3 * kNW || d.I % (d.q8 ? 1024 : 512)) return false;
+    if (d.q_dim % (d.q8 ? 1024 : 512)) return false;
+    return true;
+}
+
+hipError_t launch_decode_mega(bool q8, int G, const MegaArgs &a, hipStream_t st) {
+    const dim3 grid(kMegaGrid), block(kWaves * 64);
+#define QW3_MEGA(Q, GG) hipLaunchKernelGGL((decode_mega_kernel<Q, GG>), grid, block, 0, st, a)
+    if (q8) {
+        switch (G) {
+            case 1: QW3_MEGA(1, 1); break;
+            case 2: QW3_MEGA(1, 2); break;
+            case 4: QW3_MEGA(1, 4); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (G) {
+            case 1: QW3_MEGA(0, 1); break;
+            case 2: QW3_MEGA(0, 2); break;
+            case 4: QW3_MEGA(0, 4); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef QW3_MEGA
+    return hipGetLastError();
+}
+
+}  // namespace qw3
