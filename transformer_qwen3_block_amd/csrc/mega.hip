@@ -361,9 +361,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // tags of this launch: ep + 1 .. ep + 8L + 6 (the zeroed words of a fresh arena never match)
     auto tag = [&](int l, int ph) { return ep + 8u * (uint32_t)l + (uint32_t)ph + 1u; };
 
-    // ---- register prefetch state.  Each phase first waits for its inputs, then issues the next phase's
-    // weight loads, then computes: a wait never covers loads issued less than a phase earlier (the vector
-    // memory counter drains in issue order, so a poll also waits for every older load).
+    // ---- register prefetch state.  Each phase waits for its inputs, computes, publishes, and only then
+    // issues the loads of a later phase: a burst of loads from every workgroup at once blocks the issuing wave
+    // until the memory queues drain, so it belongs in the wait for the next inputs, not before a computation
+    // that others are waiting for (and a poll, waiting for the vector memory counter, also waits for every
+    // older load).
     int rq[RQ_MAX];
     bool rqv[RQ_MAX];
 #pragma unroll
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float su[2 * RU_MAX][CH];
     uint4 wd[1][KD_MAX];
     float sd[1][KD_MAX];
-    uint4 kA[4], vA[4], kB[4], vB[4];
+    uint4 kA[4], vA[4];
     float nq[CH][E], nu[CH][E];  // RMSNorm weight slices of the Q and U phases
     float qkn[4], rcs[2];        // QK-Norm weights (q: lane, lane + 64; k: same) and this position's cos/sin
 
@@ -431,17 +433,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (!all_ok(ok, &s_fail, a.status)) return;
         }
         {
-            const float *qnw = (const float *)(lb + a.q_norm), *knw = (const float *)(lb + a.k_norm);
-            qkn[0] = qnw[lane];
-            qkn[1] = qnw[lane + 64];
-            qkn[2] = knw[lane];
-            qkn[3] = knw[lane + 64];
-            rcs[0] = a.rope_cos[(size_t)pos * (kHeadDim / 2) + lane];
-            rcs[1] = a.rope_sin[(size_t)pos * (kHeadDim / 2) + lane];
-        }
-        load_group(kb, vb, ws, ngroups, pos, lane, kA, vA);
-        load_group(kb, vb, ws + nslot, ngroups, pos, lane, kB, vB);
-        {
             float xr[CH][E];
             rms_slice<Q8, CH>(xs, nq, a.eps, lane, xr);
             float d[RQ_MAX];
@@ -450,6 +441,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int j = 0; j < RQ_MAX; ++j)
                 if (lane == j && rqv[j]) put(a.qkv + rq[j], d[j], tag(l, 0));
+        }
+        {  // attention-phase loads: QK-Norm weights, this position's RoPE row, the first cached group
+            const float *qnw = (const float *)(lb + a.q_norm), *knw = (const float *)(lb + a.k_norm);
+            qkn[0] = qnw[lane];
+            qkn[1] = qnw[lane + 64];
+            qkn[2] = knw[lane];
+            qkn[3] = knw[lane + 64];
+            rcs[0] = a.rope_cos[(size_t)pos * (kHeadDim / 2) + lane];
+            rcs[1] = a.rope_sin[(size_t)pos * (kHeadDim / 2) + lane];
+            load_group(kb, vb, ws, ngroups, pos, lane, kA, vA);
         }
 
         // ================= A: QK-Norm + RoPE + append + attention over this split
@@ -469,7 +470,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             };
             const bool ok = poll<3>(src, (G + 2) * kHeadDim, tag(l, 0), raw, a.status);
             if (!all_ok(ok, &s_fail, a.status)) return;
-            load_rows<Q8, 1, KO_MAX>(lb + a.wo, (const float *)(lb + a.so), q_dim, ro, rov, KO, lane, wo, so);
 
             // QK-Norm ([P1] item 3, one 128-weight vector per projection) then RoPE on pairs (i, i + 64) at
             // `pos` (item 4)
@@ -518,13 +518,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
             }
-            // two register slots, each refilled once consumed
-            for (int gi = ws; gi < ngroups; gi += 2 * nslot) {
+            // the first group was prefetched; later groups (long contexts) stream one ahead
+            for (int gi = ws; gi < ngroups; gi += nslot) {
+                const bool more = gi + nslot < ngroups;
+                uint4 kN[4], vN[4];
+                if (more) load_group(kb, vb, gi + nslot, ngroups, pos, lane, kN, vN);
                 attend_group<G>(kA, vA, gi, pos, lane, qr, sl2, m, lsum, acc);
-                load_group(kb, vb, gi + 2 * nslot, ngroups, pos, lane, kA, vA);
-                if (gi + nslot >= ngroups) break;
-                attend_group<G>(kB, vB, gi + nslot, pos, lane, qr, sl2, m, lsum, acc);
-                load_group(kb, vb, gi + 3 * nslot, ngroups, pos, lane, kB, vB);
+                if (!more) break;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    kA[i] = kN[i];
+                    vA[i] = vN[i];
+                }
             }
             if (ws == ws_new) attend_new<G>(kn, vn, lane, qr, sl2, m, lsum, acc);
             // merge the wave's four position rows (the running max is wave-uniform), then the four waves
@@ -573,6 +578,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 put(ph + 2 + d, O, tag(l, 1));
             }
         }
+        load_rows<Q8, 1, KO_MAX>(lb + a.wo, (const float *)(lb + a.so), q_dim, ro, rov, KO, lane, wo, so);
 
         // ================= M: merge of the context splits of one query head, dpw output dims per workgroup
         {
@@ -589,8 +595,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             };
             const bool ok = poll<kMegaBuf / 256>(src, SP * per, tag(l, 1), big, a.status);
             if (!all_ok(ok, &s_fail, a.status)) return;
-            load_rows<Q8, 2 * RU_MAX, CH>(lb + a.wgu, (const float *)(lb + a.sgu), kHid, ru, ruv, CH, lane, wu, su);
-            load_slice<Q8, CH>((const float *)(lb + a.mlp_norm), lane, nu);
             // exact combination in fixed split order: M = max m_s, o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s
             for (int e = wave; e < dpw; e += kWaves) {
                 float M = -INFINITY;
@@ -608,17 +612,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 if (lane == 0) put(a.attn + h * kHeadDim + dc * dpw + e, O / Ls, tag(l, 2));
             }
         }
+        load_rows<Q8, 2 * RU_MAX, CH>(lb + a.wgu, (const float *)(lb + a.sgu), kHid, ru, ruv, CH, lane, wu, su);
+        load_slice<Q8, CH>((const float *)(lb + a.mlp_norm), lane, nu);
 
         // ================= O: o_proj + residual on the owned row
         {
             const uint64_t *src = a.attn;
             const bool ok = poll<8>([&](int i) { return src + i; }, q_dim, tag(l, 2), big, a.status);
             if (!all_ok(ok, &s_fail, a.status)) return;
-            load_rows<Q8, 1, KD_MAX>(lb + a.wd, (const float *)(lb + a.sd), I, ro, rov, KD, lane, wd, sd);
             const float d = wave_sum_fast(dot_lds<Q8, KO_MAX>(wo[0], so[0], big, KO, lane));
             x_own = x_own + d;
             if (lane == 0) put(a.xo + gw, x_own, tag(l, 3));
         }
+        load_rows<Q8, 1, KD_MAX>(lb + a.wd, (const float *)(lb + a.sd), I, ro, rov, KD, lane, wd, sd);
 
         // ================= U: RMSNorm + gate/up + SwiGLU
         {
@@ -627,11 +633,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (!all_ok(ok, &s_fail, a.status)) return;
             float xr[CH][E];
             rms_slice<Q8, CH>(xs, nu, a.eps, lane, xr);
-            if (l + 1 < a.L) {
-                const uint8_t *nb = lblock(l + 1);
-                load_rows<Q8, RQ_MAX, CH>(nb + a.wqkv, (const float *)(nb + a.sqkv), kHid, rq, rqv, CH, lane, wq, sq);
-                load_slice<Q8, CH>((const float *)(nb + a.attn_norm), lane, nq);
-            }
             float av[RU_MAX];
 #pragma unroll
             for (int j = 0; j < RU_MAX; ++j) {
@@ -644,6 +645,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int j = 0; j < RU_MAX; ++j)
                 if (lane == j && ruv[2 * j]) put(a.act + ru[2 * j], av[j], tag(l, 4));
+        }
+        if (l + 1 < a.L) {
+            const uint8_t *nb = lblock(l + 1);
+            load_rows<Q8, RQ_MAX, CH>(nb + a.wqkv, (const float *)(nb + a.sqkv), kHid, rq, rqv, CH, lane, wq, sq);
+            load_slice<Q8, CH>((const float *)(nb + a.attn_norm), lane, nq);
         }
 
         // ================= D: down + residual on the owned row
