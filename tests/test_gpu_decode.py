@@ -147,6 +147,16 @@ def test_decode_batched_sequences():
     _greedy_vs_oracle(shp, seed=26, steps=3, kv_fill_len=150)
 
 
+@pytest.mark.parametrize("n_seq,heads,inter", [(2, (8, 4), 1024), (16, (8, 4), 1024), (3, (16, 8), 3072)])
+def test_decode_batched_q8_mfma_shapes(n_seq, heads, inter):
+    """Batched Q8 steps take the MFMA products: 2 and 16 sequences (the extremes of the 16-wide tiles) and
+    the full-size projection shapes (q_dim 2048, intermediate 3072) at two layers."""
+    shp = replace(SMALL, fmt=synth.FMT_Q8, n_seq=n_seq, n_q_heads=heads[0], n_kv_heads=heads[1], inter=inter,
+                  max_ctx=96)
+    _say("batched q8 mfma", n_seq, heads, inter)
+    _greedy_vs_oracle(shp, seed=28, steps=3, kv_fill_len=40, seqs_checked=(0, n_seq - 1))
+
+
 def test_context_exceeded_leaves_state():
     torch = _torch()
     import transformer_qwen3_block_amd as q

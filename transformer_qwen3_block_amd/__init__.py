@@ -16,7 +16,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 _SO = os.path.join(_HERE, "libqw3.so")
-_SOURCES = ["api.hip", "decode.hip", "prefill.hip", "mega.hip"]
+_SOURCES = ["api.hip", "decode.hip", "prefill.hip", "mega.hip", "gemv_mfma.hip"]
 
 ABI_VERSION = 1
 WEIGHTS_BF16, WEIGHTS_Q8 = 1, 2

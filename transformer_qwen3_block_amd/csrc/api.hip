@@ -53,6 +53,7 @@ struct Model {
     std::vector<StepGraph> graphs;
     bool graphs_enabled = true;
     bool mega = false;  // single-sequence steps run as one persistent launch (decode_mega_kernel)
+    bool mfma_batched = false;  // Q8 steps of 2..16 sequences run their products on MFMA (gemv_mfma.hip)
     int b1_splits = kMaxSplit / 2;  // batch-1 decode attention context splits (measured best of 16/32/64)
     ~Model() {
         for (auto &g : graphs) hipGraphExecDestroy(g.exec);
@@ -197,6 +198,12 @@ int32_t plan(const Dims &d, Layout *lay, qw3_sizes_t *sz) {
     L.argpart = take(c.mul(c.mul(c.mul(kMaxSeq, kLmMaxBlocks), 2), 4));
     L.logits = d.hidden_mode ? take(0) : take(c.mul(c.mul(d.S, d.V), 4));
     L.tokens = take(c.mul(M, 4));
+    L.ssq = take(c.mul(c.mul(kMaxSeq, (d.H + 15) / 16), 4));
+    {
+        const int kmax = d.H > d.q_dim ? (d.H > d.I ? d.H : d.I) : (d.q_dim > d.I ? d.q_dim : d.I);
+        L.opnd_hi = take(c.mul(c.mul(kMaxSeq, kmax), 2));
+        L.opnd_lo = take(c.mul(c.mul(kMaxSeq, kmax), 2));
+    }
     L.scratch_end = off;
     if (c.overflow) return QW3_INTEGER_OVERFLOW;
     if (lay) *lay = L;
@@ -326,6 +333,24 @@ int32_t qw3_create(const qw3_config_t *cfg, void *arena_dev, uint64_t arena_byte
     m->graphs_enabled = !(ng && ng[0] == '1');
     const char *nm = getenv("QW3_NO_MEGA");  // run single-sequence steps kernel by kernel
     m->mega = mega_supported(d) && !(nm && nm[0] == '1');
+    {
+        // every product of a batched step must take the MFMA path, since the residual epilogues hand the
+        // next RMSNorm its sums of squares
+        GemvArgs g{};
+        g.S = d.S;
+        bool ok = d.q8 && d.S >= 2;
+        g.N = d.Nqkv, g.K = d.H;
+        ok = ok && gemv_mfma_supported(g, EPI_STORE);
+        g.N = d.H, g.K = d.q_dim;
+        ok = ok && gemv_mfma_supported(g, EPI_RESID);
+        g.N = d.I, g.K = d.H;
+        ok = ok && gemv_mfma_supported(g, EPI_SWIGLU);
+        g.N = d.H, g.K = d.I;
+        ok = ok && gemv_mfma_supported(g, EPI_RESID);
+        g.N = d.V, g.K = d.H;
+        ok = ok && gemv_mfma_supported(g, EPI_LOGITS);
+        m->mfma_batched = ok;
+    }
     const char *sp = getenv("QW3_B1_SPLITS");  // tuning override, 1..64
     if (sp && atoi(sp) >= 1 && atoi(sp) <= kMaxSplit) m->b1_splits = atoi(sp);
     std::lock_guard<std::mutex> lk(g_mu);
@@ -508,6 +533,20 @@ static int32_t launch_decode_kernel(Model *m, int which, int l, int seq0, int S,
     GemvArgs g{};
     g.S = S;
     g.eps = d.eps;
+    uint16_t *ohi[1] = {at<uint16_t>(m, L.opnd_hi)};
+    uint16_t *olo[1] = {at<uint16_t>(m, L.opnd_lo)};
+    const bool mf = m->mfma_batched && S >= 2;
+    if (mf) {
+        // RMSNorm inputs (Q/K/V, gate/up) come from the f32 residual stream and the sums of squares the
+        // residual epilogues (o_proj, down) leave; attention writes o_proj's operand, gate/up writes down's
+        g.mfma = 1;
+        g.a_hi = ohi[0];
+        g.a_lo = olo[0];
+        g.o_hi = ohi[0];
+        g.o_lo = olo[0];
+        g.ssq = at<float>(m, L.ssq);
+        g.ssq_mode = (which == DK_O || which == DK_DOWN) ? 2 : 1;
+    }
     switch (which) {
         case DK_QKV:  // Q/K/V projections with the pre-attention RMSNorm fused in
             g.w = m->arena + b + L.l_wqkv;
@@ -545,6 +584,10 @@ static int32_t launch_decode_kernel(Model *m, int which, int l, int seq0, int S,
             a.out = attn;
             a.ldo = d.q_dim;
             a.eps = d.eps;
+            if (mf) {
+                a.o_hi = ohi[0];
+                a.o_lo = olo[0];
+            }
             return dev(launch_attn_decode(d.G, a, st));
         }
         case DK_O:  // o_proj + residual
@@ -583,6 +626,9 @@ static int32_t launch_decode_kernel(Model *m, int which, int l, int seq0, int S,
 }
 
 static int32_t run_layers_decode(Model *m, int seq0, int S, hipStream_t st) {
+    if (m->mfma_batched && S >= 2)  // sums of squares of the embedding rows for the first RMSNorm
+        QW3_HIP(launch_ssq_prep(at<float>(m, m->lay.x) + (size_t)seq0 * m->d.H, m->d.H, S, m->d.H,
+                                at<float>(m, m->lay.ssq), st));
     for (int l = 0; l < m->d.L; ++l)
         for (int k = DK_QKV; k <= DK_DOWN; ++k) QW3_TRY(launch_decode_kernel(m, k, l, seq0, S, st));
     return QW3_OK;
@@ -660,6 +706,11 @@ static int32_t run_logits(Model *m, int seq0, int S, const float *xin, float *lo
     g.commit_add = commit_add;
     g.argmax_out = argmax;
     g.status = at<int>(m, L.status);
+    if (m->mfma_batched && S >= 2) {  // after a batched step the last down projection left the sums of squares
+        g.mfma = 1;
+        g.ssq = at<float>(m, L.ssq);
+        g.ssq_mode = 1;
+    }
     return dev(launch_gemv(d.q8, EPI_LOGITS, g, st));
 }
 

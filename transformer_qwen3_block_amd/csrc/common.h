@@ -32,7 +32,8 @@ struct Layout {
     // single-launch decode: epoch tag base and the tagged exchange words (f32 value | tag << 32)
     uint64_t epoch, x_o, x_d, qkv_x, part_x, attn_x, act_x;
     // scratch
-    uint64_t x, xn16, qkv, q16, attn, attn16, act, act16, part, argpart, logits, tokens;
+    uint64_t x, xn16, qkv, q16, attn, attn16, act, act16, part, argpart, logits, tokens, ssq;
+    uint64_t opnd_hi, opnd_lo;  // batched Q8 products: f16 operand pair handed from a kernel to the next product
     uint64_t weights_end, kv_end, state_end, scratch_end;
 };
 
@@ -134,9 +135,25 @@ struct GemvArgs {
     int commit_add;
     int *argmax_out;        // [S]
     int *status;
+    // Batched Q8 path on MFMA (2..16 sequences), see gemv_mfma.hip.  Activations travel between the kernels
+    // of a step as MFMA operands: f16 high part and f16 remainder, [K/32][4][kMaxSeq][8] each.
+    int mfma;               // nonzero: take the MFMA path (the caller checked gemv_mfma_supported)
+    const uint16_t *a_hi, *a_lo;  // operand of a product without RMSNorm (o_proj: attention, down: activations)
+    uint16_t *o_hi, *o_lo;        // operand written for the next product (SwiGLU epilogue)
+    float *ssq;             // [H/16][kMaxSeq] per 16-row tile sums of squares of the residual stream
+    int ssq_mode;           // 1: RMSNorm input, 1/rms from ssq; 2: the residual epilogue writes ssq
 };
+// Index of activation element k of sequence s in an MFMA operand buffer.
+__host__ __device__ inline size_t mfma_opnd_index(int k, int s) {
+    return ((size_t)((k >> 5) * 4 + ((k >> 3) & 3)) * kMaxSeq + s) * 8 + (k & 7);
+}
 
 hipError_t launch_gemv(bool q8, GemvEpi epi, const GemvArgs &a, hipStream_t st);
+bool gemv_mfma_supported(const GemvArgs &a, GemvEpi epi);
+hipError_t launch_gemv_mfma(GemvEpi epi, const GemvArgs &a, hipStream_t st);
+hipError_t launch_ssq_prep(const float *x, int ldx, int S, int K, float *ssq, hipStream_t st);
+hipError_t launch_argmax_finalize(const float *argpart, int nparts, int S, int *argmax_out, int *len, int commit_add,
+                                  hipStream_t st);
 
 struct AttnDecodeArgs {
     const float *qkv;       // raw projections [S][ldqkv]
@@ -151,6 +168,7 @@ struct AttnDecodeArgs {
     float *out;                     // [S][ldo]
     int ldo;
     float eps;
+    uint16_t *o_hi, *o_lo;          // optional: the output also as MFMA operands (batched Q8 products)
 };
 hipError_t launch_attn_decode(int G, const AttnDecodeArgs &a, hipStream_t st);
 

@@ -709,7 +709,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
 // visible after the attention kernel's boundary, which is cheaper on this chip than an in-kernel arrival
 // ticket (device-coherent stores, their completion and an atomic).
 __global__ __launch_bounds__(kHeadDim) void attn_merge_kernel(const float *part, int HQ, int n_split, float *out,
-                                                              int ldo) {
+                                                              int ldo, uint16_t *o_hi, uint16_t *o_lo) {
     static_assert(kMaxSplit == 64, "one split per lane of a wave");
     __shared__ float fm[kMaxSplit], fl[kMaxSplit];
     const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
@@ -734,6 +734,12 @@ __global__ __launch_bounds__(kHeadDim) void attn_merge_kernel(const float *part,
 #pragma unroll
     for (int sp = 0; sp < kMaxSplit; ++sp) o += fm[sp] * ov[sp];
     out[(size_t)s * ldo + h * kHeadDim + d] = o;
+    if (o_hi) {  // o_proj operand of the batched Q8 path: f16 high part and remainder
+        const _Float16 hv = (_Float16)o;
+        const size_t i = mfma_opnd_index(h * kHeadDim + d, s);
+        o_hi[i] = __builtin_bit_cast(uint16_t, hv);
+        o_lo[i] = __builtin_bit_cast(uint16_t, (_Float16)(o - (float)hv));
+    }
 }
 
 // Embedding: x[s] = row tokens[s] of the table, widened (bf16) or dequantised (code * scale).
@@ -790,7 +796,15 @@ __global__ void dequant_kernel(const void *w, const float *scales, long long tot
 
 }  // namespace
 
+hipError_t launch_argmax_finalize(const float *argpart, int nparts, int S, int *argmax_out, int *len, int commit_add,
+                                  hipStream_t st) {
+    hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(256), 0, st, argpart, nparts, S, argmax_out, len,
+                       commit_add);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv(bool q8, GemvEpi epi, const GemvArgs &a, hipStream_t st) {
+    if (a.mfma) return q8 ? launch_gemv_mfma(epi, a, st) : hipErrorInvalidValue;
     if (a.S < 1 || a.S > kMaxSeq || a.K % (q8 ? 1024 : 512)) return hipErrorInvalidValue;
 #define QW3_GEMV_EPI(Q)                                                     \
     switch (epi) {                                                          \
@@ -818,7 +832,7 @@ hipError_t launch_attn_decode(int G, const AttnDecodeArgs &a, hipStream_t st) {
         default: return hipErrorInvalidValue;
     }
     hipLaunchKernelGGL(attn_merge_kernel, dim3(a.HQ, a.S), dim3(kHeadDim), 0, st, a.part, a.HQ, a.n_split, a.out,
-                       a.ldo);
+                       a.ldo, a.o_hi, a.o_lo);
     return hipGetLastError();
 }
 

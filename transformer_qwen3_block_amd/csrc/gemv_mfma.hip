@@ -1,0 +1,311 @@
+// Batched Q8 matrix-vector products for a decode step of 2..16 sequences on gfx950 MFMA.
+//
+// y[s][row] = sum_k x[s][k] * (q[row][k] * scale[row][k/32]) for every sequence s < S: the weights stream from
+// HBM once for all sequences.  One v_mfma_f32_16x16x32_f16 covers 16 sequences x 16 weight rows x one
+// 32-column Q8 block.  The int8 codes are exact in f16; each activation is split into an f16 high part and
+// an f16 remainder (x = hi + lo to about 22 significant bits); both products accumulate in f32, and the
+// block's f32 scale multiplies the block's partial sum -- the per-block factoring of the dequantised dot
+// product of [P1] section 5, a reassociation of the same sum.
+//
+// Lane layout of v_mfma_f32_16x16x32_f16 (wave64): lane l supplies A[l%16][8*(l/16)+e] (sequence l%16, block
+// column 8*(l/16)+e) and B[8*(l/16)+e][l%16] (weight row l%16 of the tile), and receives C[4*(l/16)+r][l%16]
+// (sequence 4*(l/16)+r, row l%16).
+//
+// A workgroup of KW waves splits K: wave w owns blocks [w*NB, (w+1)*NB), forms its activation operands once
+// (RMSNorm inputs from the f32 residual stream and the per-tile sums of squares the residual epilogues leave;
+// attention outputs and SwiGLU activations as the f16 pairs their producers wrote) and keeps them in
+// registers for every 16-row tile it visits (grid-stride over tiles, the next tile's
+// codes in flight while the current one is multiplied); the waves' partial tiles are summed in LDS in wave
+// order, so every output element has a fixed summation order.  Epilogues: store (Q/K/V), residual add (o_proj,
+// down; also the per-tile sums of squares of the updated rows, which the next RMSNorm reads in tile order),
+// SwiGLU (gate/up rows interleaved in the tile so gate and up of a unit meet in one 16-lane row) and logits
+// with per-workgroup greedy partials.
+//
+// Page titles used in citations:
+//   [P1] "Scalar-Native Qwen3 Reference Runtime As The Numerical Authority"
+//   [P4] "Portable WebAssembly Runtime Architecture for TinyRustLM"
+#include <math.h>
+
+#include "common.h"
+
+namespace qw3 {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4_t mfma16(const uint4 &a, const uint4 &b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+}
+
+// Eight int8 codes -> eight f16 (exact: |q| <= 127).
+__device__ __forceinline__ uint4 codes_to_f16(uint2 w) {
+    f16x8_t h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = (_Float16)(int)(int8_t)(w.x >> (8 * e));
+        h[4 + e] = (_Float16)(int)(int8_t)(w.y >> (8 * e));
+    }
+    return __builtin_bit_cast(uint4, h);
+}
+
+// f32 -> (f16 high part, f16 remainder) bits
+__device__ __forceinline__ void split_one(float v, uint16_t &hi, uint16_t &lo) {
+    const _Float16 h = (_Float16)v;
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)h));
+}
+
+template <int KW, int NB, int EPI>
+__global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
+    __shared__ float red[KW][4][64];  // per wave: C[4*(l/16)+r][l%16] of lane l at [r][l]
+    __shared__ float s_inv[kMaxSeq];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q = lane >> 4, c = lane & 15;  // block column group, sequence (A) / row slot (B, C)
+    const int S = a.S, K = a.K, KB = K / 32;
+    const int kb0 = w * NB;
+    const int8_t *wq = (const int8_t *)a.w;
+
+    // weight row of row slot c in tile t (SwiGLU tiles: rows 0-7 gate units, 8-15 the matching up units)
+    auto wrow = [&](int t) -> long long {
+        if constexpr (EPI == EPI_SWIGLU) {
+            const int unit = t * 8 + (c & 7);
+            return c < 8 ? (long long)unit : (long long)a.N + unit;
+        } else {
+            return (long long)min(t * 16 + c, a.N - 1);
+        }
+    };
+    const int ntiles = EPI == EPI_SWIGLU ? a.N / 8 : (a.N + 15) / 16;
+    auto load_tile = [&](int t, uint2 (&cw)[NB], float (&sc)[NB]) {
+        const long long row = wrow(t < ntiles ? t : 0);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int kb = kb0 + j;
+            const u32x2_t v = __builtin_nontemporal_load((const u32x2_t *)(wq + row * K + kb * 32 + 8 * q));
+            cw[j] = make_uint2(v.x, v.y);
+            sc[j] = a.scales[row * KB + kb];
+        }
+    };
+
+    // The first tile's codes, this wave's activations and the sums of squares all go out at once: one memory
+    // round trip before the first product.
+    uint2 cw[NB];
+    float sc[NB];
+    int t = blockIdx.x;
+    load_tile(t, cw, sc);
+    uint4 ahi[NB], alo[NB];
+    if (a.norm_w) {
+        // RMSNorm input ([P1] section 2 items 1 and 6): w * (x * inv) with inv = 1 / sqrt(mean(x^2) + eps) of
+        // the sequence, from the per-16-row sums of squares (tile order, then a fixed 16-lane tree); the
+        // residual stream itself may exceed the f16 range, the normalised operand does not
+        float xv[NB][8], gv[NB][8];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int k = (kb0 + j) * 32 + 8 * q;
+            const float4 x0 = *(const float4 *)(a.x + (size_t)c * a.ldx + k);
+            const float4 x1 = *(const float4 *)(a.x + (size_t)c * a.ldx + k + 4);
+            const float4 g0 = *(const float4 *)(a.norm_w + k);
+            const float4 g1 = *(const float4 *)(a.norm_w + k + 4);
+            xv[j][0] = x0.x; xv[j][1] = x0.y; xv[j][2] = x0.z; xv[j][3] = x0.w;
+            xv[j][4] = x1.x; xv[j][5] = x1.y; xv[j][6] = x1.z; xv[j][7] = x1.w;
+            gv[j][0] = g0.x; gv[j][1] = g0.y; gv[j][2] = g0.z; gv[j][3] = g0.w;
+            gv[j][4] = g1.x; gv[j][5] = g1.y; gv[j][6] = g1.z; gv[j][7] = g1.w;
+        }
+        if (tid < 256) {
+            const int s = tid >> 4, p = tid & 15;
+            float ss = 0.f;
+            for (int tt = p; tt < K / 16; tt += 16) ss += a.ssq[tt * kMaxSeq + s];
+            ss = row16_sum(ss);
+            if (p == 0) s_inv[s] = 1.0f / sqrtf(ss / (float)K + a.eps);
+        }
+        __syncthreads();
+        const float inv = s_inv[c];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            f16x8_t h, r;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = c < S ? gv[j][e] * (xv[j][e] * inv) : 0.f;
+                h[e] = (_Float16)v;
+                r[e] = (_Float16)(v - (float)h[e]);
+            }
+            ahi[j] = __builtin_bit_cast(uint4, h);
+            alo[j] = __builtin_bit_cast(uint4, r);
+        }
+    } else {
+        // operand written by the previous kernel (attention output, SwiGLU activations)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const size_t o = ((size_t)((kb0 + j) * 4 + q) * kMaxSeq + c) * 8;
+            ahi[j] = *(const uint4 *)(a.a_hi + o);
+            alo[j] = *(const uint4 *)(a.a_lo + o);
+        }
+    }
+
+    // logits: running greedy choice of this thread's (sequence, row slot)
+    float best = -INFINITY;
+    int besti = 0x7fffffff, bad = 0;
+    const int es = tid >> 4, er = tid & 15;  // epilogue thread: sequence, row slot
+
+    for (; t < ntiles; t += gridDim.x) {
+        uint2 cn[NB];
+        float sn[NB];
+        load_tile(t + gridDim.x, cn, sn);
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const uint4 bw = codes_to_f16(cw[j]);
+            f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
+            cc = mfma16(ahi[j], bw, cc);
+            cc = mfma16(alo[j], bw, cc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] += sc[j] * cc[r];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[w][r][lane] = acc[r];
+        __syncthreads();
+        if (tid < 256) {
+            // sum of the waves' partials for (sequence es, row slot er), in wave order
+            const int sl = 16 * (es >> 2) + er, r = es & 3;
+            float v = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < KW; ++ww) v += red[ww][r][sl];
+            if constexpr (EPI == EPI_STORE) {
+                const int row = t * 16 + er;
+                if (es < S && row < a.N) a.y[(size_t)es * a.ldy + row] = v;
+            } else if constexpr (EPI == EPI_RESID) {
+                const int row = t * 16 + er;
+                float nv = 0.f;
+                if (es < S) {
+                    float *yp = a.y + (size_t)es * a.ldy + row;
+                    nv = *yp + v;
+                    *yp = nv;
+                }
+                if (a.ssq_mode == 2) {
+                    const float ss = row16_sum(nv * nv);  // the 16 rows of the tile, one sequence per 16 lanes
+                    if (er == 0) a.ssq[t * kMaxSeq + es] = ss;
+                }
+            } else if constexpr (EPI == EPI_SWIGLU) {
+                const float up = dpp_mov<0x128>(v);  // row_ror:8 -- slot er + 8 holds the up row of slot er
+                if (er < 8 && es < S) {
+                    // SwiGLU, [P1] section 5: (g * sigmoid(g)) * u with sigmoid(g) = 1 / (1 + exp(-g))
+                    const float sig = 1.0f / (1.0f + __expf(-v));
+                    const float act = (v * sig) * up;
+                    const int unit = t * 8 + er;
+                    if (a.y) a.y[(size_t)es * a.ldy + unit] = act;
+                    uint16_t h, l;
+                    split_one(act, h, l);
+                    const size_t o = mfma_opnd_index(unit, es);
+                    a.o_hi[o] = h;
+                    a.o_lo[o] = l;
+                }
+            } else {  // EPI_LOGITS
+                const int row = t * 16 + er;
+                if (es < S && row < a.N) {
+                    a.y[(size_t)es * a.ldy + row] = v;
+                    if (!isfinite(v)) bad = 1;
+                    if (v > best) {  // rows visited in increasing order: ties keep the lowest id
+                        best = v;
+                        besti = row;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            cw[j] = cn[j];
+            sc[j] = sn[j];
+        }
+    }
+
+    if constexpr (EPI == EPI_LOGITS) {
+        // per-workgroup greedy partial of each sequence: greatest value, lowest index on ties ([P4] "Sampling
+        // order"); a non-finite logit latches a numerical failure ([P1] section 4)
+        if (tid < 256) {
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+                const float ov = __shfl_xor(best, o, 64);
+                const int oi = __shfl_xor(besti, o, 64);
+                if (ov > best || (ov == best && oi < besti)) {
+                    best = ov;
+                    besti = oi;
+                }
+            }
+            if (bad) atomicOr(a.status, 1);
+            if (er == 0 && es < S) {
+                float *p = a.argpart + ((size_t)es * gridDim.x + blockIdx.x) * 2;
+                p[0] = best;
+                p[1] = __int_as_float(besti);
+            }
+        }
+    }
+}
+
+// Per-16-row sums of squares of the step's first residual stream (the embedding rows), as the residual
+// epilogues leave them for later RMSNorms.  One workgroup per sequence.
+__global__ __launch_bounds__(256) void ssq_prep_kernel(const float *x, int ldx, int K, float *ssq) {
+    const int s = blockIdx.x;
+    for (int k0 = threadIdx.x * 4; k0 < K; k0 += 1024) {
+        const float4 v = *(const float4 *)(x + (size_t)s * ldx + k0);
+        float ss = (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+        // four threads hold a 16-row tile
+        ss += dpp_mov<0xB1>(ss);
+        ss += dpp_mov<0x4E>(ss);
+        if ((threadIdx.x & 3) == 0) ssq[(k0 >> 4) * kMaxSeq + s] = ss;
+    }
+}
+
+}  // namespace
+
+bool gemv_mfma_supported(const GemvArgs &a, GemvEpi epi) {
+    if (a.S < 2 || a.S > kMaxSeq || a.K % 32) return false;
+    switch (epi) {
+        case EPI_STORE:
+        case EPI_LOGITS: return a.K == 1024;
+        case EPI_SWIGLU: return a.K == 1024 && a.N % 8 == 0;
+        case EPI_RESID: return (a.K == 1024 || a.K == 2048 || a.K == 3072) && a.N % 16 == 0;
+    }
+    return false;
+}
+
+hipError_t launch_ssq_prep(const float *x, int ldx, int S, int K, float *ssq, hipStream_t st) {
+    if (S < 1 || S > kMaxSeq || K % 16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(ssq_prep_kernel, dim3(S), dim3(256), 0, st, x, ldx, K, ssq);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_mfma(GemvEpi epi, const GemvArgs &a, hipStream_t st) {
+    if (!gemv_mfma_supported(a, epi)) return hipErrorInvalidValue;
+    switch (epi) {
+        case EPI_STORE:
+            hipLaunchKernelGGL((gemv_mfma_kernel<4, 8, EPI_STORE>), dim3((a.N + 15) / 16), dim3(256), 0, st, a);
+            break;
+        case EPI_SWIGLU:
+            hipLaunchKernelGGL((gemv_mfma_kernel<4, 8, EPI_SWIGLU>), dim3(a.N / 8), dim3(256), 0, st, a);
+            break;
+        case EPI_RESID:
+            switch (a.K) {
+                case 1024: hipLaunchKernelGGL((gemv_mfma_kernel<16, 2, EPI_RESID>), dim3(a.N / 16), dim3(1024), 0, st, a); break;
+                case 2048: hipLaunchKernelGGL((gemv_mfma_kernel<16, 4, EPI_RESID>), dim3(a.N / 16), dim3(1024), 0, st, a); break;
+                default: hipLaunchKernelGGL((gemv_mfma_kernel<16, 6, EPI_RESID>), dim3(a.N / 16), dim3(1024), 0, st, a); break;
+            }
+            break;
+        case EPI_LOGITS: {
+            const int ntiles = (a.N + 15) / 16;
+            const int grid = ntiles < 1024 ? ntiles : 1024;
+            hipLaunchKernelGGL((gemv_mfma_kernel<4, 8, EPI_LOGITS>), dim3(grid), dim3(256), 0, st, a);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            return launch_argmax_finalize(a.argpart, grid, a.S, a.argmax_out, a.len, a.commit_add, st);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace qw3
