@@ -136,16 +136,17 @@ struct GemvArgs {
     int *argmax_out;        // [S]
     int *status;
     // Batched Q8 path on MFMA (2..16 sequences), see gemv_mfma.hip.  Activations travel between the kernels
-    // of a step as MFMA operands: f16 high part and f16 remainder, [K/32][4][kMaxSeq][8] each.
+    // of a step as MFMA operands: f16 high part and f16 remainder, [K/64][4][kMaxSeq][16] each.
     int mfma;               // nonzero: take the MFMA path (the caller checked gemv_mfma_supported)
     const uint16_t *a_hi, *a_lo;  // operand of a product without RMSNorm (o_proj: attention, down: activations)
     uint16_t *o_hi, *o_lo;        // operand written for the next product (SwiGLU epilogue)
     float *ssq;             // [H/16][kMaxSeq] per 16-row tile sums of squares of the residual stream
     int ssq_mode;           // 1: RMSNorm input, 1/rms from ssq; 2: the residual epilogue writes ssq
 };
-// Index of activation element k of sequence s in an MFMA operand buffer.
+// Index of activation element k of sequence s in an MFMA operand buffer: [K/64][4][kMaxSeq][16], so the lane
+// of column group g and sequence s reads columns 16g..16g+15 of a 64-column block pair as one 32-byte run.
 __host__ __device__ inline size_t mfma_opnd_index(int k, int s) {
-    return ((size_t)((k >> 5) * 4 + ((k >> 3) & 3)) * kMaxSeq + s) * 8 + (k & 7);
+    return ((size_t)((k >> 6) * 4 + ((k >> 4) & 3)) * kMaxSeq + s) * 16 + (k & 15);
 }
 
 hipError_t launch_gemv(bool q8, GemvEpi epi, const GemvArgs &a, hipStream_t st);

@@ -61,12 +61,15 @@ __device__ __forceinline__ void split_one(float v, uint16_t &hi, uint16_t &lo) {
 
 template <int KW, int NB, int EPI>
 __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
+    static_assert(NB % 2 == 0, "blocks come in pairs");
+    constexpr int NP = NB / 2;        // 64-column block pairs per wave
     __shared__ float red[KW][4][64];  // per wave: C[4*(l/16)+r][l%16] of lane l at [r][l]
     __shared__ float s_inv[kMaxSeq];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int q = lane >> 4, c = lane & 15;  // block column group, sequence (A) / row slot (B, C)
+    const int q = lane >> 4, c = lane & 15;  // column group, sequence (A) / row slot (B, C)
+    const bool first = q < 2;                // groups 0, 1 hold the pair's first block, 2, 3 its second
     const int S = a.S, K = a.K, KB = K / 32;
     const int kb0 = w * NB;
     const int8_t *wq = (const int8_t *)a.w;
@@ -81,69 +84,78 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
         }
     };
     const int ntiles = EPI == EPI_SWIGLU ? a.N / 8 : (a.N + 15) / 16;
-    auto load_tile = [&](int t, uint2 (&cw)[NB], float (&sc)[NB]) {
+    // Lane (q, c) reads 16 codes of row c: columns 16q..16q+15 of each 64-column block pair (one 16-byte
+    // load; four lanes cover 64 contiguous bytes of a row), and the row's scales of this wave's blocks.
+    auto load_tile = [&](int t, uint4 (&cw)[NP], float (&sc)[NB]) {
         const long long row = wrow(t < ntiles ? t : 0);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int kb = kb0 + j;
-            const u32x2_t v = __builtin_nontemporal_load((const u32x2_t *)(wq + row * K + kb * 32 + 8 * q));
-            cw[j] = make_uint2(v.x, v.y);
-            sc[j] = a.scales[row * KB + kb];
+        for (int p = 0; p < NP; ++p) {
+            const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)(wq + row * K + (kb0 + 2 * p) * 32 + 16 * q));
+            cw[p] = make_uint4(v.x, v.y, v.z, v.w);
         }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) sc[j] = a.scales[row * KB + kb0 + j];
     };
 
     // The first tile's codes, this wave's activations and the sums of squares all go out at once: one memory
-    // round trip before the first product.
-    uint2 cw[NB];
+    // round trip before the first product.  Activation operands: lane (q, c) holds sequence c's columns
+    // 16q..16q+15 of each block pair, as f16 high parts and remainders (a1: first eight, a2: last eight).
+    uint4 cw[NP];
     float sc[NB];
     int t = blockIdx.x;
     load_tile(t, cw, sc);
-    uint4 ahi[NB], alo[NB];
+    uint4 a1h[NP], a1l[NP], a2h[NP], a2l[NP];
     if (a.norm_w) {
         // RMSNorm input ([P1] section 2 items 1 and 6): w * (x * inv) with inv = 1 / sqrt(mean(x^2) + eps) of
         // the sequence, from the per-16-row sums of squares (tile order, then a fixed 16-lane tree); the
         // residual stream itself may exceed the f16 range, the normalised operand does not
-        float xv[NB][8], gv[NB][8];
+        float xv[NP][16], gv[NP][16];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int k = (kb0 + j) * 32 + 8 * q;
-            const float4 x0 = *(const float4 *)(a.x + (size_t)c * a.ldx + k);
-            const float4 x1 = *(const float4 *)(a.x + (size_t)c * a.ldx + k + 4);
-            const float4 g0 = *(const float4 *)(a.norm_w + k);
-            const float4 g1 = *(const float4 *)(a.norm_w + k + 4);
-            xv[j][0] = x0.x; xv[j][1] = x0.y; xv[j][2] = x0.z; xv[j][3] = x0.w;
-            xv[j][4] = x1.x; xv[j][5] = x1.y; xv[j][6] = x1.z; xv[j][7] = x1.w;
-            gv[j][0] = g0.x; gv[j][1] = g0.y; gv[j][2] = g0.z; gv[j][3] = g0.w;
-            gv[j][4] = g1.x; gv[j][5] = g1.y; gv[j][6] = g1.z; gv[j][7] = g1.w;
+        for (int p = 0; p < NP; ++p) {
+            const int k = (kb0 + 2 * p) * 32 + 16 * q;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 xx = *(const float4 *)(a.x + (size_t)c * a.ldx + k + 4 * i);
+                const float4 gg = *(const float4 *)(a.norm_w + k + 4 * i);
+                xv[p][4 * i] = xx.x; xv[p][4 * i + 1] = xx.y; xv[p][4 * i + 2] = xx.z; xv[p][4 * i + 3] = xx.w;
+                gv[p][4 * i] = gg.x; gv[p][4 * i + 1] = gg.y; gv[p][4 * i + 2] = gg.z; gv[p][4 * i + 3] = gg.w;
+            }
         }
         if (tid < 256) {
-            const int s = tid >> 4, p = tid & 15;
+            const int s = tid >> 4, pp = tid & 15;
             float ss = 0.f;
-            for (int tt = p; tt < K / 16; tt += 16) ss += a.ssq[tt * kMaxSeq + s];
+            for (int tt = pp; tt < K / 16; tt += 16) ss += a.ssq[tt * kMaxSeq + s];
             ss = row16_sum(ss);
-            if (p == 0) s_inv[s] = 1.0f / sqrtf(ss / (float)K + a.eps);
+            if (pp == 0) s_inv[s] = 1.0f / sqrtf(ss / (float)K + a.eps);
         }
         __syncthreads();
         const float inv = s_inv[c];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            f16x8_t h, r;
+        for (int p = 0; p < NP; ++p) {
+            f16x8_t h1, l1, h2, l2;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float v = c < S ? gv[j][e] * (xv[j][e] * inv) : 0.f;
-                h[e] = (_Float16)v;
-                r[e] = (_Float16)(v - (float)h[e]);
+                const float v1 = c < S ? gv[p][e] * (xv[p][e] * inv) : 0.f;
+                const float v2 = c < S ? gv[p][8 + e] * (xv[p][8 + e] * inv) : 0.f;
+                h1[e] = (_Float16)v1;
+                l1[e] = (_Float16)(v1 - (float)h1[e]);
+                h2[e] = (_Float16)v2;
+                l2[e] = (_Float16)(v2 - (float)h2[e]);
             }
-            ahi[j] = __builtin_bit_cast(uint4, h);
-            alo[j] = __builtin_bit_cast(uint4, r);
+            a1h[p] = __builtin_bit_cast(uint4, h1);
+            a1l[p] = __builtin_bit_cast(uint4, l1);
+            a2h[p] = __builtin_bit_cast(uint4, h2);
+            a2l[p] = __builtin_bit_cast(uint4, l2);
         }
     } else {
         // operand written by the previous kernel (attention output, SwiGLU activations)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const size_t o = ((size_t)((kb0 + j) * 4 + q) * kMaxSeq + c) * 8;
-            ahi[j] = *(const uint4 *)(a.a_hi + o);
-            alo[j] = *(const uint4 *)(a.a_lo + o);
+        for (int p = 0; p < NP; ++p) {
+            const size_t o = (((size_t)(kb0 / 2 + p) * 4 + q) * kMaxSeq + c) * 16;
+            a1h[p] = *(const uint4 *)(a.a_hi + o);
+            a2h[p] = *(const uint4 *)(a.a_hi + o + 8);
+            a1l[p] = *(const uint4 *)(a.a_lo + o);
+            a2l[p] = *(const uint4 *)(a.a_lo + o + 8);
         }
     }
 
@@ -151,20 +163,29 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
     float best = -INFINITY;
     int besti = 0x7fffffff, bad = 0;
     const int es = tid >> 4, er = tid & 15;  // epilogue thread: sequence, row slot
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
 
     for (; t < ntiles; t += gridDim.x) {
-        uint2 cn[NB];
+        uint4 cn[NP];
         float sn[NB];
         load_tile(t + gridDim.x, cn, sn);
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const uint4 bw = codes_to_f16(cw[j]);
-            f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
-            cc = mfma16(ahi[j], bw, cc);
-            cc = mfma16(alo[j], bw, cc);
+        for (int p = 0; p < NP; ++p) {
+            // one product per block: the other block's lanes contribute zero codes
+            const uint4 b1 = codes_to_f16(make_uint2(cw[p].x, cw[p].y)), b2 = codes_to_f16(make_uint2(cw[p].z, cw[p].w));
+            const uint4 b1f = first ? b1 : z4, b2f = first ? b2 : z4, b1s = first ? z4 : b1, b2s = first ? z4 : b2;
+            f32x4_t cf = {0.f, 0.f, 0.f, 0.f}, cs = {0.f, 0.f, 0.f, 0.f};
+            cf = mfma16(a1h[p], b1f, cf);
+            cs = mfma16(a1h[p], b1s, cs);
+            cf = mfma16(a1l[p], b1f, cf);
+            cs = mfma16(a1l[p], b1s, cs);
+            cf = mfma16(a2h[p], b2f, cf);
+            cs = mfma16(a2h[p], b2s, cs);
+            cf = mfma16(a2l[p], b2f, cf);
+            cs = mfma16(a2l[p], b2s, cs);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] += sc[j] * cc[r];
+            for (int r = 0; r < 4; ++r) acc[r] += sc[2 * p] * cf[r] + sc[2 * p + 1] * cs[r];
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) red[w][r][lane] = acc[r];
@@ -218,10 +239,9 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            cw[j] = cn[j];
-            sc[j] = sn[j];
-        }
+        for (int p = 0; p < NP; ++p) cw[p] = cn[p];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) sc[j] = sn[j];
     }
 
     if constexpr (EPI == EPI_LOGITS) {
@@ -283,12 +303,18 @@ hipError_t launch_ssq_prep(const float *x, int ldx, int S, int K, float *ssq, hi
 hipError_t launch_gemv_mfma(GemvEpi epi, const GemvArgs &a, hipStream_t st) {
     if (!gemv_mfma_supported(a, epi)) return hipErrorInvalidValue;
     switch (epi) {
-        case EPI_STORE:
-            hipLaunchKernelGGL((gemv_mfma_kernel<4, 8, EPI_STORE>), dim3((a.N + 15) / 16), dim3(256), 0, st, a);
+        case EPI_STORE: {
+            const int ntiles = (a.N + 15) / 16;
+            hipLaunchKernelGGL((gemv_mfma_kernel<4, 8, EPI_STORE>), dim3(ntiles > 128 ? (ntiles + 1) / 2 : ntiles),
+                               dim3(256), 0, st, a);
             break;
-        case EPI_SWIGLU:
-            hipLaunchKernelGGL((gemv_mfma_kernel<4, 8, EPI_SWIGLU>), dim3(a.N / 8), dim3(256), 0, st, a);
+        }
+        case EPI_SWIGLU: {
+            const int ntiles = a.N / 8;
+            hipLaunchKernelGGL((gemv_mfma_kernel<4, 8, EPI_SWIGLU>), dim3(ntiles > 128 ? (ntiles + 1) / 2 : ntiles),
+                               dim3(256), 0, st, a);
             break;
+        }
         case EPI_RESID:
             switch (a.K) {
                 case 1024: hipLaunchKernelGGL((gemv_mfma_kernel<16, 2, EPI_RESID>), dim3(a.N / 16), dim3(1024), 0, st, a); break;
@@ -298,7 +324,7 @@ hipError_t launch_gemv_mfma(GemvEpi epi, const GemvArgs &a, hipStream_t st) {
             break;
         case EPI_LOGITS: {
             const int ntiles = (a.N + 15) / 16;
-            const int grid = ntiles < 1024 ? ntiles : 1024;
+            const int grid = ntiles < 512 ? ntiles : 512;
             hipLaunchKernelGGL((gemv_mfma_kernel<4, 8, EPI_LOGITS>), dim3(grid), dim3(256), 0, st, a);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
