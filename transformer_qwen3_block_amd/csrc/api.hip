@@ -184,6 +184,7 @@ int32_t plan(const Dims &d, Layout *lay, qw3_sizes_t *sz) {
     L.part_x = take(c.mul(c.mul((uint64_t)kMegaGrid * d.G, kPartStride), 8));  // one partial per workgroup
     L.attn_x = take(c.mul(d.q_dim, 8));
     L.act_x = take(c.mul(d.I, 8));
+    L.pf_cnt = take(attn_prefill_counter_bytes(d));
     L.state_end = off;
     const uint64_t M = (uint64_t)(d.max_prefill > d.S ? d.max_prefill : d.S);
     L.x = take(c.mul(c.mul(M, d.H), 4));
@@ -195,6 +196,7 @@ int32_t plan(const Dims &d, Layout *lay, qw3_sizes_t *sz) {
     L.act = take(c.mul(c.mul(M, d.I), 4));
     L.act16 = take(c.mul(c.mul(M, d.I), 2));
     L.part = take(c.mul(c.mul(c.mul(c.mul(d.S, d.HQ), kMaxSplit), kPartStride), 4));
+    L.pf_part = take(attn_prefill_partial_bytes(d));
     L.argpart = take(c.mul(c.mul(c.mul(kMaxSeq, kLmMaxBlocks), 2), 4));
     L.logits = d.hidden_mode ? take(0) : take(c.mul(c.mul(d.S, d.V), 4));
     L.tokens = take(c.mul(M, 4));
@@ -456,6 +458,8 @@ int32_t qw3_load_weights(uint64_t h, const qw3_tensor_t *t, int32_t n, void *str
         QW3_HIP(hipStreamSynchronize(st));
     }
     QW3_HIP(hipMemsetAsync(m->arena + L.kv_end, 0, L.state_end - L.kv_end, st));
+    // prefill attention's state slots start empty (all-ones words)
+    QW3_HIP(hipMemsetAsync(m->arena + L.pf_part, 0xff, attn_prefill_partial_bytes(d), st));
     QW3_HIP(hipStreamSynchronize(st));
     m->len.assign(d.S, 0);
     m->lens_dirty = m->status_dirty = false;
@@ -505,7 +509,7 @@ int32_t qw3_status_poll(uint64_t h, void *stream) {
     QW3_HIP(hipMemcpyAsync(&status, m->arena + m->lay.status, 4, hipMemcpyDeviceToHost, st));
     QW3_HIP(hipStreamSynchronize(st));
     if (status & 1) m->poisoned = true;
-    if (status & 4) {  // a wait of the single-launch decode timed out (its workgroups were not all resident)
+    if (status & 4) {  // a bounded device wait timed out (single-launch decode or prefill attention pairing)
         m->poisoned = true;
         return QW3_DEVICE_ERROR;
     }

@@ -31,9 +31,12 @@ struct Layout {
     uint64_t len, status;
     // single-launch decode: epoch tag base and the tagged exchange words (f32 value | tag << 32)
     uint64_t epoch, x_o, x_d, qkv_x, part_x, attn_x, act_x;
+    // prefill attention: arrival counters of the two key-range halves of each (query block, KV head)
+    uint64_t pf_cnt;
     // scratch
     uint64_t x, xn16, qkv, q16, attn, attn16, act, act16, part, argpart, logits, tokens, ssq;
     uint64_t opnd_hi, opnd_lo;  // batched Q8 products: f16 operand pair handed from a kernel to the next product
+    uint64_t pf_part;           // prefill attention: per-thread partial softmax state of each key-range half
     uint64_t weights_end, kv_end, state_end, scratch_end;
 };
 

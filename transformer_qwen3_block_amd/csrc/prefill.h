@@ -8,6 +8,11 @@ namespace qw3 {
 // at positions pos0..pos0+T-1, appending their K/V to the cache.  On return x holds the layer-stack output.
 int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, int pos0, int T, hipStream_t st);
 
+// Sizes of the prefill attention's arrival counters and partial-state buffer for up to d.max_prefill tokens
+// (zero when the tiled prefill is unavailable).  The counters live in zeroed state memory.
+uint64_t attn_prefill_counter_bytes(const Dims &d);
+uint64_t attn_prefill_partial_bytes(const Dims &d);
+
 // Widens n bf16 values to f16 (round to nearest even; exact unless |v| < 2^-14 or |v| > 65504).
 hipError_t launch_bf16_to_f16(const void *in, void *out, size_t n, hipStream_t st);
 

@@ -275,8 +275,13 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(const float *qk
 // Causal GQA flash attention for T queries at positions pos0..pos0+T-1 over cache positions 0..pos0+T-1
 // ([P1] section 2 item 5: query head h reads KV head floor(h / G); keys j <= the query's position).
 //
-// Workgroup = (query block, KV head); its four waves cover the G query heads of that KV head, 16 queries
-// per wave.  Each 64-key tile of K ([key][dim]) and V (transposed to [dim][key]) is staged in LDS once for
+// Work unit = (query block, KV head, key-range half); its eight waves cover the G query heads of that KV
+// head, 16 queries per wave.  The key tiles of a query block are split into two halves run by two
+// workgroups, so the longest causal rows take half as long; each half writes its per-thread softmax state
+// (running max, partial sum, unnormalised output) and the later of the two to arrive merges both, always
+// with the first half as the left operand, so the result does not depend on which arrives first.  Work
+// units are ordered longest first in the first half of the grid and shortest first in the second, so two
+// workgroups resident together on a compute unit carry complementary amounts of work.  Each 64-key tile of K ([key][dim]) and V (transposed to [dim][key]) is staged in LDS once for
 // all waves.  Scores are computed transposed, S^T = K Q^T, so each lane holds four keys of one query
 // (query = lane%16): the row max/sum need only two cross-lane steps, and the probabilities already sit in
 // the B-operand layout of O^T = V^T P^T (the k index of both operands runs over the same key set), so no
@@ -287,14 +292,36 @@ struct AttnPrefillArgs {
     const uint16_t *kc, *vc;  // bf16 cache, head 0 of (seq, layer): [HKV][max_ctx][128]
     int T, pos0, HQ, HKV, max_ctx;
     uint16_t *out16;          // f16 [T][HQ*128]
+    unsigned *part;           // [query block][HKV][kPfState][512] f32 bits: state of the first half to finish
+    unsigned *cnt;            // [query block][HKV] arrival counters, even between launches
+    int *status;              // bit 4 set if a published state never arrived (bounded wait)
 };
+constexpr int kPfState = 34;              // o[32], m, l per thread
+constexpr unsigned kPfEmpty = 0xffffffffu;  // slot word not yet published
+constexpr int kPfStatusTimeout = 4;
+constexpr int kPfSpin = 1 << 20;          // polling rounds before giving up (far beyond any legitimate wait)
+
+__device__ __forceinline__ void pf_put(unsigned *p, float v) {
+    __hip_atomic_store(p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Takes a published word and restores the empty pattern; ok turns false if the wait ran out.
+__device__ __forceinline__ float pf_take(unsigned *p, bool &ok) {
+    unsigned v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int n = 0; v == kPfEmpty && n < kPfSpin; ++n) {
+        __builtin_amdgcn_s_sleep(1);
+        v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    ok = ok && v != kPfEmpty;
+    __hip_atomic_store(p, kPfEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __uint_as_float(v);
+}
 
 constexpr int kKT = 64;                  // keys per tile
 constexpr int kKsLd = kHeadDim + 8;      // K tile row stride (f16 elements)
 constexpr int kVtLd = kKT + 8;           // V^T tile row stride (f16 elements)
 
 template <int G>
-__global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void attn_prefill_kernel(AttnPrefillArgs a) {
     constexpr int NW = 8;         // waves per workgroup
     constexpr int WPH = NW / G;   // waves per query head
     constexpr int QB = 16 * WPH;  // queries per workgroup
@@ -304,14 +331,21 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nqb = (a.T + QB - 1) / QB;
-    const int qb = nqb - 1 - blockIdx.x;  // longest causal rows first
-    const int kvh = blockIdx.y;
+    const int nunits = 2 * nqb * a.HKV;
+    const int j = blockIdx.x;
+    const int rank = j < (nunits + 1) / 2 ? j : nunits - 1 - (j - (nunits + 1) / 2);  // 0 = most work
+    const int half = rank & 1;
+    const int qb = nqb - 1 - (rank >> 1) / a.HKV;
+    const int kvh = (rank >> 1) % a.HKV;
     const int t0 = qb * QB;
     const int hq = kvh * G + wave / WPH;
     const int tq = t0 + (wave % WPH) * 16 + (lane & 15);  // this lane's query (C column)
     const int qpos = a.pos0 + tq;
     const int t_last = min(a.T - 1, t0 + QB - 1);
     const int n_keys = a.pos0 + t_last + 1;
+    const int hsplit = ((n_keys + kKT - 1) / kKT + 1) / 2 * kKT;  // first key of the second half
+    const int kbeg = half ? hsplit : 0;
+    const int kend = half ? n_keys : min(n_keys, hsplit);
     const int g4 = lane >> 4;
     const size_t head_off = (size_t)kvh * a.max_ctx * kHeadDim;
     const uint16_t *kb = a.kc + head_off;
@@ -372,12 +406,12 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
     float m = -INFINITY, l = 0.f;
     const float sl2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
 
-    load_tile(0);
-    for (int k0 = 0; k0 < n_keys; k0 += kKT) {
+    if (kbeg < kend) load_tile(kbeg);
+    for (int k0 = kbeg; k0 < kend; k0 += kKT) {
         __syncthreads();  // previous tile fully consumed
         store_tile();
         __syncthreads();
-        if (k0 + kKT < n_keys) load_tile(k0 + kKT);  // next tile in flight during this one
+        if (k0 + kKT < kend) load_tile(k0 + kKT);  // next tile in flight during this one
 
         // S^T tiles: lane holds scores of keys k0 + 16*kt + 4*g4 + r for its query
         float sc[4][4];
@@ -402,8 +436,11 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
             for (int r = 0; r < 4; ++r) tm = fmaxf(tm, sc[kt][r]);
         tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
         tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+        // A query of the second key half may see no unmasked key yet (its max still -inf): exponentiate
+        // against 0 then, which gives zero weights instead of inf - inf.
         const float mn = fmaxf(m, tm);
-        const float alpha = exp2f(m - mn);
+        const float mref = mn == -INFINITY ? 0.f : mn;
+        const float alpha = exp2f(m - mref);
         m = mn;
         l *= alpha;
 #pragma unroll
@@ -415,7 +452,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const int kt0 = 2 * kb2 + (e >> 2), r0 = e & 3;
-                const float p0 = exp2f(sc[kt0][r0] - mn), p1 = exp2f(sc[kt0][r0 + 1] - mn);
+                const float p0 = exp2f(sc[kt0][r0] - mref), p1 = exp2f(sc[kt0][r0 + 1] - mref);
                 l += p0 + p1;
                 pw[kb2][e >> 1] = (uint32_t)f32_to_h16(p0) | ((uint32_t)f32_to_h16(p1) << 16);
             }
@@ -434,6 +471,45 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
         }
     }
 
+    // Pair the two halves.  The first to arrive publishes its state and leaves; the second takes it and
+    // merges.  The state slot holds the empty pattern (all ones, a NaN the arithmetic never produces) between
+    // uses, and every word is stored and loaded at device scope, so the second workgroup can tell a word
+    // that has not landed yet from a published one without a cache-wide fence; the merger restores the empty
+    // pattern after reading.  m is uniform over the four lanes of a query; l is this lane's partial sum.
+    {
+        const size_t unit = (size_t)qb * a.HKV + kvh;
+        unsigned *slot = a.part + unit * kPfState * 512 + tid;
+        __shared__ unsigned s_second;
+        __syncthreads();
+        if (tid == 0) s_second = atomicAdd(a.cnt + unit, 1u) & 1u;
+        __syncthreads();
+        if (!s_second) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pf_put(slot + (4 * i + r) * 512, o[i][r]);
+            pf_put(slot + 32 * 512, m);
+            pf_put(slot + 33 * 512, l);
+            return;
+        }
+        bool ok = true;
+        const float m_o = pf_take(slot + 32 * 512, ok), l_o = pf_take(slot + 33 * 512, ok);
+        const float m0 = half ? m_o : m, m1 = half ? m : m_o;
+        const float mm = fmaxf(m0, m1);
+        const float s0 = exp2f(m0 - mm), s1 = exp2f(m1 - mm);
+        // operands picked first, then one expression: first half's term, then the second's
+        const float la = half ? l_o : l, lb = half ? l : l_o;
+        l = la * s0 + lb * s1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ov = pf_take(slot + (4 * i + r) * 512, ok);
+                const float oa = half ? ov : o[i][r], ob = half ? o[i][r] : ov;
+                o[i][r] = oa * s0 + ob * s1;
+            }
+        if (!ok) atomicOr(a.status, kPfStatusTimeout);
+    }
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     if (tq < a.T) {
@@ -448,7 +524,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
 
 hipError_t launch_attn_prefill(int G, const AttnPrefillArgs &a, hipStream_t st) {
     const int QB = 16 * (8 / G);
-    const dim3 grid((a.T + QB - 1) / QB, a.HKV);
+    const dim3 grid(2 * ((a.T + QB - 1) / QB) * a.HKV);
     switch (G) {
         case 1: hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(512), 0, st, a); break;
         case 2: hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, dim3(512), 0, st, a); break;
@@ -458,6 +534,8 @@ hipError_t launch_attn_prefill(int G, const AttnPrefillArgs &a, hipStream_t st) 
     return hipGetLastError();
 }
 
+int attn_prefill_qb(int G) { return G == 1 || G == 2 || G == 4 ? 16 * (8 / G) : 0; }
+
 inline int32_t dev_rc(hipError_t e) { return e == hipSuccess ? QW3_OK : QW3_DEVICE_ERROR; }
 #define QW3_PF_TRY(expr)                                  \
     do {                                                  \
@@ -465,6 +543,15 @@ inline int32_t dev_rc(hipError_t e) { return e == hipSuccess ? QW3_OK : QW3_DEVI
     } while (0)
 
 }  // namespace
+
+uint64_t attn_prefill_counter_bytes(const Dims &d) {
+    const int qb = attn_prefill_qb(d.G);
+    if (!d.mfma_prefill || !qb) return 0;
+    return (uint64_t)((d.max_prefill + qb - 1) / qb) * d.HKV * sizeof(unsigned);
+}
+uint64_t attn_prefill_partial_bytes(const Dims &d) {
+    return attn_prefill_counter_bytes(d) / sizeof(unsigned) * kPfState * 512 * sizeof(unsigned);
+}
 
 hipError_t launch_bf16_to_f16(const void *in, void *out, size_t n, hipStream_t st) {
     hipLaunchKernelGGL(bf16_to_f16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const uint16_t *)in,
@@ -518,6 +605,9 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         at.HKV = d.HKV;
         at.max_ctx = d.max_ctx;
         at.out16 = attn16;
+        at.part = (unsigned *)(arena + L.pf_part);
+        at.cnt = (unsigned *)(arena + L.pf_cnt);
+        at.status = (int *)(arena + L.status);
         QW3_PF_TRY(launch_attn_prefill(d.G, at, st));
         g.A = attn16;
         g.W = wo;
