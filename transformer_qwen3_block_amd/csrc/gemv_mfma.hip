@@ -104,18 +104,20 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
     float sc[NB];
     int t = blockIdx.x;
     load_tile(t, cw, sc);
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
     uint4 a1h[NP], a1l[NP], a2h[NP], a2l[NP];
     if (a.norm_w) {
         // RMSNorm input ([P1] section 2 items 1 and 6): w * (x * inv) with inv = 1 / sqrt(mean(x^2) + eps) of
         // the sequence, from the per-16-row sums of squares (tile order, then a fixed 16-lane tree); the
         // residual stream itself may exceed the f16 range, the normalised operand does not
         float xv[NP][16], gv[NP][16];
+        const int xrow = c < S ? c : S - 1;  // lanes of absent sequences read a present row (zeroed below)
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int k = (kb0 + 2 * p) * 32 + 16 * q;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float4 xx = *(const float4 *)(a.x + (size_t)c * a.ldx + k + 4 * i);
+                const float4 xx = *(const float4 *)(a.x + (size_t)xrow * a.ldx + k + 4 * i);
                 const float4 gg = *(const float4 *)(a.norm_w + k + 4 * i);
                 xv[p][4 * i] = xx.x; xv[p][4 * i + 1] = xx.y; xv[p][4 * i + 2] = xx.z; xv[p][4 * i + 3] = xx.w;
                 gv[p][4 * i] = gg.x; gv[p][4 * i + 1] = gg.y; gv[p][4 * i + 2] = gg.z; gv[p][4 * i + 3] = gg.w;
@@ -124,7 +126,8 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
         if (tid < 256) {
             const int s = tid >> 4, pp = tid & 15;
             float ss = 0.f;
-            for (int tt = pp; tt < K / 16; tt += 16) ss += a.ssq[tt * kMaxSeq + s];
+            if (s < S)
+                for (int tt = pp; tt < K / 16; tt += 16) ss += a.ssq[tt * kMaxSeq + s];
             ss = row16_sum(ss);
             if (pp == 0) s_inv[s] = 1.0f / sqrtf(ss / (float)K + a.eps);
         }
@@ -152,10 +155,11 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const size_t o = (((size_t)(kb0 / 2 + p) * 4 + q) * kMaxSeq + c) * 16;
-            a1h[p] = *(const uint4 *)(a.a_hi + o);
-            a2h[p] = *(const uint4 *)(a.a_hi + o + 8);
-            a1l[p] = *(const uint4 *)(a.a_lo + o);
-            a2l[p] = *(const uint4 *)(a.a_lo + o + 8);
+            const bool on = c < S;  // absent sequences: zero operands, no read outside this batch's slots
+            a1h[p] = on ? *(const uint4 *)(a.a_hi + o) : z4;
+            a2h[p] = on ? *(const uint4 *)(a.a_hi + o + 8) : z4;
+            a1l[p] = on ? *(const uint4 *)(a.a_lo + o) : z4;
+            a2l[p] = on ? *(const uint4 *)(a.a_lo + o + 8) : z4;
         }
     }
 
@@ -163,7 +167,6 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
     float best = -INFINITY;
     int besti = 0x7fffffff, bad = 0;
     const int es = tid >> 4, er = tid & 15;  // epilogue thread: sequence, row slot
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
 
     for (; t < ntiles; t += gridDim.x) {
         uint4 cn[NP];
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
                 }
                 if (a.ssq_mode == 2) {
                     const float ss = row16_sum(nv * nv);  // the 16 rows of the tile, one sequence per 16 lanes
-                    if (er == 0) a.ssq[t * kMaxSeq + es] = ss;
+                    if (er == 0 && es < S) a.ssq[t * kMaxSeq + es] = ss;
                 }
             } else if constexpr (EPI == EPI_SWIGLU) {
                 const float up = dpp_mov<0x128>(v);  // row_ror:8 -- slot er + 8 holds the up row of slot er
