@@ -74,11 +74,15 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float *x, int H
 
 // ---------------------------------------------------------------------------------------------------
 // C[M, N] = A[M, K] * W[N, K]^T on f16 MFMA with f32 accumulation.
-// Workgroup tile BM x BN, K in steps of 64 staged through LDS (next step prefetched into registers while
-// the current one is multiplied); WM x WN waves, each owning a (BM/WM) x (BN/WN) block of 16x16 tiles.
-// Epilogues: f32 store, f32 residual add (in place), or SwiGLU into f16: with GLU, each wave's columns
-// are half gate rows and half the matching up rows (up rows start at W row `up_off`), so gate and up of
-// one output element meet in the same lane.
+// Workgroup tile BM x BN; WM x WN waves, each owning a (BM/WM) x (BN/WN) block of 16x16 tiles.  K runs in
+// steps of 64: step j is multiplied from LDS buffer j&1 while step j+1 is written into the other buffer from
+// registers, and the global loads of step j+3 are issued into the registers that step j+1 just left, so
+// every load has two steps of products to hide behind and each step needs one barrier.  Workgroups are mapped
+// so that the tiles one XCD runs (workgroup b runs on XCD b mod 8) share their column blocks, which keeps
+// their weight rows in that XCD's L2.
+// Epilogues: f32 store, f32 residual add (in place), or SwiGLU into f16: with GLU, each wave's columns are
+// half gate rows and half the matching up rows (up rows start at W row `up_off`), so gate and up of one
+// output element meet in the same lane.
 // ---------------------------------------------------------------------------------------------------
 enum GemmEpi { G_STORE = 0, G_RESID = 1, G_SWIGLU = 2 };
 
@@ -93,7 +97,7 @@ struct GemmArgs {
 };
 
 constexpr int kBK = 64;
-constexpr int kLdsPad = 8;  // 16-bit elements of padding per LDS row
+constexpr int kLdsPad = 16;  // 16-bit elements of padding per LDS row (32 bytes: measured fastest of 0, 8, 16, 24, 32)
 
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
@@ -104,12 +108,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
     constexpr int ACH = BM * kBK / 8 / NT;  // 16-byte chunks per thread per A step
     constexpr int BCH = BN * kBK / 8 / NT;
     static_assert(ACH >= 1 && BCH >= 1 && TM >= 1 && TN >= 1, "tile too small for the wave layout");
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDR];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDR];
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDR];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDR];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WN, wn = wave % WN;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    // XCD-aware tile order: the tiles of one XCD are consecutive in column-major tile order
+    const int ntm = (g.M + BM - 1) / BM, nt = ntm * (g.N / BN);
+    int tile = blockIdx.x;
+    if (nt % 8 == 0) tile = (blockIdx.x & 7) * (nt / 8) + (blockIdx.x >> 3);
+    const int m0 = (tile % ntm) * BM, n0 = (tile / ntm) * BN;
 
     // weight row of tile row r
     auto wrow = [&](int r) -> long long {
@@ -122,63 +130,87 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
         }
     };
 
-    uint4 ra[ACH], rb[BCH];
-    auto load_tiles = [&](int k0) {
+    // Loads are unconditional (rows past M read row M-1, whose products the epilogue drops; steps past the
+    // last re-read it), so the loop body is branch-free and the compiler can wait for exactly the step it
+    // stores instead of for every load in flight.
+    // Per-thread chunk addresses are formed once; a step only adds its column offset.
+    const uint16_t *pa[ACH];
+    const uint16_t *pb[BCH];
+    int la[ACH], lb[BCH];
+#pragma unroll
+    for (int c = 0; c < ACH; ++c) {
+        const int ch = tid + NT * c, r = ch >> 3, kc = (ch & 7) * 8;
+        pa[c] = g.A + (size_t)min(m0 + r, g.M - 1) * g.K + kc;
+        la[c] = r * LDR + kc;
+    }
+#pragma unroll
+    for (int c = 0; c < BCH; ++c) {
+        const int ch = tid + NT * c, r = ch >> 3, kc = (ch & 7) * 8;
+        pb[c] = g.W + (size_t)wrow(r) * g.K + kc;
+        lb[c] = r * LDR + kc;
+    }
+    // Two register stages in named arrays (no indexing, so they stay in registers and every load keeps its
+    // own destination until it is stored): while step j is multiplied, steps j+1 and j+2 are in flight.
+    const int nsteps = g.K / kBK;
+    uint4 a0[ACH], b0[BCH], a1[ACH], b1[BCH];
+    auto load_step = [&](uint4 (&xa)[ACH], uint4 (&xb)[BCH], int step) {
+        const int k0 = min(step, nsteps - 1) * kBK;
 #pragma unroll
         for (int c = 0; c < ACH; ++c) {
-            const int ch = tid + NT * c, r = ch >> 3, kc = (ch & 7) * 8;
-            const int m = m0 + r;
-            ra[c] = m < g.M ? *(const uint4 *)(g.A + (size_t)m * g.K + k0 + kc) : make_uint4(0, 0, 0, 0);
+            const u32x4_t v = *(const u32x4_t *)(pa[c] + k0);  // vector-typed load: stays in registers
+            xa[c] = make_uint4(v.x, v.y, v.z, v.w);
         }
 #pragma unroll
-        for (int c = 0; c < BCH; ++c) {
-            const int ch = tid + NT * c, r = ch >> 3, kc = (ch & 7) * 8;
-            rb[c] = load_nt16(g.W + (size_t)wrow(r) * g.K + k0 + kc);
-        }
+        for (int c = 0; c < BCH; ++c) xb[c] = load_nt16(pb[c] + k0);
     };
-    auto store_tiles = [&]() {
+    auto store_step = [&](const uint4 (&xa)[ACH], const uint4 (&xb)[BCH], int buf) {
 #pragma unroll
-        for (int c = 0; c < ACH; ++c) {
-            const int ch = tid + NT * c, r = ch >> 3, kc = (ch & 7) * 8;
-            *(uint4 *)(As + r * LDR + kc) = ra[c];
-        }
+        for (int c = 0; c < ACH; ++c) *(uint4 *)(&As[buf][la[c]]) = xa[c];
 #pragma unroll
-        for (int c = 0; c < BCH; ++c) {
-            const int ch = tid + NT * c, r = ch >> 3, kc = (ch & 7) * 8;
-            *(uint4 *)(Bs + r * LDR + kc) = rb[c];
-        }
+        for (int c = 0; c < BCH; ++c) *(uint4 *)(&Bs[buf][lb[c]]) = xb[c];
     };
 
     f32x4_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    load_tiles(0);
-    store_tiles();
-    __syncthreads();
     const int ksub = 8 * (lane >> 4), lrow = lane & 15;
-    for (int k0 = 0; k0 < g.K; k0 += kBK) {
-        const bool more = k0 + kBK < g.K;
-        if (more) load_tiles(k0 + kBK);
+    auto multiply = [&](int buf) {
+        const uint16_t *as = As[buf], *bs = Bs[buf];
 #pragma unroll
         for (int kk = 0; kk < kBK; kk += 32) {
             uint4 af[TM], bfr[TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) af[i] = *(const uint4 *)(As + (wm * WTM + i * 16 + lrow) * LDR + kk + ksub);
+            for (int i = 0; i < TM; ++i) af[i] = *(const uint4 *)(as + (wm * WTM + i * 16 + lrow) * LDR + kk + ksub);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) bfr[j] = *(const uint4 *)(Bs + (wn * WTN + j * 16 + lrow) * LDR + kk + ksub);
+            for (int jj = 0; jj < TN; ++jj)
+                bfr[jj] = *(const uint4 *)(bs + (wn * WTN + jj * 16 + lrow) * LDR + kk + ksub);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+                for (int jj = 0; jj < TN; ++jj) acc[i][jj] = mfma16(af[i], bfr[jj], acc[i][jj]);
         }
+    };
+
+    // steps past the last re-read the last one (their stores are never multiplied)
+    load_step(a0, b0, 0);
+    load_step(a1, b1, 1);
+    store_step(a0, b0, 0);
+    load_step(a0, b0, 2);
+    __syncthreads();
+    for (int j = 0; j < nsteps; j += 2) {  // nsteps is even
+        // a1: step j+1, a0: step j+2 in flight; LDS buffer 0 holds step j
+        store_step(a1, b1, 1);
+        load_step(a1, b1, j + 3);
+        multiply(0);
         __syncthreads();
-        if (more) {
-            store_tiles();
-            __syncthreads();
-        }
+        // a0: step j+2, a1: step j+3; buffer 1 holds step j+1
+        store_step(a0, b0, 0);
+        load_step(a0, b0, j + 4);
+        multiply(1);
+        __syncthreads();
     }
 
     // epilogue: lane holds C[4*(lane/16) + r][lane%16] of each 16x16 tile
@@ -191,45 +223,45 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
             if (m >= g.M) continue;
             if constexpr (EPI == G_SWIGLU) {
 #pragma unroll
-                for (int j = 0; j < TN / 2; ++j) {
-                    const int col = n0 / 2 + wn * (WTN / 2) + j * 16 + ccol;
-                    const float gt = acc[i][j][r], up = acc[i][j + TN / 2][r];
+                for (int jj = 0; jj < TN / 2; ++jj) {
+                    const int col = n0 / 2 + wn * (WTN / 2) + jj * 16 + ccol;
+                    const float gt = acc[i][jj][r], up = acc[i][jj + TN / 2][r];
                     // SwiGLU, [P1] section 5: (g * sigmoid(g)) * u
                     const float sig = 1.0f / (1.0f + __expf(-gt));
                     g.out16[(size_t)m * g.ldo + col] = f32_to_h16((gt * sig) * up);
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int n = n0 + wn * WTN + j * 16 + ccol;
+                for (int jj = 0; jj < TN; ++jj) {
+                    const int n = n0 + wn * WTN + jj * 16 + ccol;
                     float *p = g.outf + (size_t)m * g.ldo + n;
                     if constexpr (EPI == G_STORE)
-                        *p = acc[i][j][r];
+                        *p = acc[i][jj][r];
                     else
-                        *p = *p + acc[i][j][r];
+                        *p = *p + acc[i][jj][r];
                 }
             }
         }
     }
 }
 
+template <int BM, int BN, int WM, int WN, int EPI>
+hipError_t launch_gemm_cfg(const GemmArgs &g, hipStream_t st) {
+    if (g.K % (2 * kBK) || g.N % BN) return hipErrorInvalidValue;
+    const int nt = ((g.M + BM - 1) / BM) * (g.N / BN);
+    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, WM, WN, EPI>), dim3(nt), dim3(64 * WM * WN), 0, st, g);
+    return hipGetLastError();
+}
+
+// Tile shapes measured fastest on the 2048-token shapes (Q/K/V 4096 x 1024, gate/up 6144 x 1024, o_proj
+// 1024 x 2048, down 1024 x 3072).
 template <int EPI>
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
-    if (g.K % kBK || g.N % 128) return hipErrorInvalidValue;
-    const int mt128 = (g.M + 127) / 128;
-    if (g.M <= 64) {
-        // short prompts: weight-streaming bound; many narrow column tiles, all rows in one tile
-        const dim3 grid(g.N / 32, (g.M + 63) / 64);
-        hipLaunchKernelGGL((gemm_f16_kernel<64, 32, 4, 1, EPI>), grid, dim3(256), 0, st, g);
-    } else if (mt128 * (g.N / 128) < 512) {
-        // narrow outputs (o_proj, down): 64x64 tiles so every CU gets at least two workgroups
-        const dim3 grid(g.N / 64, (g.M + 63) / 64);
-        hipLaunchKernelGGL((gemm_f16_kernel<64, 64, 2, 2, EPI>), grid, dim3(256), 0, st, g);
-    } else {
-        const dim3 grid(g.N / 128, mt128);
-        hipLaunchKernelGGL((gemm_f16_kernel<128, 128, 4, 2, EPI>), grid, dim3(512), 0, st, g);
-    }
-    return hipGetLastError();
+    if (g.K % (2 * kBK) || g.N % 128) return hipErrorInvalidValue;
+    if (g.M <= 64) return launch_gemm_cfg<64, 32, 4, 1, EPI>(g, st);  // short prompts: weight-streaming bound
+    if (EPI != G_SWIGLU && g.N <= 1024) return launch_gemm_cfg<128, 64, 4, 1, EPI>(g, st);  // narrow outputs
+    if (EPI == G_STORE && ((g.M + 255) / 256) * (g.N / 128) >= 256) return launch_gemm_cfg<256, 128, 4, 2, EPI>(g, st);
+    return launch_gemm_cfg<128, 128, 4, 2, EPI>(g, st);
 }
 
 // ---------------------------------------------------------------------------------------------------
