@@ -38,6 +38,13 @@ __device__ __forceinline__ uint32_t bf16x2_to_h16x2(uint32_t w) {
     return (uint32_t)f32_to_h16(bf16_lo(w)) | ((uint32_t)f32_to_h16(bf16_hi(w)) << 16);
 }
 
+// bf16 pair -> f16 pair in one packed conversion (round toward zero): exact wherever the value is an f16
+// normal number (bf16 carries 8 significant bits, f16 11); below 2^-14 it differs from round-to-nearest by
+// at most 2^-24.
+__device__ __forceinline__ uint32_t bf16x2_to_h16x2_pk(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(w), bf16_hi(w)));
+}
+
 __global__ void bf16_to_f16_kernel(const uint16_t *in, uint16_t *out, size_t n) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) out[i] = f32_to_h16(bf16_to_f32(in[i]));
@@ -266,7 +273,7 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
 
 // ---------------------------------------------------------------------------------------------------
 // QK-Norm + RoPE of every query/key head of T tokens ([P1] section 2 items 3-4) and the KV append
-// ([P1] section 6): query heads go to q16 (f16, [T][HQ][128]); keys (normalised, rotated) and values are
+// ([P1] section 6): query heads go to q16 (f16, [T][HQ][128], scaled for the attention kernel); keys (normalised, rotated) and values are
 // rounded to bf16 into the cache at positions pos0..pos0+T-1.  One workgroup per token, one wave per head
 // at a time; lane i holds dims i and i+64, which is exactly a RoPE pair.
 // ---------------------------------------------------------------------------------------------------
@@ -288,9 +295,12 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(const float *qk
         const float n0 = w[lane] * (v0 * inv), n1 = w[lane + 64] * (v1 * inv);
         const float r0 = n0 * c - n1 * sn, r1 = n1 * c + n0 * sn;
         if (is_q) {
+            // queries carry the attention scale in log2 units, 1/sqrt(128) * log2(e), applied before the f16
+            // rounding so the attention kernel's scores come out of the MFMA ready for exp2
+            const float qs = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
             uint16_t *dst = q16 + ((size_t)t * HQ + h) * kHeadDim;
-            dst[lane] = f32_to_h16(r0);
-            dst[lane + 64] = f32_to_h16(r1);
+            dst[lane] = f32_to_h16(r0 * qs);
+            dst[lane + 64] = f32_to_h16(r1 * qs);
         } else {
             const int hk = h - HQ;
             const size_t at = ((size_t)hk * max_ctx + pos) * kHeadDim;
@@ -320,7 +330,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(const float *qk
 // transpose of P is needed.  Online softmax in log2 units; Q, K, V and P enter the MFMA as f16.
 // ---------------------------------------------------------------------------------------------------
 struct AttnPrefillArgs {
-    const uint16_t *q16;      // f16 [T][HQ][128]
+    const uint16_t *q16;      // f16 [T][HQ][128], pre-multiplied by log2(e) / sqrt(128)
     const uint16_t *kc, *vc;  // bf16 cache, head 0 of (seq, layer): [HKV][max_ctx][128]
     int T, pos0, HQ, HKV, max_ctx;
     uint16_t *out16;          // f16 [T][HQ*128]
@@ -328,7 +338,7 @@ struct AttnPrefillArgs {
     unsigned *cnt;            // [query block][HKV] arrival counters, even between launches
     int *status;              // bit 4 set if a published state never arrived (bounded wait)
 };
-constexpr int kPfState = 34;              // o[32], m, l per thread
+constexpr int kPfState = 34;              // per thread: m, l, then o[32]
 constexpr unsigned kPfEmpty = 0xffffffffu;  // slot word not yet published
 constexpr int kPfStatusTimeout = 4;
 constexpr int kPfSpin = 1 << 20;          // polling rounds before giving up (far beyond any legitimate wait)
@@ -336,16 +346,25 @@ constexpr int kPfSpin = 1 << 20;          // polling rounds before giving up (fa
 __device__ __forceinline__ void pf_put(unsigned *p, float v) {
     __hip_atomic_store(p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Takes a published word and restores the empty pattern; ok turns false if the wait ran out.
-__device__ __forceinline__ float pf_take(unsigned *p, bool &ok) {
-    unsigned v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int n = 0; v == kPfEmpty && n < kPfSpin; ++n) {
-        __builtin_amdgcn_s_sleep(1);
-        v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Takes N published words p[0], p[stride], ... and restores the empty pattern: all N loads are issued
+// before the first is examined (one memory round trip, not N); a word still empty is polled on its own.
+// ok turns false if a wait ran out.
+template <int N>
+__device__ __forceinline__ void pf_take(unsigned *p, int stride, float (&out)[N], bool &ok) {
+    unsigned v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = __hip_atomic_load(p + i * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        for (int n = 0; v[i] == kPfEmpty && n < kPfSpin; ++n) {
+            __builtin_amdgcn_s_sleep(1);
+            v[i] = __hip_atomic_load(p + i * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        ok = ok && v[i] != kPfEmpty;
+        out[i] = __uint_as_float(v[i]);
     }
-    ok = ok && v != kPfEmpty;
-    __hip_atomic_store(p, kPfEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return __uint_as_float(v);
+#pragma unroll
+    for (int i = 0; i < N; ++i) __hip_atomic_store(p + i * stride, kPfEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 constexpr int kKT = 64;                  // keys per tile
@@ -392,15 +411,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
             const int ch = tid + 64 * NW * c, key = ch >> 4, dc = (ch & 15) * 8;
-            const int p = k0 + key;
-            kreg[c] = p < n_keys ? *(const uint4 *)(kb + (size_t)p * kHeadDim + dc) : make_uint4(0, 0, 0, 0);
+            // keys past the end read the last key's row (finite; masked out of the scores), so the tile
+            // loads are unconditional and the loop has no branches around them
+            const int p = min(k0 + key, n_keys - 1);
+            const u32x4_t v = *(const u32x4_t *)(kb + (size_t)p * kHeadDim + dc);
+            kreg[c] = make_uint4(v.x, v.y, v.z, v.w);
         }
 #pragma unroll
         for (int bt = 0; bt < KPW / 4; ++bt)
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int p = k0 + KPW * wave + 4 * bt + k;
-                vreg[bt][k] = p < n_keys ? *(const uint32_t *)(vb + (size_t)p * kHeadDim + 2 * lane) : 0u;
+                const int p = min(k0 + KPW * wave + 4 * bt + k, n_keys - 1);  // weight 0 past the end
+                vreg[bt][k] = *(const uint32_t *)(vb + (size_t)p * kHeadDim + 2 * lane);
             }
     };
     auto store_tile = [&]() {
@@ -409,13 +431,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
             const int ch = tid + 64 * NW * c, key = ch >> 4, dc = (ch & 15) * 8;
             const uint4 kv = kreg[c];
             *(uint4 *)(Ks + key * kKsLd + dc) =
-                make_uint4(bf16x2_to_h16x2(kv.x), bf16x2_to_h16x2(kv.y), bf16x2_to_h16x2(kv.z), bf16x2_to_h16x2(kv.w));
+                make_uint4(bf16x2_to_h16x2_pk(kv.x), bf16x2_to_h16x2_pk(kv.y), bf16x2_to_h16x2_pk(kv.z),
+                           bf16x2_to_h16x2_pk(kv.w));
         }
 #pragma unroll
         for (int bt = 0; bt < KPW / 4; ++bt) {
             uint32_t h[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) h[k] = bf16x2_to_h16x2(vreg[bt][k]);
+            for (int k = 0; k < 4; ++k) h[k] = bf16x2_to_h16x2_pk(vreg[bt][k]);
             // dim 2*lane: low halves of the four keys; dim 2*lane+1: high halves
             const uint2 lo = make_uint2((h[0] & 0xffffu) | (h[1] << 16), (h[2] & 0xffffu) | (h[3] << 16));
             const uint2 hi = make_uint2((h[0] >> 16) | (h[1] & 0xffff0000u), (h[2] >> 16) | (h[3] & 0xffff0000u));
@@ -436,7 +459,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f;
-    const float sl2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
+    // queries enter already multiplied by log2(e) / sqrt(128) (see qknorm_rope_append_kernel)
+    const int qpos_min = a.pos0 + t0 + (wave % WPH) * 16;  // first query position of this wave
 
     if (kbeg < kend) load_tile(kbeg);
     for (int k0 = kbeg; k0 < kend; k0 += kKT) {
@@ -445,7 +469,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
         __syncthreads();
         if (k0 + kKT < kend) load_tile(k0 + kKT);  // next tile in flight during this one
 
-        // S^T tiles: lane holds scores of keys k0 + 16*kt + 4*g4 + r for its query
+        // S^T tiles: lane holds scores of keys k0 + 16*kt + 4*g4 + r for its query.  Only tiles that reach
+        // past the wave's first query or past the last key need the causal / length mask.
+        const bool unmasked = k0 + kKT - 1 <= qpos_min && k0 + kKT <= n_keys;
         float sc[4][4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
@@ -456,10 +482,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
                 sv = mfma16(kf, qf[ks], sv);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int kp = k0 + 16 * kt + 4 * g4 + r;
-                sc[kt][r] = kp <= qpos && kp < n_keys ? sv[r] * sl2 : -INFINITY;
-            }
+            for (int r = 0; r < 4; ++r) sc[kt][r] = sv[r];
+        }
+        if (!unmasked) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int kp = k0 + 16 * kt + 4 * g4 + r;
+                    if (kp > qpos || kp >= n_keys) sc[kt][r] = -INFINITY;
+                }
         }
         float tm = -INFINITY;
 #pragma unroll
@@ -475,8 +507,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
         const float alpha = exp2f(m - mref);
         m = mn;
         l *= alpha;
+        if (__any(alpha != 1.0f))  // once the row maxima settle most tiles leave the output unscaled
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] *= alpha;
+            for (int i = 0; i < 8; ++i) o[i] *= alpha;
         // probabilities as f16 pairs: P^T fragments for the two 32-key halves of the tile
         uint32_t pw[2][4];
 #pragma unroll
@@ -516,30 +549,41 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
         if (tid == 0) s_second = atomicAdd(a.cnt + unit, 1u) & 1u;
         __syncthreads();
         if (!s_second) {
+            pf_put(slot, m);
+            pf_put(slot + 512, l);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) pf_put(slot + (4 * i + r) * 512, o[i][r]);
-            pf_put(slot + 32 * 512, m);
-            pf_put(slot + 33 * 512, l);
+                for (int r = 0; r < 4; ++r) pf_put(slot + (2 + 4 * i + r) * 512, o[i][r]);
             return;
         }
         bool ok = true;
-        const float m_o = pf_take(slot + 32 * 512, ok), l_o = pf_take(slot + 33 * 512, ok);
-        const float m0 = half ? m_o : m, m1 = half ? m : m_o;
+        float w[10];
+        pf_take<10>(slot, 512, w, ok);  // m, l, o[0][0..3], o[1][0..3]
+        const float m0 = half ? w[0] : m, m1 = half ? m : w[0];
         const float mm = fmaxf(m0, m1);
         const float s0 = exp2f(m0 - mm), s1 = exp2f(m1 - mm);
         // operands picked first, then one expression: first half's term, then the second's
-        const float la = half ? l_o : l, lb = half ? l : l_o;
-        l = la * s0 + lb * s1;
+        auto comb = [&](float mine, float other) {
+            const float xa = half ? other : mine, xb = half ? mine : other;
+            return xa * s0 + xb * s1;
+        };
+        l = comb(l, w[1]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int r = 0; r < 4; ++r) {
+            o[0][r] = comb(o[0][r], w[2 + r]);
+            o[1][r] = comb(o[1][r], w[6 + r]);
+        }
+#pragma unroll
+        for (int i = 2; i < 8; i += 2) {
+            float w8[8];
+            pf_take<8>(slot + (2 + 4 * i) * 512, 512, w8, ok);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float ov = pf_take(slot + (4 * i + r) * 512, ok);
-                const float oa = half ? ov : o[i][r], ob = half ? o[i][r] : ov;
-                o[i][r] = oa * s0 + ob * s1;
+                o[i][r] = comb(o[i][r], w8[r]);
+                o[i + 1][r] = comb(o[i + 1][r], w8[4 + r]);
             }
+        }
         if (!ok) atomicOr(a.status, kPfStatusTimeout);
     }
     l += __shfl_xor(l, 16, 64);
