@@ -368,8 +368,10 @@ __device__ __forceinline__ void pf_take(unsigned *p, int stride, float (&out)[N]
 }
 
 constexpr int kKT = 64;                  // keys per tile
-constexpr int kKsLd = kHeadDim + 8;      // K tile row stride (f16 elements)
-constexpr int kVtLd = kKT + 8;           // V^T tile row stride (f16 elements)
+// LDS rows are 64 f16 wide with a stride of 80 (160 bytes): measured free of bank conflicts for the 16-byte
+// fragment reads (16 rows x four 16-byte columns per instruction), where strides of 72 or 136 cost a 2-way
+// conflict.  K is kept as two such arrays (dims 0-63, 64-127); V^T rows hold the tile's 64 keys.
+constexpr int kLdsLd = 80;
 
 template <int G>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void attn_prefill_kernel(AttnPrefillArgs a) {
@@ -377,8 +379,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
     constexpr int WPH = NW / G;   // waves per query head
     constexpr int QB = 16 * WPH;  // queries per workgroup
     constexpr int KPW = kKT / NW; // keys of a tile whose V this wave stages
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[kKT * kKsLd];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * kVtLd];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * kKT * kLdsLd];     // [dim / 64][key][dim % 64]
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * kLdsLd];    // [dim][key position]
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nqb = (a.T + QB - 1) / QB;
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
         for (int c = 0; c < KCH; ++c) {
             const int ch = tid + 64 * NW * c, key = ch >> 4, dc = (ch & 15) * 8;
             const uint4 kv = kreg[c];
-            *(uint4 *)(Ks + key * kKsLd + dc) =
+            *(uint4 *)(Ks + ((dc >> 6) * kKT + key) * kLdsLd + (dc & 63)) =
                 make_uint4(bf16x2_to_h16x2_pk(kv.x), bf16x2_to_h16x2_pk(kv.y), bf16x2_to_h16x2_pk(kv.z),
                            bf16x2_to_h16x2_pk(kv.w));
         }
@@ -442,9 +444,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
             // dim 2*lane: low halves of the four keys; dim 2*lane+1: high halves
             const uint2 lo = make_uint2((h[0] & 0xffffu) | (h[1] << 16), (h[2] & 0xffffu) | (h[3] << 16));
             const uint2 hi = make_uint2((h[0] >> 16) | (h[1] & 0xffff0000u), (h[2] >> 16) | (h[3] & 0xffff0000u));
-            const int key0 = KPW * wave + 4 * bt;
-            *(uint2 *)(Vt + (2 * lane) * kVtLd + key0) = lo;
-            *(uint2 *)(Vt + (2 * lane + 1) * kVtLd + key0) = hi;
+            // Key positions: within each 32-key half, the four-key groups {4g..4g+3} and {16+4g..16+4g+3}
+            // sit side by side, so one 16-byte read gives a lane the eight keys its P^T fragment covers.
+            const int key0 = KPW * wave + 4 * bt, kk = key0 & 31;
+            const int pos = (key0 & 32) + 8 * ((kk & 15) >> 2) + 4 * (kk >> 4);
+            *(uint2 *)(Vt + (2 * lane) * kLdsLd + pos) = lo;
+            *(uint2 *)(Vt + (2 * lane + 1) * kLdsLd + pos) = hi;
         }
     };
 
@@ -478,7 +483,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
             f32x4_t sv = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const uint4 kf = *(const uint4 *)(Ks + (16 * kt + (lane & 15)) * kKsLd + 32 * ks + 8 * g4);
+                const uint4 kf =
+                    *(const uint4 *)(Ks + ((ks >> 1) * kKT + 16 * kt + (lane & 15)) * kLdsLd + 32 * (ks & 1) + 8 * g4);
                 sv = mfma16(kf, qf[ks], sv);
             }
 #pragma unroll
@@ -528,10 +534,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
             const uint4 pb = make_uint4(pw[kb2][0], pw[kb2][1], pw[kb2][2], pw[kb2][3]);
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
-                const uint16_t *vr = Vt + (16 * dt + (lane & 15)) * kVtLd + 32 * kb2 + 4 * g4;
-                const uint2 lo = *(const uint2 *)vr;
-                const uint2 hi = *(const uint2 *)(vr + 16);
-                o[dt] = mfma16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[dt]);
+                const uint4 vf = *(const uint4 *)(Vt + (16 * dt + (lane & 15)) * kLdsLd + 32 * kb2 + 8 * g4);
+                o[dt] = mfma16(vf, pb, o[dt]);
             }
         }
     }
