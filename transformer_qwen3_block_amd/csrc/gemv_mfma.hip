@@ -52,6 +52,17 @@ __device__ __forceinline__ uint4 codes_to_f16(uint2 w) {
     return __builtin_bit_cast(uint4, h);
 }
 
+// Component-wise select of two 16-byte values.  (A conditional expression on the struct type can make the
+// compiler select between two addresses and keep the operands in scratch memory.)
+__device__ __forceinline__ uint4 sel4(bool c, const uint4 &a, const uint4 &b) {
+    return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+// 16-byte load through the vector type (stays in registers)
+__device__ __forceinline__ uint4 ld16(const void *p) {
+    const u32x4_t v = *(const u32x4_t *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // f32 -> (f16 high part, f16 remainder) bits
 __device__ __forceinline__ void split_one(float v, uint16_t &hi, uint16_t &lo) {
     const _Float16 h = (_Float16)v;
@@ -97,19 +108,26 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
         for (int j = 0; j < NB; ++j) sc[j] = a.scales[row * KB + kb0 + j];
     };
 
-    // The first tile's codes, this wave's activations and the sums of squares all go out at once: one memory
-    // round trip before the first product.  Activation operands: lane (q, c) holds sequence c's columns
+    // This wave's activations go out first, then the first tile's codes (and the sums of squares): one memory
+    // round trip before the first product, the activations converted while the codes still stream (loads
+    // return in order).  Activation operands: lane (q, c) holds sequence c's columns
     // 16q..16q+15 of each block pair, as f16 high parts and remainders (a1: first eight, a2: last eight).
     uint4 cw[NP];
     float sc[NB];
     int t = blockIdx.x;
-    load_tile(t, cw, sc);
     const uint4 z4 = make_uint4(0, 0, 0, 0);
+    constexpr int kSsqPer = 1024 / 16 / 16;  // RMSNorm inputs have K = 1024: 64 tile sums, 4 per thread
     uint4 a1h[NP], a1l[NP], a2h[NP], a2l[NP];
     if (a.norm_w) {
         // RMSNorm input ([P1] section 2 items 1 and 6): w * (x * inv) with inv = 1 / sqrt(mean(x^2) + eps) of
         // the sequence, from the per-16-row sums of squares (tile order, then a fixed 16-lane tree); the
         // residual stream itself may exceed the f16 range, the normalised operand does not
+        // the tile sums of squares go out first: waiting for them does not wait for the later loads
+        float ssv[kSsqPer];
+        const int ss_s = tid >> 4, ss_p = tid & 15;
+#pragma unroll
+        for (int i = 0; i < kSsqPer; ++i)
+            ssv[i] = tid < 256 && ss_s < S ? a.ssq[(ss_p + 16 * i) * kMaxSeq + ss_s] : 0.f;
         float xv[NP][16], gv[NP][16];
         const int xrow = c < S ? c : S - 1;  // lanes of absent sequences read a present row (zeroed below)
 #pragma unroll
@@ -123,13 +141,13 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
                 gv[p][4 * i] = gg.x; gv[p][4 * i + 1] = gg.y; gv[p][4 * i + 2] = gg.z; gv[p][4 * i + 3] = gg.w;
             }
         }
+        load_tile(t, cw, sc);  // after the activations: they return first and are converted while codes stream
         if (tid < 256) {
-            const int s = tid >> 4, pp = tid & 15;
             float ss = 0.f;
-            if (s < S)
-                for (int tt = pp; tt < K / 16; tt += 16) ss += a.ssq[tt * kMaxSeq + s];
+#pragma unroll
+            for (int i = 0; i < kSsqPer; ++i) ss += ssv[i];
             ss = row16_sum(ss);
-            if (pp == 0) s_inv[s] = 1.0f / sqrtf(ss / (float)K + a.eps);
+            if (ss_p == 0) s_inv[ss_s] = 1.0f / sqrtf(ss / (float)K + a.eps);
         }
         __syncthreads();
         const float inv = s_inv[c];
@@ -156,11 +174,13 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
         for (int p = 0; p < NP; ++p) {
             const size_t o = (((size_t)(kb0 / 2 + p) * 4 + q) * kMaxSeq + c) * 16;
             const bool on = c < S;  // absent sequences: zero operands, no read outside this batch's slots
-            a1h[p] = on ? *(const uint4 *)(a.a_hi + o) : z4;
-            a2h[p] = on ? *(const uint4 *)(a.a_hi + o + 8) : z4;
-            a1l[p] = on ? *(const uint4 *)(a.a_lo + o) : z4;
-            a2l[p] = on ? *(const uint4 *)(a.a_lo + o + 8) : z4;
+            const size_t oc = on ? o : 0;  // absent sequences read slot 0 and are zeroed
+            a1h[p] = sel4(on, ld16(a.a_hi + oc), z4);
+            a2h[p] = sel4(on, ld16(a.a_hi + oc + 8), z4);
+            a1l[p] = sel4(on, ld16(a.a_lo + oc), z4);
+            a2l[p] = sel4(on, ld16(a.a_lo + oc + 8), z4);
         }
+        load_tile(t, cw, sc);
     }
 
     // logits: running greedy choice of this thread's (sequence, row slot)
@@ -168,16 +188,20 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
     int besti = 0x7fffffff, bad = 0;
     const int es = tid >> 4, er = tid & 15;  // epilogue thread: sequence, row slot
 
+    // The residual products launch one workgroup per tile; the others walk several tiles with the next
+    // tile's codes in flight.
+    constexpr bool kStride = EPI != EPI_RESID;
     for (; t < ntiles; t += gridDim.x) {
         uint4 cn[NP];
         float sn[NB];
-        load_tile(t + gridDim.x, cn, sn);
+        if constexpr (kStride) load_tile(t + gridDim.x, cn, sn);
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             // one product per block: the other block's lanes contribute zero codes
             const uint4 b1 = codes_to_f16(make_uint2(cw[p].x, cw[p].y)), b2 = codes_to_f16(make_uint2(cw[p].z, cw[p].w));
-            const uint4 b1f = first ? b1 : z4, b2f = first ? b2 : z4, b1s = first ? z4 : b1, b2s = first ? z4 : b2;
+            const uint4 b1f = sel4(first, b1, z4), b2f = sel4(first, b2, z4), b1s = sel4(first, z4, b1),
+                        b2s = sel4(first, z4, b2);
             f32x4_t cf = {0.f, 0.f, 0.f, 0.f}, cs = {0.f, 0.f, 0.f, 0.f};
             cf = mfma16(a1h[p], b1f, cf);
             cs = mfma16(a1h[p], b1s, cs);
@@ -241,10 +265,12 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
             }
         }
         __syncthreads();
+        if constexpr (kStride) {
 #pragma unroll
-        for (int p = 0; p < NP; ++p) cw[p] = cn[p];
+            for (int p = 0; p < NP; ++p) cw[p] = cn[p];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) sc[j] = sn[j];
+            for (int j = 0; j < NB; ++j) sc[j] = sn[j];
+        }
     }
 
     if constexpr (EPI == EPI_LOGITS) {
