@@ -76,6 +76,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
     constexpr int NP = NB / 2;        // 64-column block pairs per wave
     __shared__ float red[KW][4][64];  // per wave: C[4*(l/16)+r][l%16] of lane l at [r][l]
     __shared__ float s_inv[kMaxSeq];
+    __shared__ __attribute__((aligned(16))) float s_gw[EPI == EPI_RESID ? 1 : KW][NB * 32];  // norm weight slices
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
     const uint4 z4 = make_uint4(0, 0, 0, 0);
     constexpr int kSsqPer = 1024 / 16 / 16;  // RMSNorm inputs have K = 1024: 64 tile sums, 4 per thread
     uint4 a1h[NP], a1l[NP], a2h[NP], a2l[NP];
-    if (a.norm_w) {
+    if (EPI != EPI_RESID && a.norm_w) {
         // RMSNorm input ([P1] section 2 items 1 and 6): w * (x * inv) with inv = 1 / sqrt(mean(x^2) + eps) of
         // the sequence, from the per-16-row sums of squares (tile order, then a fixed 16-lane tree); the
         // residual stream itself may exceed the f16 range, the normalised operand does not
@@ -126,8 +127,13 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
         float ssv[kSsqPer];
         const int ss_s = tid >> 4, ss_p = tid & 15;
 #pragma unroll
-        for (int i = 0; i < kSsqPer; ++i)
-            ssv[i] = tid < 256 && ss_s < S ? a.ssq[(ss_p + 16 * i) * kMaxSeq + ss_s] : 0.f;
+        for (int i = 0; i < kSsqPer; ++i)  // unconditional (in bounds for every thread); absent ones unused
+            ssv[i] = a.ssq[(ss_p + 16 * i) * kMaxSeq + (ss_s & (kMaxSeq - 1))];
+        asm volatile("" ::: "memory");  // keep these loads ahead of the others (loads return in order)
+        // the wave's slice of the norm weight (NB * 32 = 256 floats) is read once, into LDS, instead of by
+        // each of the 16 sequence lanes
+        static_assert(EPI == EPI_RESID || NB * 32 == 4 * 64, "one 16-byte norm weight chunk per lane");
+        const float4 gwl = *(const float4 *)(a.norm_w + kb0 * 32 + 4 * lane);
         float xv[NP][16], gv[NP][16];
         const int xrow = c < S ? c : S - 1;  // lanes of absent sequences read a present row (zeroed below)
 #pragma unroll
@@ -136,21 +142,27 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float4 xx = *(const float4 *)(a.x + (size_t)xrow * a.ldx + k + 4 * i);
-                const float4 gg = *(const float4 *)(a.norm_w + k + 4 * i);
                 xv[p][4 * i] = xx.x; xv[p][4 * i + 1] = xx.y; xv[p][4 * i + 2] = xx.z; xv[p][4 * i + 3] = xx.w;
-                gv[p][4 * i] = gg.x; gv[p][4 * i + 1] = gg.y; gv[p][4 * i + 2] = gg.z; gv[p][4 * i + 3] = gg.w;
             }
         }
         load_tile(t, cw, sc);  // after the activations: they return first and are converted while codes stream
+        *(float4 *)&s_gw[w][4 * lane] = gwl;
         if (tid < 256) {
             float ss = 0.f;
 #pragma unroll
-            for (int i = 0; i < kSsqPer; ++i) ss += ssv[i];
+            for (int i = 0; i < kSsqPer; ++i) ss += ss_s < S ? ssv[i] : 0.f;
             ss = row16_sum(ss);
             if (ss_p == 0) s_inv[ss_s] = 1.0f / sqrtf(ss / (float)K + a.eps);
         }
         __syncthreads();
         const float inv = s_inv[c];
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 gg = *(const float4 *)&s_gw[w][2 * p * 32 + 16 * q + 4 * i];
+                gv[p][4 * i] = gg.x; gv[p][4 * i + 1] = gg.y; gv[p][4 * i + 2] = gg.z; gv[p][4 * i + 3] = gg.w;
+            }
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             f16x8_t h1, l1, h2, l2;
