@@ -38,12 +38,14 @@ __device__ __forceinline__ uint32_t bf16x2_to_h16x2(uint32_t w) {
     return (uint32_t)f32_to_h16(bf16_lo(w)) | ((uint32_t)f32_to_h16(bf16_hi(w)) << 16);
 }
 
-// bf16 pair -> f16 pair in one packed conversion (round toward zero): exact wherever the value is an f16
-// normal number (bf16 carries 8 significant bits, f16 11); below 2^-14 it differs from round-to-nearest by
-// at most 2^-24.
-__device__ __forceinline__ uint32_t bf16x2_to_h16x2_pk(uint32_t w) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(w), bf16_hi(w)));
+// Two f32 -> packed f16 pair, round to nearest even (one packed conversion on gfx950).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_h16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
 }
+// bf16 pair -> f16 pair (round to nearest even; exact wherever the value is an f16 normal number)
+__device__ __forceinline__ uint32_t bf16x2_to_h16x2_pk(uint32_t w) { return pack_h16x2(bf16_lo(w), bf16_hi(w)); }
 
 __global__ void bf16_to_f16_kernel(const uint16_t *in, uint16_t *out, size_t n) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -384,12 +386,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nqb = (a.T + QB - 1) / QB;
-    const int nunits = 2 * nqb * a.HKV;
-    const int j = blockIdx.x;
-    const int rank = j < (nunits + 1) / 2 ? j : nunits - 1 - (j - (nunits + 1) / 2);  // 0 = most work
-    const int half = rank & 1;
-    const int qb = nqb - 1 - (rank >> 1) / a.HKV;
-    const int kvh = (rank >> 1) % a.HKV;
+    // Work unit of this workgroup.  With a multiple of 8 KV heads, the units of a head all run on one XCD
+    // (workgroup j runs on XCD j mod 8), so each XCD's L2 holds only its own heads' K/V; within an XCD the
+    // units go longest first in its first half and shortest first in its second.
+    int half, qb, kvh;
+    {
+        const int j = blockIdx.x;
+        const bool by_xcd = a.HKV % 8 == 0;
+        const int hpg = by_xcd ? a.HKV / 8 : a.HKV;       // heads per group of units
+        const int nunits = 2 * nqb * hpg;                  // units per group
+        const int idx = by_xcd ? j >> 3 : j;
+        const int rank = idx < (nunits + 1) / 2 ? idx : nunits - 1 - (idx - (nunits + 1) / 2);  // 0 = most work
+        half = rank & 1;
+        qb = nqb - 1 - (rank >> 1) / hpg;
+        kvh = (by_xcd ? (j & 7) : 0) + (by_xcd ? 8 : 1) * ((rank >> 1) % hpg);
+        // uniform by construction; keeping them in scalar registers lets the tile loads use a scalar base
+        half = __builtin_amdgcn_readfirstlane(half);
+        qb = __builtin_amdgcn_readfirstlane(qb);
+        kvh = __builtin_amdgcn_readfirstlane(kvh);
+    }
     const int t0 = qb * QB;
     const int hq = kvh * G + wave / WPH;
     const int tq = t0 + (wave % WPH) * 16 + (lane & 15);  // this lane's query (C column)
@@ -409,22 +424,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
     constexpr int KCH = kKT * kHeadDim / 8 / (64 * NW);  // 16-byte K chunks per thread
     uint4 kreg[KCH];
     uint32_t vreg[KPW / 4][4];  // [key batch][key]: dims (2*lane, 2*lane+1) of key KPW*wave + 4*batch + k
-    auto load_tile = [&](int k0) {
+    // Keys past the end read the last key's row (finite; masked out of the scores), so the tile loads are
+    // unconditional and the loop has no branches around them.  Addresses: a tile base (uniform) plus a
+    // 32-bit per-lane offset with the key clamped to the tile's last valid key.
+    auto load_tile = [&](int k0v) {
+        const int k0 = __builtin_amdgcn_readfirstlane(k0v);  // uniform: scalar tile base
+        const int kmax = n_keys - 1 - k0;  // last valid key within the tile
+        const char *kt = (const char *)(kb + (size_t)k0 * kHeadDim);
+        const char *vt = (const char *)(vb + (size_t)k0 * kHeadDim);
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
             const int ch = tid + 64 * NW * c, key = ch >> 4, dc = (ch & 15) * 8;
-            // keys past the end read the last key's row (finite; masked out of the scores), so the tile
-            // loads are unconditional and the loop has no branches around them
-            const int p = min(k0 + key, n_keys - 1);
-            const u32x4_t v = *(const u32x4_t *)(kb + (size_t)p * kHeadDim + dc);
+            const unsigned off = (unsigned)(min(key, kmax) * kHeadDim + dc) * 2u;  // bytes
+            const u32x4_t v = *(const u32x4_t *)(kt + off);
             kreg[c] = make_uint4(v.x, v.y, v.z, v.w);
         }
 #pragma unroll
         for (int bt = 0; bt < KPW / 4; ++bt)
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int p = min(k0 + KPW * wave + 4 * bt + k, n_keys - 1);  // weight 0 past the end
-                vreg[bt][k] = *(const uint32_t *)(vb + (size_t)p * kHeadDim + 2 * lane);
+                const int key = KPW * wave + 4 * bt + k;  // weight 0 past the end
+                const unsigned off = (unsigned)(min(key, kmax) * kHeadDim + 2 * lane) * 2u;
+                vreg[bt][k] = *(const uint32_t *)(vt + off);
             }
     };
     auto store_tile = [&]() {
@@ -510,7 +531,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
         // against 0 then, which gives zero weights instead of inf - inf.
         const float mn = fmaxf(m, tm);
         const float mref = mn == -INFINITY ? 0.f : mn;
-        const float alpha = exp2f(m - mref);
+        const float alpha = __builtin_amdgcn_exp2f(m - mref);  // hardware exp2 (results below 2^-126 flush to 0)
         m = mn;
         l *= alpha;
         if (__any(alpha != 1.0f))  // once the row maxima settle most tiles leave the output unscaled
@@ -523,9 +544,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const int kt0 = 2 * kb2 + (e >> 2), r0 = e & 3;
-                const float p0 = exp2f(sc[kt0][r0] - mref), p1 = exp2f(sc[kt0][r0 + 1] - mref);
+                const float p0 = __builtin_amdgcn_exp2f(sc[kt0][r0] - mref);
+                const float p1 = __builtin_amdgcn_exp2f(sc[kt0][r0 + 1] - mref);
                 l += p0 + p1;
-                pw[kb2][e >> 1] = (uint32_t)f32_to_h16(p0) | ((uint32_t)f32_to_h16(p1) << 16);
+                pw[kb2][e >> 1] = pack_h16x2(p0, p1);
             }
         }
         // O^T += V^T P^T: A = V^T[16 dims][32 keys] with the key set {4*g4 + 0..3, 16 + 4*g4 + 0..3}
