@@ -185,6 +185,7 @@ int32_t plan(const Dims &d, Layout *lay, qw3_sizes_t *sz) {
     L.attn_x = take(c.mul(d.q_dim, 8));
     L.act_x = take(c.mul(d.I, 8));
     L.pf_cnt = take(attn_prefill_counter_bytes(d));
+    L.kv16 = take(attn_prefill_kv16_bytes(d));
     L.state_end = off;
     const uint64_t M = (uint64_t)(d.max_prefill > d.S ? d.max_prefill : d.S);
     L.x = take(c.mul(c.mul(M, d.H), 4));

@@ -31,8 +31,9 @@ struct Layout {
     uint64_t len, status;
     // single-launch decode: epoch tag base and the tagged exchange words (f32 value | tag << 32)
     uint64_t epoch, x_o, x_d, qkv_x, part_x, attn_x, act_x;
-    // prefill attention: arrival counters of the two key-range halves of each (query block, KV head)
-    uint64_t pf_cnt;
+    // prefill attention: arrival counters of the two key-range halves of each (query block, KV head), and
+    // the f16 shadow of a layer's K / V^T
+    uint64_t pf_cnt, kv16;
     // scratch
     uint64_t x, xn16, qkv, q16, attn, attn16, act, act16, part, argpart, logits, tokens, ssq;
     uint64_t opnd_hi, opnd_lo;  // batched Q8 products: f16 operand pair handed from a kernel to the next product

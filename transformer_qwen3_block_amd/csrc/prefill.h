@@ -11,6 +11,8 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
 // Sizes of the prefill attention's arrival counters and partial-state buffer for up to d.max_prefill tokens
 // (zero when the tiled prefill is unavailable).  The counters live in zeroed state memory.
 uint64_t attn_prefill_counter_bytes(const Dims &d);
+// f16 shadow of one layer's K and V^T for the prefill attention (zeroed state memory, reused by every layer)
+uint64_t attn_prefill_kv16_bytes(const Dims &d);
 uint64_t attn_prefill_partial_bytes(const Dims &d);
 
 // Widens n bf16 values to f16 (round to nearest even; exact unless |v| < 2^-14 or |v| > 65504).

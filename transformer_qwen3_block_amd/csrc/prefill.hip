@@ -33,10 +33,6 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4 &a, const uint4 &b, f32x4_
 
 // f32 -> f16 bits, round to nearest even
 __device__ __forceinline__ uint16_t f32_to_h16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
-// bf16 bits -> f16 bits
-__device__ __forceinline__ uint32_t bf16x2_to_h16x2(uint32_t w) {
-    return (uint32_t)f32_to_h16(bf16_lo(w)) | ((uint32_t)f32_to_h16(bf16_hi(w)) << 16);
-}
 
 // Two f32 -> packed f16 pair, round to nearest even (one packed conversion on gfx950).
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -44,8 +40,6 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_h16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
 }
-// bf16 pair -> f16 pair (round to nearest even; exact wherever the value is an f16 normal number)
-__device__ __forceinline__ uint32_t bf16x2_to_h16x2_pk(uint32_t w) { return pack_h16x2(bf16_lo(w), bf16_hi(w)); }
 
 __global__ void bf16_to_f16_kernel(const uint16_t *in, uint16_t *out, size_t n) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -274,6 +268,56 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------------------------------
+// f16 shadow of one layer's K/V for the prefill attention, converted from the bf16 cache after the append:
+// K as [kv head][position][128] and V transposed, [kv head][128][position], with the positions of each
+// 32-key group ordered so that the keys {4g..4g+3, 16+4g..16+4g+3} sit side by side (one 16-byte read gives
+// a lane the eight keys of its P^T fragment).  Positions are padded to a multiple of 64 so every 64-key
+// tile is in bounds; the buffer is zeroed at load, so padding and not-yet-written positions hold finite
+// values (their attention weights are 0).  The values are f16(bf16 cache value), exact in the f16 range.
+// ---------------------------------------------------------------------------------------------------
+__host__ __device__ inline int kv16_stride(int max_ctx) { return (max_ctx + 63) & ~63; }
+__device__ __forceinline__ int vt_perm(int p) {
+    const int kk = p & 31;
+    return (p & ~31) + 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);
+}
+
+// Cache positions [0, n) of every KV head into the shadow, 64 positions per workgroup: K rows are converted
+// in place of their layout, V goes through LDS to be written as 128-byte V^T rows.  Positions past n in the
+// last tile get zero V.
+__global__ __launch_bounds__(256) void kv16_convert_kernel(const uint16_t *kc, const uint16_t *vc, int max_ctx,
+                                                           int n, uint16_t *ks16, uint16_t *vt16) {
+    __shared__ __attribute__((aligned(16))) uint16_t t[kHeadDim][64 + 8];
+    const int p0 = blockIdx.x * 64, hk = blockIdx.y, tid = threadIdx.x;
+    const int ps = kv16_stride(max_ctx);
+    for (int c = tid; c < 64 * kHeadDim / 8; c += 256) {
+        const int key = c >> 4, d8 = (c & 15) * 8, p = p0 + key;
+        uint32_t kw[4] = {0, 0, 0, 0}, vw[4] = {0, 0, 0, 0};
+        if (p < n) {
+            const size_t at = ((size_t)hk * max_ctx + p) * kHeadDim + d8;
+            const uint4 k = *(const uint4 *)(kc + at), v = *(const uint4 *)(vc + at);
+            const uint32_t kr[4] = {k.x, k.y, k.z, k.w}, vr[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kw[e] = pack_h16x2(bf16_lo(kr[e]), bf16_hi(kr[e]));
+                vw[e] = pack_h16x2(bf16_lo(vr[e]), bf16_hi(vr[e]));
+            }
+            *(uint4 *)(ks16 + ((size_t)hk * ps + p) * kHeadDim + d8) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+        }
+        const int pp = vt_perm(key);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            t[d8 + 2 * e][pp] = (uint16_t)(vw[e] & 0xffffu);
+            t[d8 + 2 * e + 1][pp] = (uint16_t)(vw[e] >> 16);
+        }
+    }
+    __syncthreads();
+    for (int c = tid; c < kHeadDim * 64 / 8; c += 256) {
+        const int dim = c >> 3, k8 = (c & 7) * 8;
+        *(uint4 *)(vt16 + ((size_t)hk * kHeadDim + dim) * ps + p0 + k8) = *(const uint4 *)&t[dim][k8];
+    }
+}
+
+// ---------------------------------------------------------------------------------------------------
 // QK-Norm + RoPE of every query/key head of T tokens ([P1] section 2 items 3-4) and the KV append
 // ([P1] section 6): query heads go to q16 (f16, [T][HQ][128], scaled for the attention kernel); keys (normalised, rotated) and values are
 // rounded to bf16 into the cache at positions pos0..pos0+T-1.  One workgroup per token, one wave per head
@@ -333,7 +377,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(const float *qk
 // ---------------------------------------------------------------------------------------------------
 struct AttnPrefillArgs {
     const uint16_t *q16;      // f16 [T][HQ][128], pre-multiplied by log2(e) / sqrt(128)
-    const uint16_t *kc, *vc;  // bf16 cache, head 0 of (seq, layer): [HKV][max_ctx][128]
+    const uint16_t *ks16, *vt16;  // f16 shadow of the layer's K ([HKV][pos][128]) and V^T ([HKV][128][pos])
     int T, pos0, HQ, HKV, max_ctx;
     uint16_t *out16;          // f16 [T][HQ*128]
     unsigned *part;           // [query block][HKV][kPfState][512] f32 bits: state of the first half to finish
@@ -415,62 +459,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
     const int kbeg = half ? hsplit : 0;
     const int kend = half ? n_keys : min(n_keys, hsplit);
     const int g4 = lane >> 4;
-    const size_t head_off = (size_t)kvh * a.max_ctx * kHeadDim;
-    const uint16_t *kb = a.kc + head_off;
-    const uint16_t *vb = a.vc + head_off;
-
-    // Tile loads (registers): K as 16-byte chunks [key][8 dims]; V as 4-byte pairs so that each lane holds
-    // two dims of four consecutive keys and can write V^T rows with 8-byte stores.
-    constexpr int KCH = kKT * kHeadDim / 8 / (64 * NW);  // 16-byte K chunks per thread
-    uint4 kreg[KCH];
-    uint32_t vreg[KPW / 4][4];  // [key batch][key]: dims (2*lane, 2*lane+1) of key KPW*wave + 4*batch + k
-    // Keys past the end read the last key's row (finite; masked out of the scores), so the tile loads are
-    // unconditional and the loop has no branches around them.  Addresses: a tile base (uniform) plus a
-    // 32-bit per-lane offset with the key clamped to the tile's last valid key.
+    // Tiles come from the f16 shadow: the K tile is 64 rows of 256 bytes, the V^T tile 128 rows of 128 bytes
+    // (64 keys already in fragment order), both copied into LDS as 16-byte chunks without conversion.  Rows
+    // past the last key are in bounds (positions padded to 64) and finite; their weights are 0.
+    const int ps = kv16_stride(a.max_ctx);
+    const char *kbase = (const char *)(a.ks16 + (size_t)kvh * ps * kHeadDim);
+    const char *vbase = (const char *)(a.vt16 + (size_t)kvh * kHeadDim * ps);
+    constexpr int KCH = kKT * kHeadDim / 8 / (64 * NW);  // 16-byte chunks per thread (K; V^T the same)
+    uint4 kreg[KCH], vreg[KCH];
     auto load_tile = [&](int k0v) {
         const int k0 = __builtin_amdgcn_readfirstlane(k0v);  // uniform: scalar tile base
-        const int kmax = n_keys - 1 - k0;  // last valid key within the tile
-        const char *kt = (const char *)(kb + (size_t)k0 * kHeadDim);
-        const char *vt = (const char *)(vb + (size_t)k0 * kHeadDim);
+        const char *kt = kbase + (size_t)k0 * kHeadDim * 2;
+        const char *vt = vbase + (size_t)k0 * 2;
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
-            const int ch = tid + 64 * NW * c, key = ch >> 4, dc = (ch & 15) * 8;
-            const unsigned off = (unsigned)(min(key, kmax) * kHeadDim + dc) * 2u;  // bytes
-            const u32x4_t v = *(const u32x4_t *)(kt + off);
-            kreg[c] = make_uint4(v.x, v.y, v.z, v.w);
+            const int ch = tid + 64 * NW * c;
+            const u32x4_t kv = *(const u32x4_t *)(kt + (unsigned)ch * 16u);  // key ch/16, dims 8*(ch%16)..
+            kreg[c] = make_uint4(kv.x, kv.y, kv.z, kv.w);
+            const int dim = ch >> 3, kc8 = (ch & 7) * 8;                   // V^T row dim, keys kc8..kc8+7
+            const u32x4_t vv = *(const u32x4_t *)(vt + ((unsigned)dim * (unsigned)ps + (unsigned)kc8) * 2u);
+            vreg[c] = make_uint4(vv.x, vv.y, vv.z, vv.w);
         }
-#pragma unroll
-        for (int bt = 0; bt < KPW / 4; ++bt)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int key = KPW * wave + 4 * bt + k;  // weight 0 past the end
-                const unsigned off = (unsigned)(min(key, kmax) * kHeadDim + 2 * lane) * 2u;
-                vreg[bt][k] = *(const uint32_t *)(vt + off);
-            }
     };
     auto store_tile = [&]() {
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
             const int ch = tid + 64 * NW * c, key = ch >> 4, dc = (ch & 15) * 8;
-            const uint4 kv = kreg[c];
-            *(uint4 *)(Ks + ((dc >> 6) * kKT + key) * kLdsLd + (dc & 63)) =
-                make_uint4(bf16x2_to_h16x2_pk(kv.x), bf16x2_to_h16x2_pk(kv.y), bf16x2_to_h16x2_pk(kv.z),
-                           bf16x2_to_h16x2_pk(kv.w));
-        }
-#pragma unroll
-        for (int bt = 0; bt < KPW / 4; ++bt) {
-            uint32_t h[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) h[k] = bf16x2_to_h16x2_pk(vreg[bt][k]);
-            // dim 2*lane: low halves of the four keys; dim 2*lane+1: high halves
-            const uint2 lo = make_uint2((h[0] & 0xffffu) | (h[1] << 16), (h[2] & 0xffffu) | (h[3] << 16));
-            const uint2 hi = make_uint2((h[0] >> 16) | (h[1] & 0xffff0000u), (h[2] >> 16) | (h[3] & 0xffff0000u));
-            // Key positions: within each 32-key half, the four-key groups {4g..4g+3} and {16+4g..16+4g+3}
-            // sit side by side, so one 16-byte read gives a lane the eight keys its P^T fragment covers.
-            const int key0 = KPW * wave + 4 * bt, kk = key0 & 31;
-            const int pos = (key0 & 32) + 8 * ((kk & 15) >> 2) + 4 * (kk >> 4);
-            *(uint2 *)(Vt + (2 * lane) * kLdsLd + pos) = lo;
-            *(uint2 *)(Vt + (2 * lane + 1) * kLdsLd + pos) = hi;
+            *(uint4 *)(Ks + ((dc >> 6) * kKT + key) * kLdsLd + (dc & 63)) = kreg[c];
+            const int dim = ch >> 3, kc8 = (ch & 7) * 8;
+            *(uint4 *)(Vt + dim * kLdsLd + kc8) = vreg[c];
         }
     };
 
@@ -651,6 +668,9 @@ uint64_t attn_prefill_counter_bytes(const Dims &d) {
     if (!d.mfma_prefill || !qb) return 0;
     return (uint64_t)((d.max_prefill + qb - 1) / qb) * d.HKV * sizeof(unsigned);
 }
+uint64_t attn_prefill_kv16_bytes(const Dims &d) {
+    return d.mfma_prefill ? 2ull * d.HKV * kv16_stride(d.max_ctx) * kHeadDim * sizeof(uint16_t) : 0;
+}
 uint64_t attn_prefill_partial_bytes(const Dims &d) {
     return attn_prefill_counter_bytes(d) / sizeof(unsigned) * kPfState * 512 * sizeof(unsigned);
 }
@@ -673,6 +693,8 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
     uint16_t *act16 = (uint16_t *)(arena + L.act16);
     const float *rc = (const float *)(arena + L.rope_cos), *rs = (const float *)(arena + L.rope_sin);
     const size_t seq_stride = (size_t)d.L * d.HKV * d.max_ctx * kHeadDim;
+    uint16_t *ks16 = (uint16_t *)(arena + L.kv16);
+    uint16_t *vt16 = ks16 + (size_t)d.HKV * kv16_stride(d.max_ctx) * kHeadDim;
     for (int l = 0; l < d.L; ++l) {
         const uint64_t b = L.layer0 + (uint64_t)l * L.layer_stride;
         const uint16_t *wqkv = (const uint16_t *)(arena + b + L.l_wqkv16);
@@ -697,10 +719,13 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         hipLaunchKernelGGL(qknorm_rope_append_kernel, dim3(T), dim3(256), 0, st, qkv, d.Nqkv, d.HQ,
                            d.HKV, (const float *)(arena + b + L.l_q_norm), (const float *)(arena + b + L.l_k_norm), rc,
                            rs, pos0, d.eps, q16, kc, vc, d.max_ctx);
+        // every cached position of this layer (earlier chunks and the new one) into the f16 shadow
+        hipLaunchKernelGGL(kv16_convert_kernel, dim3((pos0 + T + 63) / 64, d.HKV), dim3(256), 0, st, kc, vc,
+                           d.max_ctx, pos0 + T, ks16, vt16);
         AttnPrefillArgs at{};
         at.q16 = q16;
-        at.kc = kc;
-        at.vc = vc;
+        at.ks16 = ks16;
+        at.vt16 = vt16;
         at.T = T;
         at.pos0 = pos0;
         at.HQ = d.HQ;
