@@ -262,8 +262,9 @@ template <int EPI>
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
     if (g.K % (2 * kBK) || g.N % 128) return hipErrorInvalidValue;
     if (g.M <= 64) return launch_gemm_cfg<64, 32, 4, 1, EPI>(g, st);  // short prompts: weight-streaming bound
-    if (EPI != G_SWIGLU && g.N <= 1024) return launch_gemm_cfg<128, 64, 4, 1, EPI>(g, st);  // narrow outputs
-    if (EPI == G_STORE && ((g.M + 255) / 256) * (g.N / 128) >= 256) return launch_gemm_cfg<256, 128, 4, 2, EPI>(g, st);
+    if (EPI != G_SWIGLU && g.N <= 1024) return launch_gemm_cfg<128, 64, 4, 2, EPI>(g, st);  // narrow outputs
+    if (EPI == G_STORE && g.N % 256 == 0 && ((g.M + 127) / 128) * (g.N / 256) >= 256)
+        return launch_gemm_cfg<128, 256, 4, 4, EPI>(g, st);
     return launch_gemm_cfg<128, 128, 4, 2, EPI>(g, st);
 }
 
