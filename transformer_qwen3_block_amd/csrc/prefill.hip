@@ -47,10 +47,41 @@ __global__ void bf16_to_f16_kernel(const uint16_t *in, uint16_t *out, size_t n) 
 }
 
 // ---------------------------------------------------------------------------------------------------
-// RMSNorm of T rows ([P1] section 2 items 1 and 6), written as f16 MFMA operands.
+// RMSNorm of T rows ([P1] section 2 items 1 and 6), written as f16 MFMA operands.  One wave per row: the
+// row stays in registers (H / 64 values per lane, H a multiple of 256), the sum of squares is a wave
+// reduction, no workgroup barrier.
 // ---------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float *x, int H, const float *w, float eps,
+template <int VPL>  // values per lane (H / 64)
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float *x, int T, const float *w, float eps,
                                                            uint16_t *out) {
+    constexpr int H = 64 * VPL;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (t >= T) return;
+    const float *xr = x + (size_t)t * H;
+    float4 v[VPL / 4];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL / 4; ++i) {
+        v[i] = *(const float4 *)(xr + 256 * i + 4 * lane);
+        ss += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
+    }
+    const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)H + eps);
+#pragma unroll
+    for (int i = 0; i < VPL / 4; ++i) {
+        const int k = 256 * i + 4 * lane;
+        const float4 g = *(const float4 *)(w + k);
+        ushort4 o;
+        o.x = f32_to_h16(g.x * (v[i].x * inv));
+        o.y = f32_to_h16(g.y * (v[i].y * inv));
+        o.z = f32_to_h16(g.z * (v[i].z * inv));
+        o.w = f32_to_h16(g.w * (v[i].w * inv));
+        *(ushort4 *)(out + (size_t)t * H + k) = o;
+    }
+}
+
+// Any H (a multiple of 4): one workgroup per row, workgroup reduction.
+__global__ __launch_bounds__(256) void rmsnorm_rows_any_kernel(const float *x, int H, const float *w, float eps,
+                                                               uint16_t *out) {
     __shared__ float red[4];
     const int t = blockIdx.x, tid = threadIdx.x;
     const float *xr = x + (size_t)t * H;
@@ -73,6 +104,20 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float *x, int H
         o.w = f32_to_h16(g.w * (v.w * inv));
         *(ushort4 *)(out + (size_t)t * H + k) = o;
     }
+}
+
+hipError_t launch_rmsnorm_rows(const float *x, int T, int H, const float *w, float eps, uint16_t *out,
+                               hipStream_t st) {
+    const dim3 grid((T + 3) / 4);
+    switch (H) {
+        case 512: hipLaunchKernelGGL(rmsnorm_rows_kernel<8>, grid, dim3(256), 0, st, x, T, w, eps, out); break;
+        case 1024: hipLaunchKernelGGL(rmsnorm_rows_kernel<16>, grid, dim3(256), 0, st, x, T, w, eps, out); break;
+        case 2048: hipLaunchKernelGGL(rmsnorm_rows_kernel<32>, grid, dim3(256), 0, st, x, T, w, eps, out); break;
+        default:
+            if (H % 4) return hipErrorInvalidValue;
+            hipLaunchKernelGGL(rmsnorm_rows_any_kernel, dim3(T), dim3(256), 0, st, x, H, w, eps, out);
+    }
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -706,8 +751,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         uint16_t *kc = (uint16_t *)(arena + L.kcache) + layer_off;
         uint16_t *vc = (uint16_t *)(arena + L.vcache) + layer_off;
 
-        hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(T), dim3(256), 0, st, x, d.H,
-                           (const float *)(arena + b + L.l_attn_norm), d.eps, xn16);
+        QW3_PF_TRY(launch_rmsnorm_rows(x, T, d.H, (const float *)(arena + b + L.l_attn_norm), d.eps, xn16, st));
         GemmArgs g{};
         g.A = xn16;
         g.W = wqkv;
@@ -744,8 +788,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         g.outf = x;
         g.ldo = d.H;
         QW3_PF_TRY(launch_gemm<G_RESID>(g, st));
-        hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(T), dim3(256), 0, st, x, d.H,
-                           (const float *)(arena + b + L.l_mlp_norm), d.eps, xn16);
+        QW3_PF_TRY(launch_rmsnorm_rows(x, T, d.H, (const float *)(arena + b + L.l_mlp_norm), d.eps, xn16, st));
         g.A = xn16;
         g.W = wgu;
         g.N = 2 * d.I;
