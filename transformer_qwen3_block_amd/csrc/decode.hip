@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a, int KC) {
 #pragma unroll
         for (int j = 0; j < NR; ++j)
 #pragma unroll
-            for (int s = 0; s < SM; ++s) acc[j][s] = wave_sum(acc[j][s]);
+            for (int s = 0; s < SM; ++s) acc[j][s] = wave_sum_fast(acc[j][s]);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int unit = grp * R + r;
