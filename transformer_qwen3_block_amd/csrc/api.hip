@@ -56,7 +56,7 @@ struct Model {
     bool mfma_batched = false;  // Q8 steps of 2..16 sequences run their products on MFMA (gemv_mfma.hip)
     int b1_splits = kMaxSplit / 2;  // batch-1 decode attention context splits (measured best of 16/32/64)
     ~Model() {
-        for (auto &g : graphs) hipGraphExecDestroy(g.exec);
+        for (auto &g : graphs) (void)hipGraphExecDestroy(g.exec);
     }
 };
 
@@ -762,14 +762,14 @@ int32_t qw3_decode_step(uint64_t h, const int32_t *tokens_dev, float *logits_dev
             int32_t rc = ok ? enqueue_decode_step(m, tokens_dev, logits_dev, argmax_dev, st) : QW3_OK;
             if (ok) ok = hipStreamEndCapture(st, &graph) == hipSuccess && rc == QW3_OK;
             if (ok) ok = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess;
-            if (graph) hipGraphDestroy(graph);
+            if (graph) (void)hipGraphDestroy(graph);
             if (!ok) {
                 (void)hipGetLastError();
                 exec = nullptr;
                 m->graphs_enabled = false;  // this stream cannot be captured: stay eager
             } else {
                 if (m->graphs.size() >= 4) {
-                    hipGraphExecDestroy(m->graphs.front().exec);
+                    (void)hipGraphExecDestroy(m->graphs.front().exec);
                     m->graphs.erase(m->graphs.begin());
                 }
                 m->graphs.push_back({tokens_dev, logits_dev, argmax_dev, exec});

@@ -786,6 +786,7 @@ __global__ void commit_kernel(int *len, int n, int add) {
 
 template <int Q8>
 __global__ void dequant_kernel(const void *w, const float *scales, long long total, int cols, float *out) {
+    (void)cols;  // rows are whole 32-blocks (cols % 32 == 0), so element i's block is i / 32
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= total) return;
     if (Q8)

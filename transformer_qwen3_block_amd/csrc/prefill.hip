@@ -470,7 +470,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
     constexpr int NW = 8;         // waves per workgroup
     constexpr int WPH = NW / G;   // waves per query head
     constexpr int QB = 16 * WPH;  // queries per workgroup
-    constexpr int KPW = kKT / NW; // keys of a tile whose V this wave stages
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * kKT * kLdsLd];     // [dim / 64][key][dim % 64]
     __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * kLdsLd];    // [dim][key position]
 
