@@ -100,10 +100,12 @@ __device__ __forceinline__ bool poll(Addr src, int n, uint32_t tag, float *dst, 
 }
 
 // Workgroup-wide agreement after a poll: true when every thread's poll succeeded.
-__device__ __forceinline__ bool all_ok(bool ok, int *s_fail, int *status) {
-    if (!ok) *(volatile int *)s_fail = 1;
+__device__ __forceinline__ bool all_ok(bool ok, int &s_fail, int *status) {
+    // workgroup-scope atomics on the LDS flag (no generic-pointer volatile access, which would wait for every
+    // global memory operation in flight)
+    if (!ok) __hip_atomic_store(&s_fail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     __syncthreads();
-    if (*(volatile int *)s_fail) {
+    if (__hip_atomic_load(&s_fail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) {
         if (threadIdx.x == 0) atomicOr(status, kStatusTimeout);
         return false;
     }
@@ -228,41 +230,44 @@ __device__ __forceinline__ void rms_slice(const float *xs, const float (&w)[CH][
         for (int e = 0; e < E; ++e) xr[c][e] = w[c][e] * (xs[c * 64 * E + lane * E + e] * inv);
 }
 
-// Cached K/V of one 16-position group for this lane (positions 16*gi + 4*i + lane/16, dims (lane%16)*8..+8).
-// Always eight loads: slots of positions at or after `pos` (the new position is written in this launch and
-// taken from LDS) or of groups past the split read position 0 and are replaced before use.
-__device__ __forceinline__ void load_group(const uint16_t *kb, const uint16_t *vb, int gi, int gend, int pos,
+// Cached K/V of one chunk of four 4-position quads for this lane: positions 4*(q0 + i) + lane/16, dims
+// (lane%16)*8..+8.  Always eight loads: slots of quads at or after qe, or of positions at or after `pos` (the new
+// position is written in this launch and taken from LDS), read position 0 and are never used.
+__device__ __forceinline__ void load_chunk(const uint16_t *kb, const uint16_t *vb, int q0, int qe, int pos,
                                            int lane, uint4 (&kr)[4], uint4 (&vr)[4]) {
     const int dsub = (lane & 15) * 8, prow = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int p = 16 * gi + 4 * i + prow;
-        const size_t pc = (gi < gend && p < pos) ? (size_t)p : 0;
+        const int p = 4 * (q0 + i) + prow;
+        const size_t pc = (q0 + i < qe && p < pos) ? (size_t)p : 0;
         kr[i] = load_nt16(kb + pc * kHeadDim + dsub);
         vr[i] = load_nt16(vb + pc * kHeadDim + dsub);
     }
 }
 
-// Online-softmax update with one 16-position group of cached positions ([P1] section 2 item 5; running max m,
-// running sum l, unnormalised accumulator acc; each lane row keeps its own l and acc).
-template <int G>
-__device__ __forceinline__ void attend_group(uint4 (&kr)[4], uint4 (&vr)[4], int gi, int pos, int lane,
+// 2^x on the transcendental unit (one v_exp_f32; exactly 0 at -inf).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online-softmax update with one chunk of cached positions: NQ quads (1..4) starting at quad q0 ([P1] section 2
+// item 5; running max m, running sum l, unnormalised accumulator acc; each lane row keeps its own l and acc).
+// Scores are in log2 units (the scale sl2 carries log2(e)), so every exponential is a single 2^x.
+template <int G, int NQ>
+__device__ __forceinline__ void attend_chunk(uint4 (&kr)[4], uint4 (&vr)[4], int q0, int pos, int lane,
                                              const float (&qr)[G][8], float sl2, float (&m)[G], float (&l)[G],
                                              float (&acc)[G][8]) {
     const int prow = lane >> 4;
-    bool val[4];
+    bool val[NQ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = 16 * gi + 4 * i + prow;
-        val[i] = p < pos;
+    for (int i = 0; i < NQ; ++i) {
+        val[i] = 4 * (q0 + i) + prow < pos;
         if (!val[i]) {  // placeholder slot: keep stale cache bits out of the sums
             kr[i] = make_uint4(0, 0, 0, 0);
             vr[i] = make_uint4(0, 0, 0, 0);
         }
     }
-    float sc[G][4];
+    float sc[G][NQ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NQ; ++i) {
         float kf[8];
         unpack_bf16x8(kr[i], kf);
 #pragma unroll
@@ -274,28 +279,42 @@ __device__ __forceinline__ void attend_group(uint4 (&kr)[4], uint4 (&vr)[4], int
             sc[h][i] = val[i] ? d * sl2 : -INFINITY;
         }
     }
-    float vf[4][8];
+    float vf[NQ][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) unpack_bf16x8(vr[i], vf[i]);
+    for (int i = 0; i < NQ; ++i) unpack_bf16x8(vr[i], vf[i]);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        float tm = fmaxf(fmaxf(sc[h][0], sc[h][1]), fmaxf(sc[h][2], sc[h][3]));  // uniform within a row
+        float tm = sc[h][0];  // uniform within a row
+#pragma unroll
+        for (int i = 1; i < NQ; ++i) tm = fmaxf(tm, sc[h][i]);
         tm = fmaxf(fmaxf(lane_get(tm, 0), lane_get(tm, 16)), fmaxf(lane_get(tm, 32), lane_get(tm, 48)));
         const float mn = fmaxf(m[h], tm);
         if (mn == -INFINITY) continue;  // nothing valid yet in this lane row set
-        const float alpha = expf(m[h] - mn);
+        const float alpha = exp2_hw(m[h] - mn);
         l[h] *= alpha;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
         m[h] = mn;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float p = expf(sc[h][i] - mn);
+        for (int i = 0; i < NQ; ++i) {
+            const float p = exp2_hw(sc[h][i] - mn);
             l[h] += p;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] += p * vf[i][e];
         }
     }
+}
+
+// attend_chunk for a run of nq quads (the same in every lane): full chunks take the four-quad form, the last
+// chunk of a run its own length
+template <int G>
+__device__ __forceinline__ void attend_run(uint4 (&kr)[4], uint4 (&vr)[4], int q0, int nq, int pos, int lane,
+                                           const float (&qr)[G][8], float sl2, float (&m)[G], float (&l)[G],
+                                           float (&acc)[G][8]) {
+    if (nq >= 4) attend_chunk<G, 4>(kr, vr, q0, pos, lane, qr, sl2, m, l, acc);
+    else if (nq == 3) attend_chunk<G, 3>(kr, vr, q0, pos, lane, qr, sl2, m, l, acc);
+    else if (nq == 2) attend_chunk<G, 2>(kr, vr, q0, pos, lane, qr, sl2, m, l, acc);
+    else if (nq == 1) attend_chunk<G, 1>(kr, vr, q0, pos, lane, qr, sl2, m, l, acc);
 }
 
 // Online-softmax update with the new position (key kn, value vn in LDS, already rounded to bf16); lane row 0
@@ -304,18 +323,26 @@ template <int G>
 __device__ __forceinline__ void attend_new(const float *kn, const float *vn, int lane, const float (&qr)[G][8],
                                            float sl2, float (&m)[G], float (&l)[G], float (&acc)[G][8]) {
     const int dsub = (lane & 15) * 8;
-    const bool row0 = lane < 16;
+    // the lane's eight dims of the new key and value, read once (unconditional 16-byte LDS reads)
+    float kf[8], vf[8];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const float4 k4 = *(const float4 *)(kn + dsub + 4 * q), v4 = *(const float4 *)(vn + dsub + 4 * q);
+        kf[4 * q] = k4.x, kf[4 * q + 1] = k4.y, kf[4 * q + 2] = k4.z, kf[4 * q + 3] = k4.w;
+        vf[4 * q] = v4.x, vf[4 * q + 1] = v4.y, vf[4 * q + 2] = v4.z, vf[4 * q + 3] = v4.w;
+    }
+    const float row0 = lane < 16 ? 1.f : 0.f;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         float d = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d += qr[h][e] * kn[dsub + e];
+        for (int e = 0; e < 8; ++e) d += qr[h][e] * kf[e];
         const float sc = row16_sum(d) * sl2;  // every row computes the same full dot product
         const float mn = fmaxf(m[h], sc);
-        const float alpha = expf(m[h] - mn), p = expf(sc - mn);
-        l[h] = l[h] * alpha + (row0 ? p : 0.f);
+        const float alpha = exp2_hw(m[h] - mn), pw = exp2_hw(sc - mn) * row0;
+        l[h] = l[h] * alpha + pw;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] * alpha + (row0 ? p * vn[dsub + e] : 0.f);
+        for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] * alpha + pw * vf[e];
         m[h] = mn;
     }
 }
@@ -334,7 +361,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     __shared__ __attribute__((aligned(16))) float xs[kHid];
     __shared__ __attribute__((aligned(16))) float big[4096];
-    __shared__ float wm[kWaves][G], wl[kWaves][G];
+    __shared__ __attribute__((aligned(16))) float wacc[kWaves * 4 * G * kHeadDim];  // [wave][lane row][G][128]
+    __shared__ float wm[kWaves][G], wl[kWaves][4][G];
     __shared__ int s_fail;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -348,13 +376,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int pos = a.len[0];
     if (tid == 0) s_fail = 0;
 
-    // this workgroup's attention share: KV head g, split sp.  The cached positions [0, pos) form 16-position
-    // groups dealt round-robin to the 4 * SP waves of the head (wave slot ws takes groups ws, ws + 4 SP, ...);
-    // the new position goes to wave slot ngroups mod 4 SP, whose workgroup also appends it to the cache.
+    // this workgroup's attention share: KV head g, split sp.  The cached positions [0, pos) form quads of four;
+    // wave slot ws = 4 sp + wave takes a contiguous run of quads [qa, qe), floor(quads / nslot) of them plus one
+    // for the first quads % nslot slots, so no wave holds more than one quad beyond the others.  The runs are
+    // processed four quads (16 positions) at a time.  The new position goes to the last slot, which never holds
+    // an extra quad, and its workgroup appends it to the cache.
     const int g = b % HKV, sp = b / HKV;
-    const int nslot = kWaves * SP, ws = sp * kWaves + wave;
-    const int ngroups = (pos + 15) / 16;
-    const int ws_new = ngroups % nslot;
+    const int nslot = kWaves * SP, ws = __builtin_amdgcn_readfirstlane(sp * kWaves + wave);
+    const int nquad = (pos + 3) / 4, qbase = nquad / nslot, qextra = nquad % nslot;
+    const int qa = ws * qbase + min(ws, qextra), qe = qa + qbase + (ws < qextra ? 1 : 0);
+    const int ws_new = nslot - 1;
     const size_t kv_head_off = (size_t)g * a.max_ctx * kHeadDim;
 
     auto lblock = [&](int l) { return a.layer0 + (size_t)l * a.layer_stride; };
@@ -393,7 +424,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float su[2 * RU_MAX][CH];
     uint4 wd[1][KD_MAX];
     float sd[1][KD_MAX];
-    uint4 kA[4], vA[4];
+    uint4 kA[4], vA[4], kB[4], vB[4];  // cached K/V of the wave's first two chunks
     float nq[CH][E], nu[CH][E];  // RMSNorm weight slices of the Q and U phases
     float qkn[4], rcs[2];        // QK-Norm weights (q: lane, lane + 64; k: same) and this position's cos/sin
 
@@ -418,9 +449,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float x_own = xs[gw];  // residual stream of the owned row
 
     const int dsub = (lane & 15) * 8;
-    // score scale f32(1/sqrt(128)) applied to the finished dot product, natural-exponent softmax with the
-    // full-precision expf: the same rounding points as the sequential definition
-    const float sl2 = 1.0f / sqrtf((float)kHeadDim);
+    // score scale 1/sqrt(128) applied to the finished dot product, in log2 units: exp(s - m) = 2^(s' - m')
+    // with s' = s * log2(e)
+    const float sl2 = (1.0f / sqrtf((float)kHeadDim)) * 1.4426950408889634f;
 
     for (int l = 0; l < a.L; ++l) {
         const uint8_t *lb = lblock(l);
@@ -430,7 +461,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (l > 0) {
             const uint64_t *src = a.xd;
             const bool ok = poll<4>([&](int i) { return src + i; }, kHid, tag(l - 1, 5), xs, a.status);
-            if (!all_ok(ok, &s_fail, a.status)) return;
+            if (!all_ok(ok, s_fail, a.status)) return;
         }
         {
             float xr[CH][E];
@@ -450,7 +481,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             qkn[3] = knw[lane + 64];
             rcs[0] = a.rope_cos[(size_t)pos * (kHeadDim / 2) + lane];
             rcs[1] = a.rope_sin[(size_t)pos * (kHeadDim / 2) + lane];
-            load_group(kb, vb, ws, ngroups, pos, lane, kA, vA);
+            load_chunk(kb, vb, qa, qe, pos, lane, kA, vA);
+            // a second chunk (contexts past 16 positions per wave slot) is in flight before the poll too, so no
+            // wave waits for a load after its inputs arrive
+            if (qa + 4 < qe) load_chunk(kb, vb, qa + 4, qe, pos, lane, kB, vB);
         }
 
         // ================= A: QK-Norm + RoPE + append + attention over this split
@@ -459,7 +493,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             float *qs = big + 768;  // [G][128] normalised, rotated queries
             float *kn = big + 1280; // new key (bf16 value)
             float *vn = big + 1408; // new value (bf16 value)
-            float *wacc = big + 1536;  // [4][G][128]
             const uint64_t *qkv = a.qkv;
             const int hq0 = g * G;
             auto src = [&](int i) {
@@ -469,7 +502,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 return qkv + row;
             };
             const bool ok = poll<3>(src, (G + 2) * kHeadDim, tag(l, 0), raw, a.status);
-            if (!all_ok(ok, &s_fail, a.status)) return;
+            if (!all_ok(ok, s_fail, a.status)) return;
 
             // QK-Norm ([P1] item 3, one 128-weight vector per projection) then RoPE on pairs (i, i + 64) at
             // `pos` (item 4)
@@ -518,41 +551,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
             }
-            // the first group was prefetched; later groups (long contexts) stream one ahead
-            for (int gi = ws; gi < ngroups; gi += nslot) {
-                const bool more = gi + nslot < ngroups;
+            // the first two chunks were prefetched; later chunks (contexts past 32 positions per wave slot)
+            // stream one ahead
+            attend_run<G>(kA, vA, qa, qe - qa, pos, lane, qr, sl2, m, lsum, acc);
+            for (int q0 = qa + 4; q0 < qe; q0 += 4) {
+                const bool more = q0 + 4 < qe;
                 uint4 kN[4], vN[4];
-                if (more) load_group(kb, vb, gi + nslot, ngroups, pos, lane, kN, vN);
-                attend_group<G>(kA, vA, gi, pos, lane, qr, sl2, m, lsum, acc);
+                if (more) load_chunk(kb, vb, q0 + 4, qe, pos, lane, kN, vN);
+                attend_run<G>(kB, vB, q0, qe - q0, pos, lane, qr, sl2, m, lsum, acc);
                 if (!more) break;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    kA[i] = kN[i];
-                    vA[i] = vN[i];
+                    kB[i] = kN[i];
+                    vB[i] = vN[i];
                 }
             }
             if (ws == ws_new) attend_new<G>(kn, vn, lane, qr, sl2, m, lsum, acc);
-            // merge the wave's four position rows (the running max is wave-uniform), then the four waves
+            // the four lane rows of each wave leave their (l, acc) in LDS (the running max is wave-uniform); one
+            // pass then combines the 16 row partials of the workgroup per output dim
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                float lv = lsum[h];
-                lv += __shfl_xor(lv, 16, 64);
-                lv += __shfl_xor(lv, 32, 64);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float av = acc[h][e];
-                    av += __shfl_xor(av, 16, 64);
-                    av += __shfl_xor(av, 32, 64);
-                    acc[h][e] = av;
-                }
-                if (lane < 16) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) wacc[(wave * G + h) * kHeadDim + dsub + e] = acc[h][e];
-                }
-                if (lane == 0) {
-                    wm[wave][h] = m[h];
-                    wl[wave][h] = lv;
-                }
+                float *wp = wacc + ((wave * 4 + (lane >> 4)) * G + h) * kHeadDim + dsub;
+                *(float4 *)wp = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+                *(float4 *)(wp + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+                if ((lane & 15) == 0) wl[wave][lane >> 4][h] = lsum[h];
+                if (lane == 0) wm[wave][h] = m[h];
             }
             __syncthreads();
             uint64_t *pp = a.part + ((size_t)(g * SP + sp) * G) * PW;
@@ -565,9 +588,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 if (M != -INFINITY) {
 #pragma unroll
                     for (int w = 0; w < kWaves; ++w) {
-                        const float f = expf(wm[w][h] - M);
-                        Ls += f * wl[w][h];
-                        O += f * wacc[(w * G + h) * kHeadDim + d];
+                        const float f = exp2_hw(wm[w][h] - M);
+                        float lw = 0.f, ow = 0.f;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            lw += wl[w][r][h];
+                            ow += wacc[((w * 4 + r) * G + h) * kHeadDim + d];
+                        }
+                        Ls += f * lw;
+                        O += f * ow;
                     }
                 }
                 uint64_t *ph = pp + (size_t)h * PW;
@@ -594,22 +623,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 return part + base + (j < 2 ? j : 2 + dc * dpw + (j - 2));
             };
             const bool ok = poll<kMegaBuf / 256>(src, SP * per, tag(l, 1), big, a.status);
-            if (!all_ok(ok, &s_fail, a.status)) return;
-            // exact combination in fixed split order: M = max m_s, o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s
-            for (int e = wave; e < dpw; e += kWaves) {
-                float M = -INFINITY;
-                for (int s = lane; s < SP; s += 64) M = fmaxf(M, big[s * per]);
-                M = wave_max_fast(M);
-                float Ls = 0.f, O = 0.f;
-                for (int s = lane; s < SP; s += 64) {
-                    const float ms = big[s * per];
-                    const float f = ms == -INFINITY ? 0.f : expf(ms - M);
-                    Ls += f * big[s * per + 1];
-                    O += f * big[s * per + 2 + e];
+            if (!all_ok(ok, s_fail, a.status)) return;
+            // exact combination (split order fixed by the reduction tree): M = max m_s,
+            // o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, scores in log2 units
+            if (SP <= 32 && dpw == 2 * kWaves) {
+                // one pass: each half wave takes one dim, lane s of the half takes split s
+                const int e = 2 * wave + (lane >> 5), s = lane & 31;
+                const bool v = s < SP;
+                const float ms = v ? big[s * per] : -INFINITY;
+                const float ls = v ? big[s * per + 1] : 0.f, os = v ? big[s * per + 2 + e] : 0.f;
+                const bool hi = lane >= 32;
+                float r = row16_max(ms);
+                const float M = hi ? fmaxf(lane_get(r, 32), lane_get(r, 48)) : fmaxf(lane_get(r, 0), lane_get(r, 16));
+                const float f = ms == -INFINITY ? 0.f : exp2_hw(ms - M);
+                const float rl = row16_sum(f * ls), ro = row16_sum(f * os);
+                const float Ls = hi ? lane_get(rl, 32) + lane_get(rl, 48) : lane_get(rl, 0) + lane_get(rl, 16);
+                const float O = hi ? lane_get(ro, 32) + lane_get(ro, 48) : lane_get(ro, 0) + lane_get(ro, 16);
+                if ((lane & 31) == 0) put(a.attn + h * kHeadDim + dc * dpw + e, O / Ls, tag(l, 2));
+            } else {
+                for (int e = wave; e < dpw; e += kWaves) {
+                    float M = -INFINITY;
+                    for (int s = lane; s < SP; s += 64) M = fmaxf(M, big[s * per]);
+                    M = wave_max_fast(M);
+                    float Ls = 0.f, O = 0.f;
+                    for (int s = lane; s < SP; s += 64) {
+                        const float ms = big[s * per];
+                        const float f = ms == -INFINITY ? 0.f : exp2_hw(ms - M);
+                        Ls += f * big[s * per + 1];
+                        O += f * big[s * per + 2 + e];
+                    }
+                    Ls = wave_sum_fast(Ls);
+                    O = wave_sum_fast(O);
+                    if (lane == 0) put(a.attn + h * kHeadDim + dc * dpw + e, O / Ls, tag(l, 2));
                 }
-                Ls = wave_sum_fast(Ls);
-                O = wave_sum_fast(O);
-                if (lane == 0) put(a.attn + h * kHeadDim + dc * dpw + e, O / Ls, tag(l, 2));
             }
         }
         load_rows<Q8, 2 * RU_MAX, CH>(lb + a.wgu, (const float *)(lb + a.sgu), kHid, ru, ruv, CH, lane, wu, su);
@@ -619,7 +665,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         {
             const uint64_t *src = a.attn;
             const bool ok = poll<8>([&](int i) { return src + i; }, q_dim, tag(l, 2), big, a.status);
-            if (!all_ok(ok, &s_fail, a.status)) return;
+            if (!all_ok(ok, s_fail, a.status)) return;
             const float d = wave_sum_fast(dot_lds<Q8, KO_MAX>(wo[0], so[0], big, KO, lane));
             x_own = x_own + d;
             if (lane == 0) put(a.xo + gw, x_own, tag(l, 3));
@@ -630,7 +676,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         {
             const uint64_t *src = a.xo;
             const bool ok = poll<4>([&](int i) { return src + i; }, kHid, tag(l, 3), xs, a.status);
-            if (!all_ok(ok, &s_fail, a.status)) return;
+            if (!all_ok(ok, s_fail, a.status)) return;
             float xr[CH][E];
             rms_slice<Q8, CH>(xs, nu, a.eps, lane, xr);
             float av[RU_MAX];
@@ -656,7 +702,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         {
             const uint64_t *src = a.act;
             const bool ok = poll<kMegaBuf / 256>([&](int i) { return src + i; }, I, tag(l, 4), big, a.status);
-            if (!all_ok(ok, &s_fail, a.status)) return;
+            if (!all_ok(ok, s_fail, a.status)) return;
             const float d = wave_sum_fast(dot_lds<Q8, KD_MAX>(wd[0], sd[0], big, KD, lane));
             x_own = x_own + d;
             if (lane == 0) {
