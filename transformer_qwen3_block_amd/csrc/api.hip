@@ -178,12 +178,12 @@ int32_t plan(const Dims &d, Layout *lay, qw3_sizes_t *sz) {
     L.status = take(4);
     // single-launch decode: epoch word and tagged exchange words (8 bytes each), zeroed at load
     L.epoch = take(4);
-    L.x_o = take(c.mul(d.H, 8));
-    L.x_d = take(c.mul(d.H, 8));
-    L.qkv_x = take(c.mul(d.Nqkv, 8));
+    L.x_o = take(c.mul(xw_words(d.H), 8));
+    L.x_d = take(c.mul(xw_words(d.H), 8));
+    L.qkv_x = take(c.mul(d.Nqkv, 8));  // dense: measured faster than the spread lines for these words
     L.part_x = take(c.mul(c.mul((uint64_t)kMegaGrid * d.G, kPartStride), 8));  // one partial per workgroup
-    L.attn_x = take(c.mul(d.q_dim, 8));
-    L.act_x = take(c.mul(d.I, 8));
+    L.attn_x = take(c.mul(xw_words(d.q_dim), 8));
+    L.act_x = take(c.mul(xw_words(d.I), 8));
     L.pf_cnt = take(attn_prefill_counter_bytes(d));
     L.kv16 = take(attn_prefill_kv16_bytes(d));
     L.state_end = off;

@@ -14,6 +14,14 @@ constexpr int kPartStride = 2 + kHeadDim;  // per split partial: running max, ru
 constexpr int kLmMaxBlocks = 16384;    // upper bound on lm_head workgroups (argmax partials)
 constexpr int kMegaGrid = 256;         // resident workgroups of the single-launch decode kernel
 constexpr int kMegaWaves = 4;          // its waves per workgroup
+// The single-launch decode kernel's all-gathered exchange words (hidden rows, attention output, activations)
+// sit 16 to a 128-byte line, with consecutive lines kXwLine words (1 KiB) apart: measured on gfx950, packing
+// those lines densely (each line written from four XCDs and polled by every workgroup) made the layer stack
+// about 4 % slower.  The Q/K/V words, which each workgroup polls only for its own KV head, measured faster
+// dense.
+constexpr int kXwLine = 128;
+__host__ __device__ inline int xw_index(int i) { return (i >> 4) * kXwLine + (i & 15); }  // 32-bit: keeps the poll addressing in 32-bit offsets
+inline uint64_t xw_words(int n) { return (uint64_t)((n + 15) / 16) * kXwLine; }
 
 // Byte offsets of every region inside the caller's arena.  Per-layer weight blocks repeat with a fixed
 // stride, so layer l's block starts at layer0 + l * layer_stride.

@@ -460,7 +460,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // ================= Q: RMSNorm + Q/K/V rows
         if (l > 0) {
             const uint64_t *src = a.xd;
-            const bool ok = poll<4>([&](int i) { return src + i; }, kHid, tag(l - 1, 5), xs, a.status);
+            const bool ok = poll<4>([&](int i) { return src + xw_index(i); }, kHid, tag(l - 1, 5), xs, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
         }
         {
@@ -639,7 +639,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 const float rl = row16_sum(f * ls), ro = row16_sum(f * os);
                 const float Ls = hi ? lane_get(rl, 32) + lane_get(rl, 48) : lane_get(rl, 0) + lane_get(rl, 16);
                 const float O = hi ? lane_get(ro, 32) + lane_get(ro, 48) : lane_get(ro, 0) + lane_get(ro, 16);
-                if ((lane & 31) == 0) put(a.attn + h * kHeadDim + dc * dpw + e, O / Ls, tag(l, 2));
+                if ((lane & 31) == 0) put(a.attn + xw_index(h * kHeadDim + dc * dpw + e), O / Ls, tag(l, 2));
             } else {
                 for (int e = wave; e < dpw; e += kWaves) {
                     float M = -INFINITY;
@@ -654,7 +654,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     }
                     Ls = wave_sum_fast(Ls);
                     O = wave_sum_fast(O);
-                    if (lane == 0) put(a.attn + h * kHeadDim + dc * dpw + e, O / Ls, tag(l, 2));
+                    if (lane == 0) put(a.attn + xw_index(h * kHeadDim + dc * dpw + e), O / Ls, tag(l, 2));
                 }
             }
         }
@@ -664,18 +664,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // ================= O: o_proj + residual on the owned row
         {
             const uint64_t *src = a.attn;
-            const bool ok = poll<8>([&](int i) { return src + i; }, q_dim, tag(l, 2), big, a.status);
+            const bool ok = poll<8>([&](int i) { return src + xw_index(i); }, q_dim, tag(l, 2), big, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
             const float d = wave_sum_fast(dot_lds<Q8, KO_MAX>(wo[0], so[0], big, KO, lane));
             x_own = x_own + d;
-            if (lane == 0) put(a.xo + gw, x_own, tag(l, 3));
+            if (lane == 0) put(a.xo + xw_index(gw), x_own, tag(l, 3));
         }
         load_rows<Q8, 1, KD_MAX>(lb + a.wd, (const float *)(lb + a.sd), I, ro, rov, KD, lane, wd, sd);
 
         // ================= U: RMSNorm + gate/up + SwiGLU
         {
             const uint64_t *src = a.xo;
-            const bool ok = poll<4>([&](int i) { return src + i; }, kHid, tag(l, 3), xs, a.status);
+            const bool ok = poll<4>([&](int i) { return src + xw_index(i); }, kHid, tag(l, 3), xs, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
             float xr[CH][E];
             rms_slice<Q8, CH>(xs, nu, a.eps, lane, xr);
@@ -690,7 +690,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
 #pragma unroll
             for (int j = 0; j < RU_MAX; ++j)
-                if (lane == j && ruv[2 * j]) put(a.act + ru[2 * j], av[j], tag(l, 4));
+                if (lane == j && ruv[2 * j]) put(a.act + xw_index(ru[2 * j]), av[j], tag(l, 4));
         }
         if (l + 1 < a.L) {
             const uint8_t *nb = lblock(l + 1);
@@ -701,13 +701,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // ================= D: down + residual on the owned row
         {
             const uint64_t *src = a.act;
-            const bool ok = poll<kMegaBuf / 256>([&](int i) { return src + i; }, I, tag(l, 4), big, a.status);
+            const bool ok = poll<kMegaBuf / 256>([&](int i) { return src + xw_index(i); }, I, tag(l, 4), big, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
             const float d = wave_sum_fast(dot_lds<Q8, KD_MAX>(wd[0], sd[0], big, KD, lane));
             x_own = x_own + d;
             if (lane == 0) {
                 if (l + 1 < a.L)
-                    put(a.xd + gw, x_own, tag(l, 5));
+                    put(a.xd + xw_index(gw), x_own, tag(l, 5));
                 else
                     a.x_out[gw] = x_own;
             }
