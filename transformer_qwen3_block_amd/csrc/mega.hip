@@ -397,11 +397,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // until the memory queues drain, so it belongs in the wait for the next inputs, not before a computation
     // that others are waiting for (and a poll, waiting for the vector memory counter, also waits for every
     // older load).
+    // With eight KV heads (the attention of KV head g runs on workgroups b = g mod 8, which the dispatcher
+    // places on XCD g), the Q/K/V rows of KV head g and the split merge of its query heads go to the same
+    // workgroups' XCD: measured slightly faster.  Placement only: every exchange stays device-coherent.
+    const bool xcd_local = HKV == 8 && G == 2;
     int rq[RQ_MAX];
     bool rqv[RQ_MAX];
 #pragma unroll
     for (int j = 0; j < RQ_MAX; ++j) {
-        rq[j] = gw + kNW * j;
+        if (xcd_local) {  // the (G + 2) * 128 = 512 rows of KV head b mod 8 over the 128 waves of its XCD
+            const int gx = b & 7, lr = (b >> 3) * kWaves + wave + (kNW / 8) * j;
+            rq[j] = lr < G * kHeadDim ? gx * G * kHeadDim + lr
+                                      : (lr < (G + 1) * kHeadDim ? q_dim + gx * kHeadDim + (lr - G * kHeadDim)
+                                                                 : q_dim + kv_dim + gx * kHeadDim + (lr - (G + 1) * kHeadDim));
+        } else {
+            rq[j] = gw + kNW * j;
+        }
         rqv[j] = rq[j] < Nqkv;
     }
     int ru[2 * RU_MAX];
@@ -613,7 +624,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         {
             const int wph = kMegaGrid / HQ;  // workgroups per query head
             const int dpw = kHeadDim / wph;  // dims per workgroup
-            const int h = b / wph, dc = b % wph;
+            const int h = xcd_local ? (b & 7) * G + (b >> 3) / wph : b / wph;
+            const int dc = xcd_local ? (b >> 3) % wph : b % wph;
             const int gh = h / G, hh = h % G;
             const int per = 2 + dpw;
             const uint64_t *part = a.part;
