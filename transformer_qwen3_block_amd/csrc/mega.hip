@@ -696,8 +696,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int j = 0; j < RU_MAX; ++j) {
                 const float gt = wave_sum_fast(dot_reg<Q8, CH>(wu[2 * j], su[2 * j], xr));
                 const float up = wave_sum_fast(dot_reg<Q8, CH>(wu[2 * j + 1], su[2 * j + 1], xr));
-                // SwiGLU, [P1] section 5: (g * sigmoid(g)) * u with sigmoid(g) = 1 / (1 + exp(-g))
-                const float sig = 1.0f / (1.0f + expf(-gt));
+                // SwiGLU, [P1] section 5: (g * sigmoid(g)) * u with sigmoid(g) = 1 / (1 + exp(-g)), on the
+                // transcendental unit (2^x and reciprocal, each within about 1 ulp)
+                const float sig = __builtin_amdgcn_rcpf(1.0f + exp2_hw(-gt * 1.4426950408889634f));
                 av[j] = (gt * sig) * up;
             }
 #pragma unroll
