@@ -33,6 +33,7 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4 &a, const uint4 &b, f32x4_
 
 // f32 -> f16 bits, round to nearest even
 __device__ __forceinline__ uint16_t f32_to_h16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ float h16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
 // Two f32 -> packed f16 pair, round to nearest even (one packed conversion on gfx950).
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -58,18 +59,19 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float *x, int T
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (t >= T) return;
     const float *xr = x + (size_t)t * H;
-    float4 v[VPL / 4];
+    float4 v[VPL / 4], wg[VPL / 4];  // the row and the norm weights, all loads in flight before the reduction
+#pragma unroll
+    for (int i = 0; i < VPL / 4; ++i) v[i] = *(const float4 *)(xr + 256 * i + 4 * lane);
+#pragma unroll
+    for (int i = 0; i < VPL / 4; ++i) wg[i] = *(const float4 *)(w + 256 * i + 4 * lane);
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < VPL / 4; ++i) {
-        v[i] = *(const float4 *)(xr + 256 * i + 4 * lane);
-        ss += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
-    }
-    const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)H + eps);
+    for (int i = 0; i < VPL / 4; ++i) ss += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
+    const float inv = 1.0f / sqrtf(wave_sum_fast(ss) / (float)H + eps);
 #pragma unroll
     for (int i = 0; i < VPL / 4; ++i) {
         const int k = 256 * i + 4 * lane;
-        const float4 g = *(const float4 *)(w + k);
+        const float4 g = wg[i];
         ushort4 o;
         o.x = f32_to_h16(g.x * (v[i].x * inv));
         o.y = f32_to_h16(g.y * (v[i].y * inv));
@@ -128,11 +130,11 @@ hipError_t launch_rmsnorm_rows(const float *x, int T, int H, const float *w, flo
 // every load has two steps of products to hide behind and each step needs one barrier.  Workgroups are mapped
 // so that the tiles one XCD runs (workgroup b runs on XCD b mod 8) share their column blocks, which keeps
 // their weight rows in that XCD's L2.
-// Epilogues: f32 store, f32 residual add (in place), or SwiGLU into f16: with GLU, each wave's columns are
+// Epilogues: f32 store, f16 store, f32 residual add (in place), or SwiGLU into f16: with GLU, each wave's columns are
 // half gate rows and half the matching up rows (up rows start at W row `up_off`), so gate and up of one
 // output element meet in the same lane.
 // ---------------------------------------------------------------------------------------------------
-enum GemmEpi { G_STORE = 0, G_RESID = 1, G_SWIGLU = 2 };
+enum GemmEpi { G_STORE = 0, G_RESID = 1, G_SWIGLU = 2, G_STORE16 = 3, G_QKNORM = 4 };
 
 struct GemmArgs {
     const uint16_t *A;  // f16 [M][K]
@@ -140,8 +142,14 @@ struct GemmArgs {
     int M, N, K;        // N = columns of C (SwiGLU: 2 x output columns)
     int up_off;         // SwiGLU: first up row of W
     float *outf;        // G_STORE / G_RESID: [M][ldo]
-    uint16_t *out16;    // G_SWIGLU: f16 [M][ldo]
+    uint16_t *out16;    // G_SWIGLU / G_STORE16: f16 [M][ldo]
     int ldo;
+    // G_QKNORM (the Q/K/V projection of a prefill chunk, columns = HQ query, HKV key, HKV value heads of 128):
+    // QK-Norm, RoPE and the KV append straight from the accumulators, as qknorm_rope_append_kernel does
+    const float *q_norm, *k_norm, *rope_cos, *rope_sin;
+    float eps;
+    int HQ, HKV, pos0, max_ctx;
+    uint16_t *q16, *kc, *vc;
 };
 
 constexpr int kBK = 64;
@@ -156,8 +164,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
     constexpr int ACH = BM * kBK / 8 / NT;  // 16-byte chunks per thread per A step
     constexpr int BCH = BN * kBK / 8 / NT;
     static_assert(ACH >= 1 && BCH >= 1 && TM >= 1 && TN >= 1, "tile too small for the wave layout");
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDR];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDR];
+    // one LDS region: the double-buffered A and B staging tiles, reused by the fused Q/K/V epilogue
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDR];
+    uint16_t(*As)[BM * LDR] = reinterpret_cast<uint16_t(*)[BM * LDR]>(smem);
+    uint16_t(*Bs)[BN * LDR] = reinterpret_cast<uint16_t(*)[BN * LDR]>(smem + 2 * BM * LDR);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WN, wn = wave % WN;
@@ -263,6 +273,102 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
 
     // epilogue: lane holds C[4*(lane/16) + r][lane%16] of each 16x16 tile
     const int crow = 4 * (lane >> 4), ccol = lane & 15;
+    if constexpr (EPI == G_QKNORM) {
+        // A head's 128 columns are the 64-column tiles of waves wn and wn ^ 1 (same wm); the per-row sums of
+        // squares and the RoPE partner halves (dims d and d + 64) cross between the two through LDS, 8 rows per
+        // wave at a time; results are staged as a 2-byte tile in LDS and leave in 16-byte chunks.  All of it in
+        // the staging region, free after the K loop (which ends with a barrier).  [P1] section 2 items 3-4 and
+        // the section 6 append: the same steps and rounding points as qknorm_rope_append_kernel, from the f32
+        // accumulators.
+        constexpr int OLD = BN + 8;  // 2-byte elements per staged output row (16-byte padding)
+        static_assert(WTN == 64 && WN % 2 == 0 && BN % 128 == 0 && TM * 16 == WTM, "a head spans two waves' 64 columns");
+        static_assert(BM * OLD * 2 + (WM * WN * (8 * 64 + WTM)) * 4 <= (int)sizeof(smem), "epilogue fits in LDS");
+        uint16_t *otile = smem;                        // [BM][OLD]
+        float *xch = (float *)(smem + BM * OLD);       // [wave][8 rows][64]
+        float *ssq = xch + WM * WN * 8 * 64;           // [wave][WTM]
+        const int partner = wave ^ 1;
+        const int hcol = (n0 + wn * WTN) / kHeadDim;  // this wave's head among the Q/K/V heads
+        const bool is_q = hcol < g.HQ, is_v = hcol >= g.HQ + g.HKV;
+        const int dlo = (wn & 1) * 64;              // the wave's dims within its head
+        float wv[TN];
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj) wv[jj] = is_v ? 1.f : (is_q ? g.q_norm : g.k_norm)[dlo + jj * 16 + ccol];
+        if (!is_v) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float p = 0.f;
+#pragma unroll
+                    for (int jj = 0; jj < TN; ++jj) p += acc[i][jj][r] * acc[i][jj][r];
+                    p = row16_sum(p);  // the 16 lanes of a row group hold the wave's 64 columns
+                    if (ccol == 0) ssq[wave * WTM + i * 16 + crow + r] = p;
+                }
+        }
+        const float qs = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int rh = 0; rh < 2; ++rh) {
+                // this pass: rows crow + 2 rh + q (q = 0, 1) of sub-tile i; its RoPE table entries first
+                float cs[2][TN], sn[2][TN];
+                if (!is_v) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int m = m0 + wm * WTM + i * 16 + crow + 2 * rh + q;
+                        const size_t pr = (size_t)(g.pos0 + (m < g.M ? m : 0)) * 64;
+#pragma unroll
+                        for (int jj = 0; jj < TN; ++jj) {
+                            cs[q][jj] = g.rope_cos[pr + jj * 16 + ccol];
+                            sn[q][jj] = g.rope_sin[pr + jj * 16 + ccol];
+                        }
+                    }
+                }
+                __syncthreads();  // ssq complete (first pass) / the previous pass's exchange has been read
+                float nv[2][TN];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int rl = i * 16 + crow + 2 * rh + q;
+                    const float inv =
+                        is_v ? 1.f
+                             : 1.0f / sqrtf((ssq[wave * WTM + rl] + ssq[partner * WTM + rl]) / (float)kHeadDim + g.eps);
+#pragma unroll
+                    for (int jj = 0; jj < TN; ++jj) {
+                        nv[q][jj] = is_v ? acc[i][jj][2 * rh + q] : wv[jj] * (acc[i][jj][2 * rh + q] * inv);
+                        xch[(wave * 8 + 2 * (lane >> 4) + q) * 64 + jj * 16 + ccol] = nv[q][jj];
+                    }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int orow = wm * WTM + i * 16 + crow + 2 * rh + q;
+#pragma unroll
+                    for (int jj = 0; jj < TN; ++jj) {
+                        float o = nv[q][jj];
+                        if (!is_v) {
+                            const float other = xch[(partner * 8 + 2 * (lane >> 4) + q) * 64 + jj * 16 + ccol];
+                            o = dlo == 0 ? o * cs[q][jj] - other * sn[q][jj] : o * cs[q][jj] + other * sn[q][jj];
+                        }
+                        otile[orow * OLD + wn * WTN + jj * 16 + ccol] = is_q ? f32_to_h16(o * qs) : f32_to_bf16(o);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // the staged tile out in 16-byte chunks: query heads to q16, key and value heads into the cache
+        constexpr int CPR = BN / 8;
+        for (int c = tid; c < BM * CPR; c += NT) {
+            const int row = c / CPR, cc = (c % CPR) * 8, m = m0 + row;
+            if (m >= g.M) continue;
+            const int col = n0 + cc, h = col / kHeadDim, d = col % kHeadDim;
+            uint16_t *dst = h < g.HQ ? g.q16 + ((size_t)m * g.HQ + h) * kHeadDim + d
+                            : h < g.HQ + g.HKV
+                                ? g.kc + ((size_t)(h - g.HQ) * g.max_ctx + g.pos0 + m) * kHeadDim + d
+                                : g.vc + ((size_t)(h - g.HQ - g.HKV) * g.max_ctx + g.pos0 + m) * kHeadDim + d;
+            *(uint4 *)dst = *(const uint4 *)(otile + row * OLD + cc);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -278,6 +384,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
                     const float sig = 1.0f / (1.0f + __expf(-gt));
                     g.out16[(size_t)m * g.ldo + col] = f32_to_h16((gt * sig) * up);
                 }
+            } else if constexpr (EPI == G_STORE16) {
+#pragma unroll
+                for (int jj = 0; jj < TN; ++jj)
+                    g.out16[(size_t)m * g.ldo + n0 + wn * WTN + jj * 16 + ccol] = f32_to_h16(acc[i][jj][r]);
             } else {
 #pragma unroll
                 for (int jj = 0; jj < TN; ++jj) {
@@ -306,11 +416,17 @@ hipError_t launch_gemm_cfg(const GemmArgs &g, hipStream_t st) {
 template <int EPI>
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
     if (g.K % (2 * kBK) || g.N % 128) return hipErrorInvalidValue;
-    if (g.M <= 64) return launch_gemm_cfg<64, 32, 4, 1, EPI>(g, st);  // short prompts: weight-streaming bound
-    if (EPI != G_SWIGLU && g.N <= 1024) return launch_gemm_cfg<128, 64, 4, 2, EPI>(g, st);  // narrow outputs
-    if (EPI == G_STORE && g.N % 256 == 0 && ((g.M + 127) / 128) * (g.N / 256) >= 256)
-        return launch_gemm_cfg<128, 256, 4, 4, EPI>(g, st);
-    return launch_gemm_cfg<128, 128, 4, 2, EPI>(g, st);
+    if constexpr (EPI == G_QKNORM) {  // tiles whose waves hold 64 columns: two waves per 128-column head
+        if (g.M <= 64) return hipErrorInvalidValue;
+        if (g.N % 256 == 0 && ((g.M + 127) / 128) * (g.N / 256) >= 256) return launch_gemm_cfg<128, 256, 4, 4, EPI>(g, st);
+        return launch_gemm_cfg<128, 128, 4, 2, EPI>(g, st);
+    } else {
+        if (g.M <= 64) return launch_gemm_cfg<64, 32, 4, 1, EPI>(g, st);  // short prompts: weight-streaming bound
+        if (EPI != G_SWIGLU && g.N <= 1024) return launch_gemm_cfg<128, 64, 4, 2, EPI>(g, st);  // narrow outputs
+        if ((EPI == G_STORE || EPI == G_STORE16) && g.N % 256 == 0 && ((g.M + 127) / 128) * (g.N / 256) >= 256)
+            return launch_gemm_cfg<128, 256, 4, 4, EPI>(g, st);
+        return launch_gemm_cfg<128, 128, 4, 2, EPI>(g, st);
+    }
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -365,42 +481,61 @@ __global__ __launch_bounds__(256) void kv16_convert_kernel(const uint16_t *kc, c
 
 // ---------------------------------------------------------------------------------------------------
 // QK-Norm + RoPE of every query/key head of T tokens ([P1] section 2 items 3-4) and the KV append
-// ([P1] section 6): query heads go to q16 (f16, [T][HQ][128], scaled for the attention kernel); keys (normalised, rotated) and values are
+// ([P1] section 6), from the f16 Q/K/V projections (the GEMM's f16 epilogue): query heads go to q16 (f16, [T][HQ][128], scaled for the attention kernel); keys (normalised, rotated) and values are
 // rounded to bf16 into the cache at positions pos0..pos0+T-1.  One workgroup per token, one wave per head
 // at a time; lane i holds dims i and i+64, which is exactly a RoPE pair.
 // ---------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void qknorm_rope_append_kernel(const float *qkv, int ldqkv, int HQ, int HKV,
+constexpr int kQkMaxHeadsPerWave = 8;  // query + key heads of a wave whose loads are in flight together
+
+__global__ __launch_bounds__(256) void qknorm_rope_append_kernel(const uint16_t *qkv, int ldqkv, int HQ, int HKV,
                                                                  const float *q_norm, const float *k_norm,
                                                                  const float *rope_cos, const float *rope_sin,
                                                                  int pos0, float eps, uint16_t *q16, uint16_t *kc,
                                                                  uint16_t *vc, int max_ctx) {
     const int t = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int pos = pos0 + t;
-    const float *row = qkv + (size_t)t * ldqkv;
+    const uint16_t *row = qkv + (size_t)t * ldqkv;
     const float c = rope_cos[(size_t)pos * 64 + lane], sn = rope_sin[(size_t)pos * 64 + lane];
-    for (int h = wave; h < HQ + HKV; h += 4) {
-        const bool is_q = h < HQ;
-        const float *src = row + (size_t)h * kHeadDim;  // query heads, then key heads
-        const float v0 = src[lane], v1 = src[lane + 64];
-        const float inv = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) / (float)kHeadDim + eps);
-        const float *w = is_q ? q_norm : k_norm;
-        const float n0 = w[lane] * (v0 * inv), n1 = w[lane + 64] * (v1 * inv);
-        const float r0 = n0 * c - n1 * sn, r1 = n1 * c + n0 * sn;
-        if (is_q) {
-            // queries carry the attention scale in log2 units, 1/sqrt(128) * log2(e), applied before the f16
-            // rounding so the attention kernel's scores come out of the MFMA ready for exp2
-            const float qs = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
-            uint16_t *dst = q16 + ((size_t)t * HQ + h) * kHeadDim;
-            dst[lane] = f32_to_h16(r0 * qs);
-            dst[lane + 64] = f32_to_h16(r1 * qs);
-        } else {
-            const int hk = h - HQ;
-            const size_t at = ((size_t)hk * max_ctx + pos) * kHeadDim;
-            kc[at + lane] = f32_to_bf16(r0);
-            kc[at + lane + 64] = f32_to_bf16(r1);
-            const float *vs = row + (size_t)(HQ + HKV + hk) * kHeadDim;
-            vc[at + lane] = f32_to_bf16(vs[lane]);
-            vc[at + lane + 64] = f32_to_bf16(vs[lane + 64]);
+    const float qw0 = q_norm[lane], qw1 = q_norm[lane + 64], kw0 = k_norm[lane], kw1 = k_norm[lane + 64];
+    // the wave's query and key heads h = wave, wave + 4, ... in groups of kQkMaxHeadsPerWave: every load of a
+    // group (a key head's value row with it) is issued before the first is used, one memory latency per group
+    for (int h0 = wave; h0 < HQ + HKV; h0 += 4 * kQkMaxHeadsPerWave) {
+        uint16_t raw[kQkMaxHeadsPerWave][4];
+#pragma unroll
+        for (int i = 0; i < kQkMaxHeadsPerWave; ++i) {
+            const int h = h0 + 4 * i;
+            const int hh = h < HQ + HKV ? h : 0;
+            const uint16_t *src = row + (size_t)hh * kHeadDim;  // query heads, then key heads
+            const uint16_t *vs = row + (size_t)(HQ + HKV + (hh >= HQ ? hh - HQ : 0)) * kHeadDim;
+            raw[i][0] = src[lane];
+            raw[i][1] = src[lane + 64];
+            raw[i][2] = vs[lane];
+            raw[i][3] = vs[lane + 64];
+        }
+#pragma unroll
+        for (int i = 0; i < kQkMaxHeadsPerWave; ++i) {
+            const int h = h0 + 4 * i;
+            if (h >= HQ + HKV) break;
+            const bool is_q = h < HQ;
+            const float v0 = h16_to_f32(raw[i][0]), v1 = h16_to_f32(raw[i][1]);
+            const float inv = 1.0f / sqrtf(wave_sum_fast(v0 * v0 + v1 * v1) / (float)kHeadDim + eps);
+            const float n0 = (is_q ? qw0 : kw0) * (v0 * inv), n1 = (is_q ? qw1 : kw1) * (v1 * inv);
+            const float r0 = n0 * c - n1 * sn, r1 = n1 * c + n0 * sn;
+            if (is_q) {
+                // queries carry the attention scale in log2 units, 1/sqrt(128) * log2(e), applied before the f16
+                // rounding so the attention kernel's scores come out of the MFMA ready for exp2
+                const float qs = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
+                uint16_t *dst = q16 + ((size_t)t * HQ + h) * kHeadDim;
+                dst[lane] = f32_to_h16(r0 * qs);
+                dst[lane + 64] = f32_to_h16(r1 * qs);
+            } else {
+                const int hk = h - HQ;
+                const size_t at = ((size_t)hk * max_ctx + pos) * kHeadDim;
+                kc[at + lane] = f32_to_bf16(r0);
+                kc[at + lane + 64] = f32_to_bf16(r1);
+                vc[at + lane] = f32_to_bf16(h16_to_f32(raw[i][2]));
+                vc[at + lane + 64] = f32_to_bf16(h16_to_f32(raw[i][3]));
+            }
         }
     }
 }
@@ -732,7 +867,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
     if (!d.mfma_prefill || T < 1 || T > d.max_prefill || pos0 + T > d.max_ctx) return QW3_INVALID_ARGUMENT;
     float *x = (float *)(arena + L.x);
     uint16_t *xn16 = (uint16_t *)(arena + L.xn16);
-    float *qkv = (float *)(arena + L.qkv);
+    uint16_t *qkv16 = (uint16_t *)(arena + L.qkv);  // f16 Q/K/V projections of the prefill (the f32 buffer's space)
     uint16_t *q16 = (uint16_t *)(arena + L.q16);
     uint16_t *attn16 = (uint16_t *)(arena + L.attn16);
     uint16_t *act16 = (uint16_t *)(arena + L.act16);
@@ -757,12 +892,28 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         g.M = T;
         g.N = d.Nqkv;
         g.K = d.H;
-        g.outf = qkv;
+        g.out16 = qkv16;
         g.ldo = d.Nqkv;
-        QW3_PF_TRY(launch_gemm<G_STORE>(g, st));
-        hipLaunchKernelGGL(qknorm_rope_append_kernel, dim3(T), dim3(256), 0, st, qkv, d.Nqkv, d.HQ,
-                           d.HKV, (const float *)(arena + b + L.l_q_norm), (const float *)(arena + b + L.l_k_norm), rc,
-                           rs, pos0, d.eps, q16, kc, vc, d.max_ctx);
+        if (T > 64) {  // QK-Norm, RoPE and the append in the projection's epilogue
+            g.q_norm = (const float *)(arena + b + L.l_q_norm);
+            g.k_norm = (const float *)(arena + b + L.l_k_norm);
+            g.rope_cos = rc;
+            g.rope_sin = rs;
+            g.eps = d.eps;
+            g.HQ = d.HQ;
+            g.HKV = d.HKV;
+            g.pos0 = pos0;
+            g.max_ctx = d.max_ctx;
+            g.q16 = q16;
+            g.kc = kc;
+            g.vc = vc;
+            QW3_PF_TRY(launch_gemm<G_QKNORM>(g, st));
+        } else {
+            QW3_PF_TRY(launch_gemm<G_STORE16>(g, st));
+            hipLaunchKernelGGL(qknorm_rope_append_kernel, dim3(T), dim3(256), 0, st, qkv16, d.Nqkv, d.HQ,
+                               d.HKV, (const float *)(arena + b + L.l_q_norm), (const float *)(arena + b + L.l_k_norm),
+                               rc, rs, pos0, d.eps, q16, kc, vc, d.max_ctx);
+        }
         // every cached position of this layer (earlier chunks and the new one) into the f16 shadow
         hipLaunchKernelGGL(kv16_convert_kernel, dim3((pos0 + T + 63) / 64, d.HKV), dim3(256), 0, st, kc, vc,
                            d.max_ctx, pos0 + T, ks16, vt16);
