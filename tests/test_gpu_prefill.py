@@ -77,6 +77,14 @@ def test_prefill_several_tiles():
     _prefill_vs_oracle(replace(SMALL, max_prefill=48), seed=32, T=130, decode_steps=2)
 
 
+@pytest.mark.parametrize("chunk,T", [(128, 300), (100, 290)])
+def test_prefill_chunks_fused_projection_paths(chunk, T):
+    """Chunked prefill through every projection path: chunks of more than 64 tokens starting on a 64-position
+    boundary (the projection epilogue writes the attention's f16 K/V shadow), or off it (the shadow is
+    converted from the cache afterwards), and a last chunk of 64 tokens or fewer (separate QK-Norm kernel)."""
+    _prefill_vs_oracle(replace(SMALL, max_prefill=chunk), seed=36, T=T, decode_steps=2)
+
+
 @pytest.mark.parametrize("heads", [(8, 8), (8, 2)])
 def test_prefill_gqa_group_sizes(heads):
     shp = replace(SMALL, n_q_heads=heads[0], n_kv_heads=heads[1], n_layers=1)

@@ -150,7 +150,19 @@ struct GemmArgs {
     float eps;
     int HQ, HKV, pos0, max_ctx;
     uint16_t *q16, *kc, *vc;
+    // optional (pos0 a multiple of 64): the attention's f16 shadow of K ([HKV][ps][128]) and V^T ([HKV][128][ps]),
+    // written for the chunk's positions from the same staged tile; null: left to kv16_convert_kernel
+    uint16_t *ks16, *vt16;
+    int ps;
 };
+
+__host__ __device__ inline int kv16_stride(int max_ctx) { return (max_ctx + 63) & ~63; }
+// key slot of position p inside its 32-key group of the V^T shadow (see kv16_convert_kernel)
+__device__ __forceinline__ int vt_perm(int p) {
+    const int kk = p & 31;
+    return (p & ~31) + 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);
+}
+__device__ __forceinline__ uint32_t bf16x2_to_h16x2(uint32_t w) { return pack_h16x2(bf16_lo(w), bf16_hi(w)); }
 
 constexpr int kBK = 64;
 constexpr int kLdsPad = 16;  // 16-bit elements of padding per LDS row (32 bytes: measured fastest of 0, 8, 16, 24, 32)
@@ -365,7 +377,39 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
                             : h < g.HQ + g.HKV
                                 ? g.kc + ((size_t)(h - g.HQ) * g.max_ctx + g.pos0 + m) * kHeadDim + d
                                 : g.vc + ((size_t)(h - g.HQ - g.HKV) * g.max_ctx + g.pos0 + m) * kHeadDim + d;
-            *(uint4 *)dst = *(const uint4 *)(otile + row * OLD + cc);
+            const uint4 v = *(const uint4 *)(otile + row * OLD + cc);
+            *(uint4 *)dst = v;
+            if (g.ks16 && h >= g.HQ && h < g.HQ + g.HKV)  // the key row's f16 shadow (exact: bf16 values in range)
+                *(uint4 *)(g.ks16 + ((size_t)(h - g.HQ) * g.ps + g.pos0 + m) * kHeadDim + d) =
+                    make_uint4(bf16x2_to_h16x2(v.x), bf16x2_to_h16x2(v.y), bf16x2_to_h16x2(v.z), bf16x2_to_h16x2(v.w));
+        }
+        // V^T shadow of the tile's value heads: 16-byte chunks of 8 key slots of a 32-position group (the
+        // tile's rows start at a multiple of 64 positions); rows past the chunk's last position up to the next
+        // multiple of 64 get zero, so every attention tile holds finite values
+        if (g.ks16 && (n0 + BN) / kHeadDim > g.HQ + g.HKV) {
+            const int vrows = min(BM, ((g.M - m0) + 63) & ~63);  // rows of this tile the shadow covers
+            constexpr int HPT = BN / kHeadDim;                   // heads per tile
+            const int nch = HPT * kHeadDim * (vrows / 8);        // (head, dim, 8-slot group) chunks
+            for (int c = tid; c < nch; c += NT) {
+                const int hl = c / (kHeadDim * (vrows / 8)), rem = c % (kHeadDim * (vrows / 8));
+                const int h = n0 / kHeadDim + hl;
+                if (h < g.HQ + g.HKV) continue;  // query / key head of a mixed tile
+                const int dim = rem / (vrows / 8), sg = rem % (vrows / 8);  // slots 8 sg .. 8 sg + 7 of the tile
+                uint32_t pk[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float f2[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int s8 = 8 * (sg & 3) + 2 * e + u;  // slot within the 32-group
+                        const int row = 32 * (sg >> 2) + 16 * ((s8 >> 2) & 1) + 4 * (s8 >> 3) + (s8 & 3);
+                        f2[u] = m0 + row < g.M ? bf16_to_f32(otile[row * OLD + hl * kHeadDim + dim]) : 0.f;
+                    }
+                    pk[e] = pack_h16x2(f2[0], f2[1]);
+                }
+                *(uint4 *)(g.vt16 + ((size_t)(h - g.HQ - g.HKV) * kHeadDim + dim) * g.ps + g.pos0 + m0 + 8 * sg) =
+                    make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            }
         }
         return;
     }
@@ -437,11 +481,6 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
 // tile is in bounds; the buffer is zeroed at load, so padding and not-yet-written positions hold finite
 // values (their attention weights are 0).  The values are f16(bf16 cache value), exact in the f16 range.
 // ---------------------------------------------------------------------------------------------------
-__host__ __device__ inline int kv16_stride(int max_ctx) { return (max_ctx + 63) & ~63; }
-__device__ __forceinline__ int vt_perm(int p) {
-    const int kk = p & 31;
-    return (p & ~31) + 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);
-}
 
 // Cache positions [0, n) of every KV head into the shadow, 64 positions per workgroup: K rows are converted
 // in place of their layout, V goes through LDS to be written as 128-byte V^T rows.  Positions past n in the
@@ -894,7 +933,16 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         g.K = d.H;
         g.out16 = qkv16;
         g.ldo = d.Nqkv;
-        if (T > 64) {  // QK-Norm, RoPE and the append in the projection's epilogue
+        // QK-Norm, RoPE and the append in the projection's epilogue (prompts past 64 tokens); with the chunk
+        // starting on a 64-position boundary the epilogue also writes the chunk's part of the f16 K / V^T
+        // shadow, and only the earlier positions are converted from the cache (before, so the epilogue's
+        // writes land last)
+        const bool fused = T > 64;
+        const bool fused_shadow = fused && pos0 % 64 == 0;
+        if (fused_shadow && pos0 > 0)
+            hipLaunchKernelGGL(kv16_convert_kernel, dim3(pos0 / 64, d.HKV), dim3(256), 0, st, kc, vc, d.max_ctx, pos0,
+                               ks16, vt16);
+        if (fused) {
             g.q_norm = (const float *)(arena + b + L.l_q_norm);
             g.k_norm = (const float *)(arena + b + L.l_k_norm);
             g.rope_cos = rc;
@@ -907,6 +955,9 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
             g.q16 = q16;
             g.kc = kc;
             g.vc = vc;
+            g.ks16 = fused_shadow ? ks16 : nullptr;
+            g.vt16 = fused_shadow ? vt16 : nullptr;
+            g.ps = kv16_stride(d.max_ctx);
             QW3_PF_TRY(launch_gemm<G_QKNORM>(g, st));
         } else {
             QW3_PF_TRY(launch_gemm<G_STORE16>(g, st));
@@ -915,8 +966,9 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
                                rc, rs, pos0, d.eps, q16, kc, vc, d.max_ctx);
         }
         // every cached position of this layer (earlier chunks and the new one) into the f16 shadow
-        hipLaunchKernelGGL(kv16_convert_kernel, dim3((pos0 + T + 63) / 64, d.HKV), dim3(256), 0, st, kc, vc,
-                           d.max_ctx, pos0 + T, ks16, vt16);
+        if (!fused_shadow)
+            hipLaunchKernelGGL(kv16_convert_kernel, dim3((pos0 + T + 63) / 64, d.HKV), dim3(256), 0, st, kc, vc,
+                               d.max_ctx, pos0 + T, ks16, vt16);
         AttnPrefillArgs at{};
         at.q16 = q16;
         at.ks16 = ks16;
