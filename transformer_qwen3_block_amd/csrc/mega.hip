@@ -500,10 +500,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
         // ================= A: QK-Norm + RoPE + append + attention over this split
         {
-            float *raw = big;       // [(G + 2) * 128]: q heads, k, v
-            float *qs = big + 768;  // [G][128] normalised, rotated queries
-            float *kn = big + 1280; // new key (bf16 value)
-            float *vn = big + 1408; // new value (bf16 value)
+            float *raw = big;                                // [(G + 2) * 128]: q heads, k, v
+            float *qs = big + 1024 + wave * G * kHeadDim;    // this wave's [G][128] normalised, rotated queries
+            float *kn = big + 3072;                          // new key (bf16 value)
+            float *vn = big + 3200;                          // new value (bf16 value)
             const uint64_t *qkv = a.qkv;
             const int hq0 = g * G;
             auto src = [&](int i) {
@@ -516,38 +516,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (!all_ok(ok, s_fail, a.status)) return;
 
             // QK-Norm ([P1] item 3, one 128-weight vector per projection) then RoPE on pairs (i, i + 64) at
-            // `pos` (item 4)
+            // `pos` (item 4).  Every wave normalises the G query heads into LDS rows of its own (read back by the
+            // same wave: no workgroup barrier); the key head and the value matter only to the wave of the new
+            // position, which also appends both to the cache ([P1] section 6, rounded to the cache's bf16).
             const float c = rcs[0], s = rcs[1];
-            for (int h = wave; h <= G; h += kWaves) {
+            auto norm_rope = [&](int h, float w0, float w1, float &r0, float &r1) {
                 const float v0 = raw[h * kHeadDim + lane], v1 = raw[h * kHeadDim + lane + 64];
                 const float inv = 1.0f / sqrtf(wave_sum_fast(v0 * v0 + v1 * v1) / (float)kHeadDim + a.eps);
-                const float w0 = h < G ? qkn[0] : qkn[2], w1 = h < G ? qkn[1] : qkn[3];
                 const float n0 = w0 * (v0 * inv), n1 = w1 * (v1 * inv);
-                const float r0 = n0 * c - n1 * s, r1 = n1 * c + n0 * s;
-                if (h < G) {
-                    qs[h * kHeadDim + lane] = r0;
-                    qs[h * kHeadDim + lane + 64] = r1;
-                } else {
-                    // key and value rounded to the cache's bf16 ([P1] section 6 append); the split holding `pos`
-                    // writes them
-                    const uint16_t k0 = f32_to_bf16(r0), k1 = f32_to_bf16(r1);
-                    const uint16_t v0b = f32_to_bf16(raw[(G + 1) * kHeadDim + lane]);
-                    const uint16_t v1b = f32_to_bf16(raw[(G + 1) * kHeadDim + lane + 64]);
-                    kn[lane] = bf16_to_f32(k0);
-                    kn[lane + 64] = bf16_to_f32(k1);
-                    vn[lane] = bf16_to_f32(v0b);
-                    vn[lane + 64] = bf16_to_f32(v1b);
-                    if (sp == ws_new / kWaves) {
-                        uint16_t *kc = (uint16_t *)kb + (size_t)pos * kHeadDim;
-                        uint16_t *vc = (uint16_t *)vb + (size_t)pos * kHeadDim;
-                        kc[lane] = k0;
-                        kc[lane + 64] = k1;
-                        vc[lane] = v0b;
-                        vc[lane + 64] = v1b;
-                    }
-                }
+                r0 = n0 * c - n1 * s;
+                r1 = n1 * c + n0 * s;
+            };
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float r0, r1;
+                norm_rope(h, qkn[0], qkn[1], r0, r1);
+                qs[h * kHeadDim + lane] = r0;
+                qs[h * kHeadDim + lane + 64] = r1;
             }
-            __syncthreads();
+            if (ws == ws_new) {
+                float r0, r1;
+                norm_rope(G, qkn[2], qkn[3], r0, r1);
+                const uint16_t k0 = f32_to_bf16(r0), k1 = f32_to_bf16(r1);
+                const uint16_t v0b = f32_to_bf16(raw[(G + 1) * kHeadDim + lane]);
+                const uint16_t v1b = f32_to_bf16(raw[(G + 1) * kHeadDim + lane + 64]);
+                kn[lane] = bf16_to_f32(k0);
+                kn[lane + 64] = bf16_to_f32(k1);
+                vn[lane] = bf16_to_f32(v0b);
+                vn[lane + 64] = bf16_to_f32(v1b);
+                uint16_t *kc = (uint16_t *)kb + (size_t)pos * kHeadDim;
+                uint16_t *vc = (uint16_t *)vb + (size_t)pos * kHeadDim;
+                kc[lane] = k0;
+                kc[lane + 64] = k1;
+                vc[lane] = v0b;
+                vc[lane + 64] = v1b;
+            }
 
             float qr[G][8];
 #pragma unroll
