@@ -388,13 +388,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
         // multiple of 64 get zero, so every attention tile holds finite values
         if (g.ks16 && (n0 + BN) / kHeadDim > g.HQ + g.HKV) {
             const int vrows = min(BM, ((g.M - m0) + 63) & ~63);  // rows of this tile the shadow covers
-            constexpr int HPT = BN / kHeadDim;                   // heads per tile
-            const int nch = HPT * kHeadDim * (vrows / 8);        // (head, dim, 8-slot group) chunks
-            for (int c = tid; c < nch; c += NT) {
-                const int hl = c / (kHeadDim * (vrows / 8)), rem = c % (kHeadDim * (vrows / 8));
+            constexpr int SG = BM / 8;                           // 8-slot groups per dim of a full tile
+            for (int c = tid; c < (BN / kHeadDim) * kHeadDim * SG; c += NT) {
+                const int hl = c / (kHeadDim * SG), dim = (c / SG) % kHeadDim, sg = c % SG;  // powers of two
                 const int h = n0 / kHeadDim + hl;
-                if (h < g.HQ + g.HKV) continue;  // query / key head of a mixed tile
-                const int dim = rem / (vrows / 8), sg = rem % (vrows / 8);  // slots 8 sg .. 8 sg + 7 of the tile
+                if (h < g.HQ + g.HKV || 8 * sg >= vrows) continue;  // query / key head of a mixed tile, or past the rows
                 uint32_t pk[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
