@@ -613,10 +613,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
                 float d = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) d += qr[h][e] * kf[e];
-                d += __shfl_xor(d, 8, 64);
-                d += __shfl_xor(d, 4, 64);
-                d += __shfl_xor(d, 2, 64);
-                d += __shfl_xor(d, 1, 64);
+                d = row16_sum(d);  // the 16 lanes of a row hold one position's dims (DPP, no LDS round trip)
                 sc[h][i] = val[i] ? d * sl2 : -INFINITY;
             }
         }
@@ -641,18 +638,17 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float tm = fmaxf(fmaxf(sc[h][0], sc[h][1]), fmaxf(sc[h][2], sc[h][3]));
-            tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-            tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+            float tm = fmaxf(fmaxf(sc[h][0], sc[h][1]), fmaxf(sc[h][2], sc[h][3]));  // uniform within a row
+            tm = fmaxf(fmaxf(lane_get(tm, 0), lane_get(tm, 16)), fmaxf(lane_get(tm, 32), lane_get(tm, 48)));
             const float mn = fmaxf(m[h], tm);
-            const float alpha = exp2f(m[h] - mn);
+            const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);  // v_exp_f32 (exactly 0 at -inf)
             l[h] *= alpha;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
             m[h] = mn;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = exp2f(sc[h][i] - mn);
+                const float p = __builtin_amdgcn_exp2f(sc[h][i] - mn);
                 l[h] += p;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[h][e] += p * vf[i][e];
