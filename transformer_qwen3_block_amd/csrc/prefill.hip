@@ -642,8 +642,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
     constexpr int NW = 8;         // waves per workgroup
     constexpr int WPH = NW / G;   // waves per query head
     constexpr int QB = 16 * WPH;  // queries per workgroup
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * kKT * kLdsLd];     // [dim / 64][key][dim % 64]
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * kLdsLd];    // [dim][key position]
+    // two buffers of each tile: the next tile is stored while this one is multiplied (one barrier per tile);
+    // 80 KB per workgroup, two workgroups per compute unit
+    __shared__ __attribute__((aligned(16))) uint16_t KsB[2][2 * kKT * kLdsLd];  // [dim / 64][key][dim % 64]
+    __shared__ __attribute__((aligned(16))) uint16_t VtB[2][kHeadDim * kLdsLd]; // [dim][key position]
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nqb = (a.T + QB - 1) / QB;
@@ -698,7 +700,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
             vreg[c] = make_uint4(vv.x, vv.y, vv.z, vv.w);
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) {
+        uint16_t *Ks = KsB[buf], *Vt = VtB[buf];
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
             const int ch = tid + 64 * NW * c, key = ch >> 4, dc = (ch & 15) * 8;
@@ -722,12 +725,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
     // queries enter already multiplied by log2(e) / sqrt(128) (see qknorm_rope_append_kernel)
     const int qpos_min = a.pos0 + t0 + (wave % WPH) * 16;  // first query position of this wave
 
-    if (kbeg < kend) load_tile(kbeg);
-    for (int k0 = kbeg; k0 < kend; k0 += kKT) {
-        __syncthreads();  // previous tile fully consumed
-        store_tile();
-        __syncthreads();
-        if (k0 + kKT < kend) load_tile(k0 + kKT);  // next tile in flight during this one
+    if (kbeg < kend) {
+        load_tile(kbeg);
+        store_tile(0);
+        if (kbeg + kKT < kend) load_tile(kbeg + kKT);  // the next tile in flight during this one
+    }
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = kbeg; k0 < kend; k0 += kKT, buf ^= 1) {
+        const uint16_t *Ks = KsB[buf], *Vt = VtB[buf];
 
         // S^T tiles: lane holds scores of keys k0 + 16*kt + 4*g4 + r for its query.  Only tiles that reach
         // past the wave's first query or past the last key need the causal / length mask.
@@ -794,6 +800,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
                 o[dt] = mfma16(vf, pb, o[dt]);
             }
         }
+        // the next tile into the other buffer (last read before the previous barrier), the one after it in
+        // flight; the barrier publishes the stores and frees this buffer
+        if (k0 + kKT < kend) {
+            store_tile(buf ^ 1);
+            if (k0 + 2 * kKT < kend) load_tile(k0 + 2 * kKT);
+        }
+        __syncthreads();
     }
 
     // Pair the two halves.  The first to arrive publishes its state and leaves; the second takes it and
@@ -804,7 +817,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
     {
         const size_t unit = (size_t)qb * a.HKV + kvh;
         unsigned *slot = a.part + unit * kPfState * 512 + tid;
-        __shared__ unsigned s_second;
+        unsigned &s_second = *(unsigned *)&KsB[0][0];  // the tile buffers are free after the loop's last barrier
         __syncthreads();
         if (tid == 0) s_second = atomicAdd(a.cnt + unit, 1u) & 1u;
         __syncthreads();
