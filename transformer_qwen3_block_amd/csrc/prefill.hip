@@ -285,6 +285,33 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
 
     // epilogue: lane holds C[4*(lane/16) + r][lane%16] of each 16x16 tile
     const int crow = 4 * (lane >> 4), ccol = lane & 15;
+    if constexpr (EPI == G_RESID && BM * (BN + 4) * 4 <= (int)sizeof(smem)) {
+        // residual add through an LDS copy of the tile (the staging region is free: the K loop ended with a
+        // barrier), so the read-modify-write of x runs in 16-byte chunks covering whole row segments
+        constexpr int CLD = BN + 4;  // floats per staged row
+        float *ct = (float *)smem;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int jj = 0; jj < TN; ++jj)
+                    ct[(wm * WTM + i * 16 + crow + r) * CLD + wn * WTN + jj * 16 + ccol] = acc[i][jj][r];
+        __syncthreads();
+        for (int c = tid; c < BM * (BN / 4); c += NT) {
+            const int row = c / (BN / 4), c4 = (c % (BN / 4)) * 4, m = m0 + row;
+            if (m >= g.M) continue;
+            float4 *px = (float4 *)(g.outf + (size_t)m * g.ldo + n0 + c4);
+            const float4 a4 = *(const float4 *)(ct + row * CLD + c4);
+            float4 x4 = *px;
+            x4.x += a4.x;
+            x4.y += a4.y;
+            x4.z += a4.z;
+            x4.w += a4.w;
+            *px = x4;
+        }
+        return;
+    }
     if constexpr (EPI == G_QKNORM) {
         // A head's 128 columns are the 64-column tiles of waves wn and wn ^ 1 (same wm); the per-row sums of
         // squares and the RoPE partner halves (dims d and d + 64) cross between the two through LDS, 8 rows per
