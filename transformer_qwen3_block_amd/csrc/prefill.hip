@@ -285,6 +285,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
 
     // epilogue: lane holds C[4*(lane/16) + r][lane%16] of each 16x16 tile
     const int crow = 4 * (lane >> 4), ccol = lane & 15;
+    if constexpr (EPI == G_SWIGLU && BM * (BN / 2 + 8) * 2 <= (int)sizeof(smem)) {
+        // SwiGLU, [P1] section 5: (g * sigmoid(g)) * u, staged as an f16 tile in LDS (the staging region is
+        // free after the K loop's last barrier) and written in 16-byte chunks covering whole row segments
+        constexpr int OCW = BN / 2, OLD = OCW + 8;  // output columns of the tile, f16 per staged row
+        uint16_t *ot = smem;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int jj = 0; jj < TN / 2; ++jj) {
+                    const float gt = acc[i][jj][r], up = acc[i][jj + TN / 2][r];
+                    const float sig = 1.0f / (1.0f + __expf(-gt));
+                    ot[(wm * WTM + i * 16 + crow + r) * OLD + wn * (WTN / 2) + jj * 16 + ccol] = f32_to_h16((gt * sig) * up);
+                }
+        __syncthreads();
+        for (int c = tid; c < BM * (OCW / 8); c += NT) {
+            const int row = c / (OCW / 8), c8 = (c % (OCW / 8)) * 8, m = m0 + row;
+            if (m >= g.M) continue;
+            *(uint4 *)(g.out16 + (size_t)m * g.ldo + n0 / 2 + c8) = *(const uint4 *)(ot + row * OLD + c8);
+        }
+        return;
+    }
     if constexpr (EPI == G_RESID && BM * (BN + 4) * 4 <= (int)sizeof(smem)) {
         // residual add through an LDS copy of the tile (the staging region is free: the K loop ended with a
         // barrier), so the read-modify-write of x runs in 16-byte chunks covering whole row segments
