@@ -911,13 +911,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
     }
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    if (tq < a.T) {
+    // the wave's 16 query rows x 128 dims staged in its own slice of the (now free) V^T buffers, then written
+    // as 16-byte chunks, four whole 256-byte rows per store instruction; the same wave writes and reads its
+    // slice, so no workgroup barrier is needed
+    {
+        constexpr int OLD = kHeadDim + 8;  // f16 per staged row
+        static_assert(NW * 16 * OLD * 2 <= (int)sizeof(VtB), "output staging fits in the V^T buffers");
+        uint16_t *ow = &VtB[0][0] + wave * 16 * OLD;
         const float inv = 1.0f / l;
-        uint16_t *orow = a.out16 + (size_t)tq * a.HQ * kHeadDim + hq * kHeadDim;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) orow[16 * dt + 4 * g4 + r] = f32_to_h16(o[dt][r] * inv);
+            for (int r = 0; r < 4; ++r) ow[(lane & 15) * OLD + 16 * dt + 4 * g4 + r] = f32_to_h16(o[dt][r] * inv);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int row = 4 * k + (lane >> 4), c8 = (lane & 15) * 8;
+            const int t = t0 + (wave % WPH) * 16 + row;
+            if (t < a.T)
+                *(uint4 *)(a.out16 + (size_t)t * a.HQ * kHeadDim + hq * kHeadDim + c8) = *(const uint4 *)(ow + row * OLD + c8);
+        }
     }
 }
 
