@@ -52,32 +52,42 @@ __global__ void bf16_to_f16_kernel(const uint16_t *in, uint16_t *out, size_t n) 
 // row stays in registers (H / 64 values per lane, H a multiple of 256), the sum of squares is a wave
 // reduction, no workgroup barrier.
 // ---------------------------------------------------------------------------------------------------
-template <int VPL>  // values per lane (H / 64)
+template <int VPL, int RPW>  // values per lane (H / 64), rows per wave
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float *x, int T, const float *w, float eps,
                                                            uint16_t *out) {
     constexpr int H = 64 * VPL;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (t >= T) return;
-    const float *xr = x + (size_t)t * H;
-    float4 v[VPL / 4], wg[VPL / 4];  // the row and the norm weights, all loads in flight before the reduction
+    const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW, lane = threadIdx.x & 63;
+    if (t0 >= T) return;
+    // the wave's rows and the norm weights, all loads in flight before the first reduction
+    float4 v[RPW][VPL / 4], wg[VPL / 4];
 #pragma unroll
-    for (int i = 0; i < VPL / 4; ++i) v[i] = *(const float4 *)(xr + 256 * i + 4 * lane);
+    for (int q = 0; q < RPW; ++q) {
+        const float *xr = x + (size_t)min(t0 + q, T - 1) * H;
+#pragma unroll
+        for (int i = 0; i < VPL / 4; ++i) v[q][i] = *(const float4 *)(xr + 256 * i + 4 * lane);
+    }
 #pragma unroll
     for (int i = 0; i < VPL / 4; ++i) wg[i] = *(const float4 *)(w + 256 * i + 4 * lane);
-    float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < VPL / 4; ++i) ss += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
-    const float inv = 1.0f / sqrtf(wave_sum_fast(ss) / (float)H + eps);
+    for (int q = 0; q < RPW; ++q) {
+        const int t = t0 + q;
+        if (t >= T) break;
+        float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < VPL / 4; ++i) {
-        const int k = 256 * i + 4 * lane;
-        const float4 g = wg[i];
-        ushort4 o;
-        o.x = f32_to_h16(g.x * (v[i].x * inv));
-        o.y = f32_to_h16(g.y * (v[i].y * inv));
-        o.z = f32_to_h16(g.z * (v[i].z * inv));
-        o.w = f32_to_h16(g.w * (v[i].w * inv));
-        *(ushort4 *)(out + (size_t)t * H + k) = o;
+        for (int i = 0; i < VPL / 4; ++i)
+            ss += (v[q][i].x * v[q][i].x + v[q][i].y * v[q][i].y) + (v[q][i].z * v[q][i].z + v[q][i].w * v[q][i].w);
+        const float inv = 1.0f / sqrtf(wave_sum_fast(ss) / (float)H + eps);
+#pragma unroll
+        for (int i = 0; i < VPL / 4; ++i) {
+            const int k = 256 * i + 4 * lane;
+            const float4 g = wg[i];
+            ushort4 o;
+            o.x = f32_to_h16(g.x * (v[q][i].x * inv));
+            o.y = f32_to_h16(g.y * (v[q][i].y * inv));
+            o.z = f32_to_h16(g.z * (v[q][i].z * inv));
+            o.w = f32_to_h16(g.w * (v[q][i].w * inv));
+            *(ushort4 *)(out + (size_t)t * H + k) = o;
+        }
     }
 }
 
@@ -110,11 +120,12 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_any_kernel(const float *x, i
 
 hipError_t launch_rmsnorm_rows(const float *x, int T, int H, const float *w, float eps, uint16_t *out,
                                hipStream_t st) {
-    const dim3 grid((T + 3) / 4);
+    constexpr int RPW = 2;  // rows per wave: twice the loads in flight per wave
+    const dim3 grid((T + 4 * RPW - 1) / (4 * RPW));
     switch (H) {
-        case 512: hipLaunchKernelGGL(rmsnorm_rows_kernel<8>, grid, dim3(256), 0, st, x, T, w, eps, out); break;
-        case 1024: hipLaunchKernelGGL(rmsnorm_rows_kernel<16>, grid, dim3(256), 0, st, x, T, w, eps, out); break;
-        case 2048: hipLaunchKernelGGL(rmsnorm_rows_kernel<32>, grid, dim3(256), 0, st, x, T, w, eps, out); break;
+        case 512: hipLaunchKernelGGL((rmsnorm_rows_kernel<8, RPW>), grid, dim3(256), 0, st, x, T, w, eps, out); break;
+        case 1024: hipLaunchKernelGGL((rmsnorm_rows_kernel<16, RPW>), grid, dim3(256), 0, st, x, T, w, eps, out); break;
+        case 2048: hipLaunchKernelGGL((rmsnorm_rows_kernel<32, RPW>), grid, dim3(256), 0, st, x, T, w, eps, out); break;
         default:
             if (H % 4) return hipErrorInvalidValue;
             hipLaunchKernelGGL(rmsnorm_rows_any_kernel, dim3(T), dim3(256), 0, st, x, H, w, eps, out);
