@@ -142,6 +142,14 @@ def test_decode_over_prefilled_cache_ragged_context(path):
     _greedy_vs_oracle(shp, seed=25, steps=4, kv_fill_len=333, path=path)
 
 
+def test_decode_uneven_position_split_long_context():
+    """Eight KV heads over 2301 cached positions: 576 four-position quads over 128 wave slots per KV head, so
+    half the slots take five quads (one past a full chunk) and the rest four."""
+    shp = replace(SMALL, fmt=synth.FMT_Q8, n_q_heads=16, n_kv_heads=8, n_layers=1, max_ctx=2400)
+    _say("uneven split", shp)
+    _greedy_vs_oracle(shp, seed=27, steps=3, kv_fill_len=2301, path="mega")
+
+
 def test_decode_batched_sequences():
     shp = replace(SMALL, fmt=synth.FMT_Q8, n_seq=5, max_ctx=200)
     _greedy_vs_oracle(shp, seed=26, steps=3, kv_fill_len=150)
