@@ -40,7 +40,7 @@ class Cfg(ctypes.Structure):
 
 class Mat(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("bf16", ctypes.c_void_p),
-                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("q8_0", ctypes.c_void_p)]
 
 
 class Layer(ctypes.Structure):
@@ -71,16 +71,28 @@ def lib():
                                                    ctypes.c_int32, ctypes.c_int32, _F]),
             "orc_silu": (ctypes.c_float, [ctypes.c_float]),
             "orc_q8_dot": (ctypes.c_float, [_F, _F, _F, ctypes.c_int32]),
+            "orc_q8_0_dot": (ctypes.c_float, [_F, _F, ctypes.c_int32]),
+            "orc_f16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
             "orc_bf16_dot": (ctypes.c_float, [_F, _F, ctypes.c_int32]),
             "orc_dequant_row": (None, [ctypes.POINTER(Mat), ctypes.c_int32, _F]),
             "orc_matvec": (None, [ctypes.POINTER(Mat), _F, _F]),
             "orc_argmax": (ctypes.c_int32, [_F, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
+            "orc_pcg32_seed": (None, [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p]),
+            "orc_pcg32_next": (ctypes.c_uint32, [ctypes.c_void_p]),
+            "orc_pcg32_uniform": (ctypes.c_float, [ctypes.c_uint32]),
+            "orc_sample_prepare": (ctypes.c_int32, [_F, ctypes.c_int32, ctypes.c_float, _F, ctypes.c_int32, _F,
+                                                    ctypes.c_int32, _F, _F]),
+            "orc_sample": (ctypes.c_int32, [_F, ctypes.c_int32, ctypes.c_void_p, _F, ctypes.c_int32, _F,
+                                            ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), _F, _F,
+                                            ctypes.POINTER(ctypes.c_int32)]),
             "orc_set_threads": (None, [ctypes.c_int32]),
             "orc_get_threads": (ctypes.c_int32, []),
             "orc_create": (ctypes.c_void_p, [ctypes.POINTER(Cfg), ctypes.POINTER(Mat), _F, ctypes.POINTER(Layer)]),
             "orc_destroy": (None, [ctypes.c_void_p]),
             "orc_step": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, _F, _F, _F,
                                           ctypes.POINTER(ctypes.c_int32)]),
+            "orc_step_kv": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, _F, _F, _F,
+                                             ctypes.POINTER(ctypes.c_int32), _F, _F]),
             "orc_kv_write": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32, _F, _F]),
             "orc_kv_read": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -163,6 +175,17 @@ def q8_dot(codes, scales, act):
     return np.float32(lib().orc_q8_dot(_p(codes), _p(scales), _p(act), codes.size))
 
 
+def q8_0_dot(blocks, act):
+    """blocks: uint8 [n/32 * 34] (little-endian f16 scale, 32 int8 codes per block)."""
+    blocks = np.ascontiguousarray(blocks, np.uint8)
+    act = f32(act)
+    return np.float32(lib().orc_q8_0_dot(_p(blocks), _p(act), act.size))
+
+
+def f16_to_f32(bits):
+    return np.float32(lib().orc_f16_to_f32(int(bits)))
+
+
 def bf16_dot(w_bits, act):
     w_bits = np.ascontiguousarray(w_bits, np.uint16)
     act = f32(act)
@@ -176,6 +199,60 @@ def argmax(v):
     return rc, idx.value
 
 
+class Pcg32(ctypes.Structure):
+    """PCG32 generator state (state, odd increment) of the sampling contract."""
+    _fields_ = [("state", ctypes.c_uint64), ("inc", ctypes.c_uint64)]
+
+    @classmethod
+    def seeded(cls, seed, stream_id):
+        r = cls()
+        lib().orc_pcg32_seed(seed, stream_id, ctypes.byref(r))
+        return r
+
+    def next(self):
+        return int(lib().orc_pcg32_next(ctypes.byref(self)))
+
+
+def pcg32_uniform(word):
+    return float(lib().orc_pcg32_uniform(int(word)))
+
+
+class SampleParams(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_p", ctypes.c_float), ("repetition_penalty", ctypes.c_float),
+                ("top_k", ctypes.c_int32)]
+
+
+def _i32(a):
+    return np.ascontiguousarray(np.asarray(a if a is not None else [], np.int32))
+
+
+def sample_prepare(logits, penalty=1.0, history=None, forbid=None):
+    """Steps 1-5 of the sampling order: (rc, transformed logits)."""
+    lg = f32(logits)
+    h, fb = _i32(history), _i32(forbid)
+    z = np.empty_like(lg)
+    seen = np.zeros(lg.size, np.uint8)
+    rc = lib().orc_sample_prepare(_p(lg), lg.size, penalty, _p(h) if h.size else None, h.size,
+                                  _p(fb) if fb.size else None, fb.size, _p(z), _p(seen))
+    return rc, z
+
+
+def sample(logits, rng, temperature=1.0, top_k=50, top_p=1.0, penalty=1.0, history=None, forbid=None):
+    """One draw; returns (rc, token, candidate ids in draw order, their final probabilities).  `rng` (Pcg32) is
+    advanced in place (not at temperature 0)."""
+    lg = f32(logits)
+    h, fb = _i32(history), _i32(forbid)
+    prm = SampleParams(temperature, top_p, penalty, top_k)
+    tok = ctypes.c_int32(-1)
+    n = ctypes.c_int32(0)
+    probs = np.empty(lg.size, np.float32)
+    ids = np.empty(lg.size, np.int32)
+    rc = lib().orc_sample(_p(lg), lg.size, ctypes.byref(prm), _p(h) if h.size else None, h.size,
+                          _p(fb) if fb.size else None, fb.size, ctypes.byref(rng) if rng is not None else None,
+                          ctypes.byref(tok), _p(probs), _p(ids), ctypes.byref(n))
+    return rc, tok.value, ids[:n.value].copy(), probs[:n.value].copy()
+
+
 def set_threads(n):
     lib().orc_set_threads(int(n))
 
@@ -185,10 +262,12 @@ def get_threads():
 
 
 def mat_struct(m) -> Mat:
-    """m: synth.Matrix (bf16 bits, or int8 codes + f32 scales)."""
+    """m: synth.Matrix (bf16 bits, int8 codes + f32 scales, or Q8_0 34-byte blocks, which take precedence)."""
+    if getattr(m, "q8_0", None) is not None:
+        return Mat(m.rows, m.cols, None, None, None, _p(m.q8_0))
     if m.is_q8:
-        return Mat(m.rows, m.cols, None, _p(m.codes), _p(m.scales))
-    return Mat(m.rows, m.cols, _p(m.bf16), None, None)
+        return Mat(m.rows, m.cols, None, _p(m.codes), _p(m.scales), None)
+    return Mat(m.rows, m.cols, _p(m.bf16), None, None, None)
 
 
 def dequant_row(m, row):
@@ -251,6 +330,21 @@ class Model:
         rc = lib().orc_step(self.h, seq, int(tok), _p(hin), _p(hout), _p(lg),
                             ctypes.byref(am) if (self.shape.input_mode == 0 and want_argmax) else None)
         return rc, am.value, lg, hout
+
+    def step_forced(self, seq, tok=-1, kv_force=None, hidden_in=None, want_hidden=False):
+        """A step whose appended position takes the given bf16 K/V bits (uint16 [L][2][HKV][D]: K heads then V
+        heads per layer) instead of the oracle's own rounding.  Returns (rc, argmax, logits or None, hidden or
+        None, own) where own holds the oracle's own bf16 K/V bits of that position in the same layout."""
+        s = self.shape
+        hin = f32(hidden_in) if hidden_in is not None else None
+        hout = np.empty(s.hidden, np.float32) if want_hidden else None
+        lg = np.empty(s.vocab, np.float32) if s.input_mode == 0 else None
+        own = np.empty((s.n_layers, 2, s.n_kv_heads, s.head_dim), np.uint16)
+        force = None if kv_force is None else np.ascontiguousarray(kv_force, np.uint16)
+        am = ctypes.c_int32(-1)
+        rc = lib().orc_step_kv(self.h, seq, int(tok), _p(hin), _p(hout), _p(lg),
+                               ctypes.byref(am) if s.input_mode == 0 else None, _p(force), _p(own))
+        return rc, am.value, lg, hout, own
 
     def prefill(self, tokens, seq=0):
         """Token-by-token prefill; returns (rc, argmax, logits) of the last position."""

@@ -185,6 +185,34 @@ float orc_q8_dot(const int8_t *codes, const float *scales, const float *act, int
     return acc;
 }
 
+/* IEEE 754 binary16 -> f32, from the format's definition: sign bit, 5-bit exponent (bias 15), 10-bit
+ * fraction; exponent 0 is a subnormal m * 2^-24, exponent 31 an infinity (m = 0) or a NaN.  Every binary16
+ * value is exactly representable in f32, so no rounding happens. */
+float orc_f16_to_f32(uint16_t h) {
+    const uint32_t sign = h >> 15, e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+    float v;
+    if (e == 0) v = (float)m * 0x1p-24f;
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexpf((float)(1024u + m), (int)e - 25);
+    return sign ? -v : v;
+}
+
+/* Q8_0 dot, [P1] section 3 "The Q8_0 Block Contract" and section 5 "Quantized Tensor Access": a row is a
+ * run of 34-byte blocks; per block the little-endian f16 scale is read and promoted to f32, each signed
+ * 8-bit code is promoted to f32, and acc = acc + act_i * (q_i * scale) runs strictly from index 0 upward. */
+float orc_q8_0_dot(const uint8_t *blocks, const float *act, int32_t n) {
+    float acc = 0.0f;
+    for (int32_t b = 0; b < n / 32; ++b) {
+        const uint8_t *blk = blocks + (size_t)b * 34;
+        const float scale = orc_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+        for (int32_t i = 0; i < 32; ++i) {
+            const float q = (float)(int8_t)blk[2 + i];
+            acc = acc + act[b * 32 + i] * (q * scale);
+        }
+    }
+    return acc;
+}
+
 /* bf16 weight row dot: acc = acc + act_i * w_i in index order, w_i widened exactly. */
 float orc_bf16_dot(const uint16_t *w, const float *act, int32_t n) {
     float acc = 0.0f;
@@ -195,6 +223,14 @@ float orc_bf16_dot(const uint16_t *w, const float *act, int32_t n) {
 /* Dequantized weight: one f32 multiply q * scale for Q8, exact widening for bf16. */
 void orc_dequant_row(const orc_mat_t *m, int32_t row, float *out) {
     size_t base = (size_t)row * (size_t)m->cols;
+    if (m->q8_0) {
+        const uint8_t *blocks = m->q8_0 + (size_t)row * (size_t)(m->cols / 32) * 34;
+        for (int32_t i = 0; i < m->cols; ++i) {
+            const uint8_t *blk = blocks + (size_t)(i / 32) * 34;
+            out[i] = (float)(int8_t)blk[2 + i % 32] * orc_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+        }
+        return;
+    }
     for (int32_t i = 0; i < m->cols; ++i) {
         if (m->bf16)
             out[i] = orc_bf16_to_f32(m->bf16[base + i]);
@@ -206,6 +242,7 @@ void orc_dequant_row(const orc_mat_t *m, int32_t row, float *out) {
 static float row_dot(const orc_mat_t *m, int32_t row, const float *x) {
     size_t base = (size_t)row * (size_t)m->cols;
     if (m->bf16) return orc_bf16_dot(m->bf16 + base, x, m->cols);
+    if (m->q8_0) return orc_q8_0_dot(m->q8_0 + (size_t)row * (size_t)(m->cols / 32) * 34, x, m->cols);
     return orc_q8_dot(m->codes + base, m->scales + (size_t)row * (m->cols / 32), x, m->cols);
 }
 
@@ -225,6 +262,183 @@ int32_t orc_argmax(const float *v, int32_t n, int32_t *idx) {
     }
     *idx = best;
     return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Deterministic sampling                                                                       */
+/* ------------------------------------------------------------------------------------------ */
+
+/* PCG32 as [P4] "Deterministic sampling contract" freezes it: state' = state * 6364136223846793005 + inc
+ * (mod 2^64); output = the 32-bit rotate-right of ((old >> 18) ^ old) >> 27 by old >> 59.  Seeding: state 0,
+ * inc = 2 * stream_id + 1, advance, add the seed, advance. */
+uint32_t orc_pcg32_next(orc_pcg32_t *r) {
+    uint64_t old = r->state;
+    r->state = old * 6364136223846793005ULL + r->inc;
+    uint32_t xs = (uint32_t)(((old >> 18) ^ old) >> 27);
+    uint32_t rot = (uint32_t)(old >> 59);
+    return (xs >> rot) | (xs << ((32u - rot) & 31u));
+}
+
+void orc_pcg32_seed(uint64_t seed, uint64_t stream_id, orc_pcg32_t *r) {
+    r->state = 0;
+    r->inc = (stream_id << 1) | 1u;
+    (void)orc_pcg32_next(r);
+    r->state += seed;
+    (void)orc_pcg32_next(r);
+}
+
+/* The high 24 bits of a word as a uniform in [0, 1): (r >> 8) * 2^-24, exact in f32 ([P4]). */
+float orc_pcg32_uniform(uint32_t word) { return (float)(word >> 8) * (1.0f / 16777216.0f); }
+
+typedef struct {
+    float v;
+    int32_t id;
+} orc_cand_t;
+
+/* descending value, ascending token id on equal values ([P1] section 7 "Tie-Breaking Sort") */
+static int cand_cmp(const void *a, const void *b) {
+    const orc_cand_t *x = (const orc_cand_t *)a, *y = (const orc_cand_t *)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return x->id < y->id ? -1 : (x->id > y->id ? 1 : 0);
+}
+
+/* Steps 1-5 of the sampling order below, into z (vocab floats); seen: vocab zeroed bytes of scratch.  A +inf
+ * value after them is a numerical failure. */
+int32_t orc_sample_prepare(const float *logits, int32_t vocab, float penalty, const int32_t *history,
+                           int32_t n_history, const int32_t *forbid, int32_t n_forbid, float *z, unsigned char *seen) {
+    for (int32_t i = 0; i < vocab; ++i) z[i] = logits[i];
+    for (int32_t j = 0; j < n_forbid; ++j)
+        if (forbid[j] >= 0 && forbid[j] < vocab) z[forbid[j]] = -INFINITY;
+    for (int32_t j = 0; j < n_history; ++j) {
+        int32_t t = history[j];
+        if (t < 0 || t >= vocab || seen[t]) continue;
+        seen[t] = 1;
+        if (z[t] > 0.0f) z[t] = z[t] / penalty;
+        else if (z[t] < 0.0f) z[t] = z[t] * penalty;
+    }
+    for (int32_t i = 0; i < vocab; ++i) {
+        if (isnan(z[i])) z[i] = -INFINITY;
+        if (z[i] == 0.0f) z[i] = 0.0f;
+        if (isinf(z[i]) && z[i] > 0.0f) return ORC_NUMERICAL_FAILURE;
+    }
+    return ORC_OK;
+}
+
+/* One token from a logits vector, following [P4] "Sampling order" (with [P1] section 7):
+ *  1. copy the logits in token order; 2. forbidden tokens -> -inf; 3. repetition penalty on every token
+ *  present in the history (counted once): a positive logit is divided by the penalty, a negative one
+ *  multiplied; 4. NaN -> -inf; 5. -0 -> +0; a +inf logit is a numerical failure ([P1] section 4);
+ *  6. temperature 0: the greatest logit, lowest id on ties, and no draw;
+ *  7. otherwise divide by the temperature; 8. top-k by (value desc, id asc) among the finite logits;
+ *  9. stable probabilities over the survivors (max subtracted, exp, sum in order, divide);
+ *  10. order by (probability desc, id asc); 11. top-p: the shortest prefix whose cumulative probability is
+ *  at least p (at least one token); 12. re-normalise the prefix ([P1] section 7); 13. draw u from the
+ *  generator and take the first token whose cumulative probability exceeds u (the last one if rounding
+ *  leaves every cumulative value at or below u).
+ * Optional outputs: the final candidates' ids and probabilities in draw order, and their count. */
+int32_t orc_sample(const float *logits, int32_t vocab, const orc_sample_params_t *p, const int32_t *history,
+                   int32_t n_history, const int32_t *forbid, int32_t n_forbid, orc_pcg32_t *rng, int32_t *token,
+                   float *probs_out, int32_t *ids_out, int32_t *n_out) {
+    if (!logits || vocab <= 0 || !p || !token || n_history < 0 || n_forbid < 0) return ORC_INVALID_ARGUMENT;
+    if (!(p->repetition_penalty > 0.0f) || isinf(p->repetition_penalty)) return ORC_INVALID_ARGUMENT;
+    if (!(p->temperature >= 0.0f) || isinf(p->temperature)) return ORC_INVALID_ARGUMENT;
+    if (p->temperature > 0.0f && (p->top_k < 1 || !(p->top_p > 0.0f) || !(p->top_p <= 1.0f) || !rng))
+        return ORC_INVALID_ARGUMENT;
+    float *z = (float *)malloc(sizeof(float) * (size_t)vocab);
+    unsigned char *seen = (unsigned char *)calloc((size_t)vocab, 1);
+    orc_cand_t *c = (orc_cand_t *)malloc(sizeof(orc_cand_t) * (size_t)vocab);
+    float *pr = (float *)malloc(sizeof(float) * (size_t)vocab);
+    int32_t rc = ORC_OK;
+    if (!z || !seen || !c || !pr) {
+        rc = ORC_INVALID_ARGUMENT;
+        goto done;
+    }
+    rc = orc_sample_prepare(logits, vocab, p->repetition_penalty, history, n_history, forbid, n_forbid, z, seen);
+    if (rc != ORC_OK) goto done;
+    if (p->temperature == 0.0f) {
+        int32_t best = -1;
+        for (int32_t i = 0; i < vocab; ++i)
+            if (z[i] > -INFINITY && (best < 0 || z[i] > z[best])) best = i;
+        if (best < 0) {
+            rc = ORC_NUMERICAL_FAILURE;
+            goto done;
+        }
+        *token = best;
+        if (ids_out) ids_out[0] = best;
+        if (probs_out) probs_out[0] = 1.0f;
+        if (n_out) *n_out = 1;
+        goto done;
+    }
+    int32_t n = 0;
+    for (int32_t i = 0; i < vocab; ++i) {
+        float v = z[i] / p->temperature;
+        if (isinf(v) && v > 0.0f) { /* a finite logit overflowed by the temperature division */
+            rc = ORC_NUMERICAL_FAILURE;
+            goto done;
+        }
+        if (v > -INFINITY) {
+            c[n].v = v;
+            c[n].id = i;
+            ++n;
+        }
+    }
+    if (n == 0) {
+        rc = ORC_NUMERICAL_FAILURE;
+        goto done;
+    }
+    qsort(c, (size_t)n, sizeof(orc_cand_t), cand_cmp);
+    if (n > p->top_k) n = p->top_k;
+    {
+        const float m = c[0].v;
+        float sum = 0.0f;
+        for (int32_t j = 0; j < n; ++j) {
+            pr[j] = orc_exp(c[j].v - m);
+            sum = sum + pr[j];
+        }
+        for (int32_t j = 0; j < n; ++j) c[j].v = pr[j] / sum;
+    }
+    qsort(c, (size_t)n, sizeof(orc_cand_t), cand_cmp); /* (probability desc, id asc) */
+    int32_t keep = n;
+    {
+        float cum = 0.0f;
+        for (int32_t j = 0; j < n; ++j) {
+            cum = cum + c[j].v;
+            if (cum >= p->top_p) {
+                keep = j + 1;
+                break;
+            }
+        }
+    }
+    {
+        float s2 = 0.0f;
+        for (int32_t j = 0; j < keep; ++j) s2 = s2 + c[j].v;
+        for (int32_t j = 0; j < keep; ++j) c[j].v = c[j].v / s2;
+    }
+    {
+        const float u = orc_pcg32_uniform(orc_pcg32_next(rng));
+        float cum = 0.0f;
+        int32_t pick = keep - 1;
+        for (int32_t j = 0; j < keep; ++j) {
+            cum = cum + c[j].v;
+            if (cum > u) {
+                pick = j;
+                break;
+            }
+        }
+        *token = c[pick].id;
+    }
+    for (int32_t j = 0; j < keep; ++j) {
+        if (ids_out) ids_out[j] = c[j].id;
+        if (probs_out) probs_out[j] = c[j].v;
+    }
+    if (n_out) *n_out = keep;
+done:
+    free(z);
+    free(seen);
+    free(c);
+    free(pr);
+    return rc;
 }
 
 void orc_set_threads(int32_t n) {
@@ -256,6 +470,12 @@ orc_model_t *orc_create(const orc_cfg_t *cfg, const orc_mat_t *embed, const void
                         const orc_layer_t *layers) {
     if (!cfg || cfg->n_q_heads <= 0 || cfg->n_kv_heads <= 0 || cfg->n_q_heads % cfg->n_kv_heads) return NULL;
     if (cfg->head_dim % 2 || cfg->max_ctx <= 0 || cfg->n_seq <= 0) return NULL;
+    if (cfg->fmt != ORC_FMT_BF16 && cfg->fmt != ORC_FMT_Q8 && cfg->fmt != ORC_FMT_Q8_0) return NULL;
+    /* quantized blocks of 32 along every contraction: no tail groups ([P1] section 3, a shape failing the
+     * modulo-32 check is an initialisation fault) */
+    if (cfg->fmt != ORC_FMT_BF16 &&
+        (cfg->hidden % 32 || (cfg->n_q_heads * cfg->head_dim) % 32 || cfg->inter % 32))
+        return NULL;
     orc_model_t *m = (orc_model_t *)calloc(1, sizeof(orc_model_t));
     if (!m) return NULL;
     m->c = *cfg;
@@ -334,7 +554,11 @@ static void load_norm(const void *w, int32_t fmt, int32_t n, float *out) {
 
 /* One decoder layer for one token at position pos, following the step order of [P1] section 5
  * "Transformer Layer Execution Loop" (and section 2 items 1-6). x is updated in place. */
-static int32_t decode_layer(orc_model_t *m, int32_t seq, int32_t l, int32_t pos, float *x) {
+/* force / own: NULL, or this layer's [2][HKV][D] bf16 bits (K heads, then V heads) of the appended position:
+ * `own` receives the oracle's own rounded values, `force` replaces them in the cache (teacher forcing of the
+ * current position; the caller checks that the two differ by rounding only). */
+static int32_t decode_layer(orc_model_t *m, int32_t seq, int32_t l, int32_t pos, float *x, const uint16_t *force,
+                            uint16_t *own) {
     const orc_cfg_t *c = &m->c;
     const orc_layer_t *W = &m->layers[l];
     const int32_t H = c->hidden, D = c->head_dim, HQ = c->n_q_heads, HKV = c->n_kv_heads;
@@ -389,8 +613,18 @@ static int32_t decode_layer(orc_model_t *m, int32_t seq, int32_t l, int32_t pos,
         for (int32_t d = 0; d < D; ++d) {
             size_t at = kv_index(m, seq, l, h, pos) + d;
             float kf = k[(size_t)h * D + d], vf = v[(size_t)h * D + d];
-            m->k_cache[at] = c->kv_f32 ? kf : orc_bf16_to_f32(orc_f32_to_bf16(kf));
-            m->v_cache[at] = c->kv_f32 ? vf : orc_bf16_to_f32(orc_f32_to_bf16(vf));
+            const size_t ki = (size_t)h * D + d, vi = (size_t)HKV * D + ki;
+            if (own) {
+                own[ki] = orc_f32_to_bf16(kf);
+                own[vi] = orc_f32_to_bf16(vf);
+            }
+            if (force) {
+                m->k_cache[at] = orc_bf16_to_f32(force[ki]);
+                m->v_cache[at] = orc_bf16_to_f32(force[vi]);
+            } else {
+                m->k_cache[at] = c->kv_f32 ? kf : orc_bf16_to_f32(orc_f32_to_bf16(kf));
+                m->v_cache[at] = c->kv_f32 ? vf : orc_bf16_to_f32(orc_f32_to_bf16(vf));
+            }
         }
 
     /* 6. grouped-query attention over positions 0..pos of this layer's cache */
@@ -436,8 +670,17 @@ done:
 
 int32_t orc_step(orc_model_t *m, int32_t seq, int32_t tok, const float *hidden_in, float *hidden_out,
                  float *logits, int32_t *argmax) {
+    return orc_step_kv(m, seq, tok, hidden_in, hidden_out, logits, argmax, NULL, NULL);
+}
+
+/* orc_step with the appended position's bf16 K/V taken from kv_force ([L][2][HKV][D] bits) instead of the
+ * oracle's own rounding, which is written to kv_own (same layout) when given.  Only for a bf16 cache. */
+int32_t orc_step_kv(orc_model_t *m, int32_t seq, int32_t tok, const float *hidden_in, float *hidden_out,
+                    float *logits, int32_t *argmax, const uint16_t *kv_force, uint16_t *kv_own) {
     const orc_cfg_t *c = &m->c;
     if (seq < 0 || seq >= c->n_seq) return ORC_INVALID_ARGUMENT;
+    if (kv_force && c->kv_f32) return ORC_INVALID_ARGUMENT;
+    const size_t per_layer = (size_t)2 * c->n_kv_heads * c->head_dim;
     if (c->n_q_heads > 1024) return ORC_UNSUPPORTED_SHAPE;
     int32_t pos = m->len[seq];
     /* a position at or past the admitted context is a typed error; no ring buffering
@@ -460,7 +703,9 @@ int32_t orc_step(orc_model_t *m, int32_t seq, int32_t tok, const float *hidden_i
         }
         orc_dequant_row(&m->embed, tok, x);
     }
-    for (int32_t l = 0; l < c->n_layers && rc == ORC_OK; ++l) rc = decode_layer(m, seq, l, pos, x);
+    for (int32_t l = 0; l < c->n_layers && rc == ORC_OK; ++l)
+        rc = decode_layer(m, seq, l, pos, x, kv_force ? kv_force + (size_t)l * per_layer : NULL,
+                          kv_own ? kv_own + (size_t)l * per_layer : NULL);
     if (rc == ORC_OK && hidden_out) {
         for (int32_t i = 0; i < H; ++i)
             if (!isfinite(x[i])) rc = ORC_NUMERICAL_FAILURE;

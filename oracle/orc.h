@@ -30,10 +30,10 @@ extern "C" {
 
 enum { ORC_OK = 0, ORC_INVALID_ARGUMENT = 1, ORC_UNSUPPORTED_QUANT = 12, ORC_UNSUPPORTED_SHAPE = 13,
        ORC_CONTEXT_EXCEEDED = 14, ORC_NUMERICAL_FAILURE = 18 };
-enum { ORC_FMT_BF16 = 1, ORC_FMT_Q8 = 2 };
+enum { ORC_FMT_BF16 = 1, ORC_FMT_Q8 = 2, ORC_FMT_Q8_0 = 3 };
 
 typedef struct {
-    int32_t fmt;        /* ORC_FMT_BF16 or ORC_FMT_Q8 */
+    int32_t fmt;        /* ORC_FMT_BF16, ORC_FMT_Q8 or ORC_FMT_Q8_0 */
     int32_t input_mode; /* 0: token ids, 1: fp32 hidden vectors (no embedding / final norm / logits) */
     int32_t vocab, hidden, n_layers, n_q_heads, n_kv_heads, head_dim, inter, max_ctx, n_seq;
     int32_t kv_f32;     /* 0: cache holds bf16-rounded K/V (default); 1: cache keeps f32 K/V */
@@ -41,15 +41,17 @@ typedef struct {
     double theta;
 } orc_cfg_t;
 
-/* Canonical [rows, cols] row-major matrix: bf16 bits, or Q8 codes + f32 scale per 32 along cols. */
+/* Canonical [rows, cols] row-major matrix: bf16 bits, or Q8 codes + f32 scale per 32 along cols, or
+ * Q8_0 blocks: per row cols/32 blocks of 34 bytes (little-endian f16 scale, then 32 int8 codes). */
 typedef struct {
     int32_t rows, cols;
     const uint16_t *bf16;
     const int8_t *codes;
     const float *scales;
+    const uint8_t *q8_0;
 } orc_mat_t;
 
-/* Norm weights are bf16 bits when fmt == BF16 and f32 when fmt == Q8. */
+/* Norm weights are bf16 bits when fmt == BF16 and f32 when fmt == Q8 or Q8_0. */
 typedef struct {
     const void *attn_norm, *q_norm, *k_norm, *mlp_norm;
     orc_mat_t q, k, v, o, gate, up, down;
@@ -75,6 +77,27 @@ float orc_bf16_dot(const uint16_t *w, const float *act, int32_t n);
 void orc_dequant_row(const orc_mat_t *m, int32_t row, float *out);
 void orc_matvec(const orc_mat_t *m, const float *x, float *out);
 int32_t orc_argmax(const float *v, int32_t n, int32_t *idx);
+float orc_f16_to_f32(uint16_t h);
+float orc_q8_0_dot(const uint8_t *blocks, const float *act, int32_t n);
+
+/* Deterministic sampling ([P1] section 7; [P4] "Deterministic sampling contract", "Sampling order"). */
+typedef struct {
+    uint64_t state, inc; /* PCG32 state and (odd) increment */
+} orc_pcg32_t;
+void orc_pcg32_seed(uint64_t seed, uint64_t stream_id, orc_pcg32_t *r);
+uint32_t orc_pcg32_next(orc_pcg32_t *r);
+float orc_pcg32_uniform(uint32_t word);
+typedef struct {
+    float temperature;        /* 0: greedy (no draw); else positive and finite */
+    float top_p;              /* (0, 1] */
+    float repetition_penalty; /* positive and finite; 1 leaves the logits unchanged */
+    int32_t top_k;            /* >= 1 */
+} orc_sample_params_t;
+int32_t orc_sample_prepare(const float *logits, int32_t vocab, float penalty, const int32_t *history,
+                           int32_t n_history, const int32_t *forbid, int32_t n_forbid, float *z, unsigned char *seen);
+int32_t orc_sample(const float *logits, int32_t vocab, const orc_sample_params_t *p, const int32_t *history,
+                   int32_t n_history, const int32_t *forbid, int32_t n_forbid, orc_pcg32_t *rng, int32_t *token,
+                   float *probs_out, int32_t *ids_out, int32_t *n_out);
 void orc_set_threads(int32_t n);
 int32_t orc_get_threads(void);
 
@@ -86,6 +109,8 @@ void orc_destroy(orc_model_t *m);
  * and/or logits (vocab f32) and argmax when non-NULL.  KV length advances only on success. */
 int32_t orc_step(orc_model_t *m, int32_t seq, int32_t tok, const float *hidden_in, float *hidden_out,
                  float *logits, int32_t *argmax);
+int32_t orc_step_kv(orc_model_t *m, int32_t seq, int32_t tok, const float *hidden_in, float *hidden_out,
+                    float *logits, int32_t *argmax, const uint16_t *kv_force, uint16_t *kv_own);
 int32_t orc_kv_write(orc_model_t *m, int32_t seq, int32_t layer, int32_t pos0, int32_t n_pos, const uint16_t *k,
                      const uint16_t *v);
 int32_t orc_kv_read(const orc_model_t *m, int32_t seq, int32_t layer, int32_t pos0, int32_t n_pos, uint16_t *k,

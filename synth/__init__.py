@@ -27,6 +27,7 @@ SYN_NORMAL_F32, SYN_NORMAL_BF16, SYN_UNIFORM_F32, SYN_INT8, SYN_INT32 = range(5)
 
 FMT_BF16 = 1
 FMT_Q8 = 2
+FMT_Q8_0 = 3     # Q8 with the pages' block layout: per 32 codes a 34-byte block led by a little-endian f16 scale
 INPUT_TOKENS = 0
 INPUT_HIDDEN = 1
 
@@ -154,16 +155,20 @@ SCALE_ID = 1 << 20       # offset of a Q8 matrix's scale stream
 TOKENS_ID = 1 << 24      # token-id streams
 HIDDEN_ID = 1 << 25      # fp32 hidden-state inputs
 KV_ID = 1 << 26          # KV-cache fill streams
+LOGITS_ID = 1 << 27      # synthetic logits rows (sampling inputs)
 
 
 @dataclass
 class Matrix:
-    """Canonical [rows, cols] matrix: bf16 bits, or Q8 int8 codes + f32 scales [rows, cols/32]."""
+    """Canonical [rows, cols] matrix: bf16 bits, or Q8 int8 codes + f32 scales [rows, cols/32].  For the
+    Q8_0 format also the 34-byte blocks [rows, cols/32 * 34] (f16 scale bits little-endian, then the 32
+    codes); its `scales` then hold the f16 scale values widened to f32 (exact)."""
     rows: int
     cols: int
     bf16: np.ndarray | None = None
     codes: np.ndarray | None = None
     scales: np.ndarray | None = None
+    q8_0: np.ndarray | None = None
 
     @property
     def is_q8(self):
@@ -182,8 +187,21 @@ def _matrix(shape: ModelShape, seed: int, tid: int, rows: int, cols: int, std: f
     if shape.fmt == FMT_BF16:
         return Matrix(rows, cols, bf16=normal_bf16(seed, tid, (rows, cols), 0.0, std))
     assert cols % 32 == 0
-    return Matrix(rows, cols, codes=int8_uniform(seed, tid, (rows, cols), -127, 127),
-                  scales=uniform_f32(seed, tid + SCALE_ID, (rows, cols // 32), 1e-3, 1e-2))
+    codes = int8_uniform(seed, tid, (rows, cols), -127, 127)
+    scales = uniform_f32(seed, tid + SCALE_ID, (rows, cols // 32), 1e-3, 1e-2)
+    if shape.fmt == FMT_Q8:
+        return Matrix(rows, cols, codes=codes, scales=scales)
+    return q8_0_matrix(codes, scales.astype(np.float16))
+
+
+def q8_0_matrix(codes: np.ndarray, scales16: np.ndarray) -> Matrix:
+    """Packs int8 codes [rows, cols] and f16 scales [rows, cols/32] into Q8_0 blocks."""
+    rows, cols = codes.shape
+    nb = cols // 32
+    blk = np.empty((rows, nb, 34), np.uint8)
+    blk[:, :, :2] = np.ascontiguousarray(scales16.astype("<f2")).view(np.uint8).reshape(rows, nb, 2)
+    blk[:, :, 2:] = codes.reshape(rows, nb, 32).view(np.uint8)
+    return Matrix(rows, cols, codes=codes, scales=scales16.astype(np.float32), q8_0=blk.reshape(rows, nb * 34))
 
 
 def _norm(shape: ModelShape, seed: int, tid: int, n: int):
@@ -220,6 +238,12 @@ def tokens(seed: int, purpose: int, n: int, vocab: int) -> np.ndarray:
 
 def hidden_inputs(seed: int, purpose: int, n: int, hidden: int) -> np.ndarray:
     return normal_f32(seed, HIDDEN_ID + purpose, (n, hidden), 0.0, 1.0)
+
+
+def logits_rows(seed: int, purpose: int, rows: int, vocab: int, std: float = 3.0) -> np.ndarray:
+    """f32 N(0, std) rows standing in for a decode step's logits (the Q8 workload's logits have RMS ~14, the
+    bf16 workload's ~1-3)."""
+    return normal_f32(seed, LOGITS_ID + purpose, (rows, vocab), 0.0, std)
 
 
 def kv_fill(seed: int, seq: int, layer: int, n_kv: int, n_pos: int, head_dim: int):
@@ -273,12 +297,14 @@ def abi_config_kwargs(shape: ModelShape) -> dict:
 
 def abi_tensors(w: Weights, with_lm_head: bool = False) -> list:
     """Tensor list (kind name, layer, dtype code, arrays) in the order of the inventory; dtype codes
-    1 = bf16 bits, 2 = f32, 3 = int8 codes + f32 scales."""
-    q8 = w.shape.fmt == FMT_Q8
+    1 = bf16 bits, 2 = f32, 3 = int8 codes + f32 scales, 4 = Q8_0 34-byte blocks."""
+    q8 = w.shape.fmt in (FMT_Q8, FMT_Q8_0)
     out = []
 
     def mat(kind, layer, m):
-        if q8:
+        if w.shape.fmt == FMT_Q8_0:
+            out.append(dict(kind=kind, layer=layer, dtype=4, data=m.q8_0))
+        elif q8:
             out.append(dict(kind=kind, layer=layer, dtype=3, data=m.codes, scales=m.scales))
         else:
             out.append(dict(kind=kind, layer=layer, dtype=1, data=m.bf16))

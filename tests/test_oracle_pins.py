@@ -402,3 +402,110 @@ def test_reset_then_replay_equals_fresh_and_kv_roundtrip():
     rc, k2, v2 = m.kv_read(0, 1, 3, 5)
     assert rc == 0 and np.array_equal(k, k2) and np.array_equal(v, v2)
     assert m.kv_write(0, 1, TINY.max_ctx - 2, k, v) == oracle.ORC_INVALID_ARGUMENT
+
+
+
+# ---------------------------------------------------------------------------------------------------------
+# Q8_0 blocks ("Scalar-Native ...", section 3 "The Q8_0 Block Contract", section 5 q8_dot, section 9
+# "Quantized Tails")
+# ---------------------------------------------------------------------------------------------------------
+def test_f16_to_f32_every_bit_pattern():
+    """The oracle's binary16 widening, written from the format definition, against numpy's IEEE half type for
+    all 65,536 patterns (NaN patterns must stay NaN)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([oracle.f16_to_f32(b) for b in bits], np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def _block(scale16_bits, codes):
+    return np.concatenate([np.array([scale16_bits & 0xFF, scale16_bits >> 8], np.uint8),
+                           np.asarray(codes, np.int8).view(np.uint8)])
+
+
+@pytest.mark.parametrize("scale_bits", [0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF])
+def test_q8_0_quantized_tails_vector(scale_bits):
+    """Section 9's vector: one block whose payload alternates the extremes +127/-127, against ones.  Every
+    product q * scale is exact in f32 even for a subnormal f16 scale (2^-24 * 127 is a normal f32), so the
+    sequential sum returns to exactly 0 after each pair: the result is exactly 0, with no underflow."""
+    codes = np.array([127, -127] * 16, np.int8)
+    assert oracle.q8_0_dot(_block(scale_bits, codes), np.ones(32, np.float32)) == 0.0
+    # and a constant payload gives exactly 32 * q * scale (every partial sum is a small multiple of q * s)
+    s = float(np.array([scale_bits], np.uint16).view(np.float16)[0])
+    got = oracle.q8_0_dot(_block(scale_bits, np.full(32, 5, np.int8)), np.ones(32, np.float32))
+    assert got == np.float32(np.float32(5.0) * np.float32(s)) * 32
+
+
+def test_q8_0_dot_follows_the_page_order_and_equals_widened_q8():
+    """The block reader against the pages' loop evaluated in numpy f32 step by step, and against the f32-scale
+    Q8 dot with the scales widened (identical arithmetic once the f16 scale is read)."""
+    rng = np.random.default_rng(7)
+    n = 1024
+    codes = rng.integers(-127, 128, n).astype(np.int8)
+    scales16 = rng.uniform(1e-3, 1e-2, n // 32).astype(np.float16)
+    act = rng.standard_normal(n).astype(np.float32)
+    m = synth.q8_0_matrix(codes.reshape(1, n), scales16.reshape(1, -1))
+    got = oracle.q8_0_dot(m.q8_0[0], act)
+    acc = np.float32(0)
+    for b in range(n // 32):
+        sc = np.float32(scales16[b])
+        for i in range(32):
+            acc = np.float32(acc + np.float32(act[32 * b + i] * np.float32(np.float32(codes[32 * b + i]) * sc)))
+    assert got == acc
+    assert got == oracle.q8_dot(codes, scales16.astype(np.float32), act)
+
+
+def test_q8_0_round_trip_and_dequant():
+    """Dequantized element = one f32 multiply of the code by the widened f16 scale; re-quantizing with that
+    scale returns every code in [-127, 127]."""
+    shp = replace(synth.QWEN3_06B, fmt=synth.FMT_Q8_0, vocab=64, n_layers=1, hidden=1024, inter=1024,
+                  n_q_heads=8, n_kv_heads=4)
+    W = synth.make_weights(shp, seed=3)
+    m = W.layers[0]["o"]
+    for r in (0, 17, m.rows - 1):
+        row = oracle.dequant_row(m, r)
+        sc = np.repeat(m.scales[r], 32)
+        assert np.array_equal(row.view(np.uint32), (m.codes[r].astype(np.float32) * sc).view(np.uint32))
+        assert np.array_equal(np.rint(row / sc).astype(np.int32), m.codes[r].astype(np.int32))
+
+
+def test_q8_0_model_equals_widened_q8_model():
+    """A whole Q8_0 model through the oracle gives bit-identical logits to the same model given as codes plus
+    the widened scales (the block format changes storage, not arithmetic), and agrees with the fp64 twin."""
+    shp = replace(TINY, fmt=synth.FMT_Q8_0)
+    W = synth.make_weights(shp, seed=12)
+    toks = synth.tokens(12, 0, 6, shp.vocab)
+    a = oracle.Model(W)
+    # the same codes and widened scales without the blocks: the oracle reads them as the f32-scale format
+    plain = lambda m: synth.Matrix(m.rows, m.cols, codes=m.codes, scales=m.scales)
+    W8 = synth.Weights(replace(shp, fmt=synth.FMT_Q8), plain(W.embed), W.final_norm,
+                       [{k: (plain(v) if isinstance(v, synth.Matrix) else v) for k, v in d.items()} for d in W.layers])
+    b = oracle.Model(W8)
+    for t in toks:
+        ra, _, la, _ = a.step(0, int(t))
+        rb, _, lb, _ = b.step(0, int(t))
+        assert ra == rb == 0 and np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+    _, l64 = twin64.forward64(W, tokens=toks, kv_round_bf16=True)
+    assert np.max(np.abs(la - l64)) / np.max(np.abs(l64)) < 1e-4
+
+
+def test_step_with_its_own_kv_forced_is_the_plain_step():
+    """Teacher forcing of the appended position: a step that reports its own rounded K/V gives the plain step's
+    logits bit for bit and caches exactly those values; a forced value is what the cache then holds."""
+    W = synth.make_weights(replace(TINY, fmt=synth.FMT_Q8), seed=13)
+    a, b = oracle.Model(W), oracle.Model(W)
+    toks = synth.tokens(13, 0, 5, TINY.vocab)
+    for i, t in enumerate(toks):
+        ra, _, la, _ = a.step(0, int(t))
+        rb, _, lb, _, own = b.step_forced(0, int(t))
+        assert ra == rb == 0 and np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+        _, k, v = b.kv_read(0, 1, i, 1)
+        assert np.array_equal(k[:, 0], own[1, 0]) and np.array_equal(v[:, 0], own[1, 1])
+    c = oracle.Model(W)
+    forced = own.copy()
+    forced[0, 1, 0, 3] ^= 1
+    assert c.step_forced(0, int(toks[0]), kv_force=forced)[0] == 0
+    _, k, v = c.kv_read(0, 0, 0, 1)
+    assert v[0, 0, 3] == forced[0, 1, 0, 3] and np.array_equal(k[:, 0], forced[0, 0])
