@@ -60,7 +60,7 @@ typedef enum {
     QW3_DEVICE_ERROR = 21
 } qw3_status_t;
 
-enum { QW3_WEIGHTS_BF16 = 1, QW3_WEIGHTS_Q8 = 2 };
+enum { QW3_WEIGHTS_BF16 = 1, QW3_WEIGHTS_Q8 = 2, QW3_WEIGHTS_Q8_0 = 3 };
 enum { QW3_INPUT_TOKENS = 0, QW3_INPUT_HIDDEN = 1 };
 
 /* Model and session shape.  Every field is explicit; nothing is defaulted ("M1 — Load the weights",
@@ -70,8 +70,11 @@ enum { QW3_INPUT_TOKENS = 0, QW3_INPUT_HIDDEN = 1 };
  *   1 <= n_seq <= 16; 1 <= max_prefill; max_ctx >= 1; vocab_size >= 1 in token mode.
  * weight_format QW3_WEIGHTS_Q8 stores every matrix (projections, MLP, embedding) as int8 codes in
  * [-127, 127] with one f32 scale per 32 consecutive input elements ("Scalar-Native ...", section 3
- * "Mixed-Q8 Quantization Definition", with the scale widened to f32).  Norm weights are bf16 in the
- * bf16 format and f32 in the Q8 format.
+ * "Mixed-Q8 Quantization Definition", with the scale widened to f32).  QW3_WEIGHTS_Q8_0 takes the same
+ * matrices in that section's own Q8_0 block layout (QW3_DT_Q8_0 tensors: per 32 inputs one 34-byte block,
+ * a little-endian f16 scale then 32 int8 codes); the packer splits the blocks into codes and scales widened
+ * exactly to f32, so both formats run the same kernels and dequantize to the same f32 values.  Norm weights
+ * are bf16 in the bf16 format and f32 in the Q8 formats.
  * input_mode QW3_INPUT_HIDDEN runs the layer stack on caller-supplied f32 hidden states (no embedding,
  * no final norm, no logits; vocab_size must be 0). */
 typedef struct qw3_config {
@@ -118,11 +121,14 @@ enum {
     QW3_T_UP = 12,        /* [intermediate, hidden] */
     QW3_T_DOWN = 13       /* [hidden, intermediate] */
 };
-enum { QW3_DT_BF16 = 1, QW3_DT_F32 = 2, QW3_DT_Q8 = 3 };
+enum { QW3_DT_BF16 = 1, QW3_DT_F32 = 2, QW3_DT_Q8 = 3, QW3_DT_Q8_0 = 4 };
 
 /* One canonical host tensor.  Matrices are [rows = out, cols = in] row-major (y = x W^T).
  * QW3_DT_BF16: data = uint16 bf16 bit patterns.  QW3_DT_F32: data = float.
  * QW3_DT_Q8: data = int8 codes [rows, cols], scales = float [rows, cols/32].
+ * QW3_DT_Q8_0: data = uint8 blocks [rows, cols/32, 34] (bytes 0-1 the f16 scale, little-endian; bytes 2-33
+ * the int8 codes of inputs 32b..32b+31), scales = NULL ("Scalar-Native ...", section 3 "The Q8_0 Block
+ * Contract"; a non-finite scale is rejected with QW3_INVALID_MODEL).
  * Norm tensors are vectors: rows = 1, cols = length.  layer = -1 for global tensors. */
 typedef struct qw3_tensor {
     int32_t kind;
@@ -135,8 +141,17 @@ typedef struct qw3_tensor {
     const float *scales;
 } qw3_tensor_t;
 
-/* ABI version the library was built with. */
+/* ABI version the library was built with; a caller compares it with QW3_ABI_VERSION before any other call
+ * ("Portable WebAssembly Runtime Architecture for TinyRustLM", "Typed host/Wasm API": the boundary is
+ * versioned and a mismatch is a typed error, QW3_UNSUPPORTED_ABI from qw3_preflight/qw3_create). */
 uint32_t qw3_abi_version(void);
+
+/* Host-only: the RoPE cos/sin table the library uploads at load time ("Scalar-Native ...", section 2 item
+ * 4, rotation of pair i by pos * theta^(-2i/head_dim); "Portable WebAssembly ..." recommends packed RoPE
+ * tables over platform libm).  Angles, cos and sin are evaluated in double and rounded once to f32.
+ * cos_out, sin_out: caller-owned host arrays [n_pos][head_dim/2].  Errors: QW3_INVALID_ARGUMENT for NULL
+ * outputs, odd or < 2 head_dim, negative n_pos or theta <= 1.  Touches no device. */
+int32_t qw3_rope_table(double theta, int32_t head_dim, int32_t n_pos, float *cos_out, float *sin_out);
 
 /* Validates cfg and reports the arena budget.  Allocates nothing ("Portable WebAssembly Runtime ...",
  * memory formulas: preflight rejects a model/context pair before allocating).  Sizes use checked 64-bit
@@ -145,8 +160,11 @@ uint32_t qw3_abi_version(void);
 int32_t qw3_preflight(const qw3_config_t *cfg, qw3_sizes_t *out);
 
 /* Creates a model in a caller-owned device arena of at least qw3_preflight(cfg).total bytes, 256-byte
- * aligned (QW3_ALIGNMENT otherwise; QW3_OUT_OF_MEMORY if too small).  No device work is done here;
- * the arena is initialised by qw3_load_weights.  Writes the new handle to *handle_out. */
+ * aligned (QW3_ALIGNMENT otherwise; QW3_OUT_OF_MEMORY if too small or the 64-entry handle table is full).
+ * No device work is done here; the arena is initialised by qw3_load_weights.  Writes the new handle
+ * (generation << 32 | slot, "Portable WebAssembly ...", "Generational handles") to *handle_out.  The
+ * single-launch batch-1 decode is selected only when the current device can hold its whole grid at once
+ * (occupancy query); otherwise single-sequence steps run kernel by kernel. */
 int32_t qw3_create(const qw3_config_t *cfg, void *arena_dev, uint64_t arena_bytes, uint64_t *handle_out);
 
 /* Validates and uploads the whole tensor set, packing it into the arena's device layout, then resets
@@ -157,6 +175,40 @@ int32_t qw3_create(const qw3_config_t *cfg, void *arena_dev, uint64_t arena_byte
  * QW3_INVALID_MODEL before any device work.  Host buffers are read during the call only; the call
  * returns after the copies have completed on `stream`. */
 int32_t qw3_load_weights(uint64_t handle, const qw3_tensor_t *tensors, int32_t n, void *stream);
+
+/* ---- weight files ("Scalar-Native ...", section 3 "File Layout and Safe Metadata Parsing"; "M1 — Load the
+ *      weights", "The safetensors format -- three regions" and "The cross-check") -------------------------- */
+
+/* What qw3_inspect_file found in a weight file ("M1 — Load the weights", "What it prints": tensor count and
+ * the stored / logical / embedding parameter totals, a tied lm_head copy counted once in logical_params). */
+typedef struct qw3_file_report {
+    int64_t n_tensors;
+    int64_t stored_params;
+    int64_t logical_params;
+    int64_t embed_params;
+    int64_t header_bytes;
+    int32_t n_layers;        /* highest layer index named + 1 */
+    int32_t lm_head_present; /* the file ships lm_head.weight */
+} qw3_file_report_t;
+
+/* Host-only: maps `path` read-only and validates it as a safetensors container (an 8-byte little-endian
+ * header length, a JSON header of {name: {dtype, shape, data_offsets}} and an optional "__metadata__" map of
+ * strings, then the data blob).  Checks, in this precedence per entry: a header length beyond the file
+ * (QW3_BOUNDS), malformed JSON, an unknown or duplicate name (the Qwen3 inventory: model.embed_tokens.weight,
+ * model.norm.weight, optional lm_head.weight, model.layers.<l>.{input_layernorm, self_attn.{q,k,v,o}_proj,
+ * self_attn.{q,k}_norm, post_attention_layernorm, mlp.{gate,up,down}_proj}.weight) or an unknown dtype
+ * (BF16, F32, or Q8_0: shape [rows, cols] stored as the Q8_0 34-byte blocks of QW3_DT_Q8_0) ->
+ * QW3_INVALID_MODEL; a size that does not match the shape -> QW3_INVALID_MODEL (wrapping arithmetic ->
+ * QW3_INTEGER_OVERFLOW); an end offset beyond the blob -> QW3_BOUNDS; a tensor whose file offset is not a
+ * multiple of 8 -> QW3_ALIGNMENT; spans that overlap, leave a hole or leave trailing bytes ->
+ * QW3_INVALID_MODEL.  An unreadable path is QW3_INVALID_ARGUMENT.  Fills *out on success. */
+int32_t qw3_inspect_file(const char *path, qw3_file_report_t *out);
+
+/* Validates `path` as qw3_inspect_file does, then hands its tensors (pointing into the read-only mapping,
+ * no copy on the host) to qw3_load_weights, which checks them against the handle's configuration (dtypes:
+ * BF16 matrices and norms for QW3_WEIGHTS_BF16; Q8_0 matrices and F32 norms -- the SLM2 layout -- for
+ * QW3_WEIGHTS_Q8_0) and uploads them.  The mapping is released before the call returns. */
+int32_t qw3_load_file(uint64_t handle, const char *path, void *stream);
 
 /* Prefill of sequence `seq`: appends n_tokens tokens at positions len..len+n_tokens-1 (KV cache, "Scalar-
  * Native ...", section 6 "Continuation and Append") and writes the last position's logits (vocab f32,
@@ -170,9 +222,15 @@ int32_t qw3_prefill(uint64_t handle, int32_t seq, const int32_t *tokens_dev, int
 /* One greedy decode step for all n_seq sequences: tokens_dev int32 [n_seq] (may alias the previous
  * step's argmax_dev), logits_dev f32 [n_seq, vocab] (may be NULL), argmax_dev int32 [n_seq] (required).
  * Each sequence appends one position and commits len += 1.  Any sequence at len == max_ctx returns
- * QW3_CONTEXT_EXCEEDED with nothing launched.  A non-finite logit latches QW3_NUMERICAL_FAILURE
- * ("Scalar-Native ...", section 4 "NaN/Inf Rejection"), reported by qw3_status_poll and by every later
- * call until qw3_reset_kv; the argmax of steps completed before stays valid (section 8). */
+ * QW3_CONTEXT_EXCEEDED with nothing launched.
+ * Failures found on the device ("Scalar-Native ...", section 4 "NaN/Inf Rejection": a NaN or infinite
+ * logit; also a token outside [0, vocab), or a cross-workgroup wait that gave up) are latched in a device
+ * status word.  The failing step commits nothing, and neither does any step enqueued after it: the
+ * committed lengths stay where the last good step left them (section 8: the argmax of completed steps
+ * stays valid).  Calls are asynchronous, so the host learns of a latched failure only through
+ * qw3_status_poll; from that poll on, every call that would launch work returns the latched code with
+ * nothing launched, until qw3_reset_kv.  Logits and argmax written by the failing step and by any step
+ * after it are unspecified. */
 int32_t qw3_decode_step(uint64_t handle, const int32_t *tokens_dev, float *logits_dev, int32_t *argmax_dev,
                         void *stream);
 
@@ -181,17 +239,77 @@ int32_t qw3_decode_step(uint64_t handle, const int32_t *tokens_dev, float *logit
  * length ("Scalar-Native ...", section 6 "Cancellation and Reset").  Host-side only. */
 int32_t qw3_reset_kv(uint64_t handle, int32_t seq);
 
-/* Waits for `stream` and returns the latched device status: QW3_OK, QW3_NUMERICAL_FAILURE, or
- * QW3_DEVICE_ERROR when a wait inside the single-launch decode kernel timed out (its workgroups could not
- * all be resident at once, e.g. because other work held the compute units).  Both poison the handle until
- * qw3_reset_kv. */
+/* Waits for `stream` and returns the latched device status ("Scalar-Native ...", section 8: failures are
+ * typed and never repaired; "Portable WebAssembly ...", "Error taxonomy"), by precedence:
+ * QW3_DEVICE_ERROR when a bounded wait between workgroups gave up (the single-launch decode's workgroups
+ * could not all be resident at once, e.g. because other work held the compute units), else
+ * QW3_NUMERICAL_FAILURE for a non-finite logit or a cached key/value beyond the f16 range of the prefill
+ * attention, else QW3_INVALID_ARGUMENT for a token id outside [0, vocab); QW3_OK when nothing is latched.
+ * Any failure poisons the handle until qw3_reset_kv and sets the host's lengths (qw3_get_len) to the
+ * device's committed lengths. */
 int32_t qw3_status_poll(uint64_t handle, void *stream);
 
-/* Host copy of a sequence's committed KV length. */
+/* Host copy of a sequence's KV length: the length after every call enqueued so far, or, after
+ * qw3_status_poll has reported a failure, the committed length the device kept ("Scalar-Native ...",
+ * section 6: current_seq_len). */
 int32_t qw3_get_len(uint64_t handle, int32_t seq, int32_t *len_out);
 
-/* Releases the handle (the arena stays owned by the caller).  Later use returns QW3_STALE_HANDLE. */
+/* Releases the handle (the arena stays owned by the caller).  Later use returns QW3_STALE_HANDLE
+ * ("Portable WebAssembly ...", "Generational handles": a stale handle is detected, never reused). */
 int32_t qw3_destroy(uint64_t handle);
+
+/* ---- deterministic sampling ("Scalar-Native ...", section 7 "Deterministic Sampling Contract";
+ *      "Portable WebAssembly ...", "Deterministic sampling contract" and "Sampling order") ------------ */
+
+#define QW3_SAMPLE_MAX_TOP_K 1024u   /* candidates kept by top-k when temperature > 0 */
+#define QW3_SAMPLE_MAX_VOCAB 262144u
+#define QW3_SAMPLE_MAX_ROWS 16u
+#define QW3_SAMPLE_MAX_STOP 8u
+
+typedef struct qw3_sample_params {
+    float temperature;        /* 0: greedy (greatest logit, lowest id on ties, no draw); else positive, finite */
+    float top_p;              /* (0, 1]: keep the shortest (probability desc, id asc) prefix reaching top_p */
+    float repetition_penalty; /* positive, finite; 1 changes nothing */
+    int32_t top_k;            /* 1..QW3_SAMPLE_MAX_TOP_K (ignored when temperature == 0) */
+} qw3_sample_params_t;
+
+/* Host-only: PCG32 state for (seed, stream_id) as "Portable WebAssembly ..." freezes its seeding (state 0,
+ * increment 2*stream_id+1, advance, add the seed, advance).  state_out[0] = state, state_out[1] = increment:
+ * the per-row generator layout qw3_sample reads and advances. */
+int32_t qw3_pcg32_seed(uint64_t seed, uint64_t stream_id, uint64_t *state_out);
+
+/* Bytes of device workspace qw3_sample needs for n_rows rows (QW3_INVALID_ARGUMENT outside
+ * 1..QW3_SAMPLE_MAX_ROWS). */
+int32_t qw3_sample_workspace_bytes(int32_t n_rows, uint64_t *bytes_out);
+
+/* One token per row of logits, in the order of "Portable WebAssembly ...", "Sampling order" (with
+ * "Scalar-Native ...", section 7): forbidden tokens -> -inf; repetition penalty on every token present in the
+ * row's history (positive logits divided by the penalty, negative ones multiplied, each token once); NaN ->
+ * -inf; -0 -> +0; temperature 0 -> greedy; otherwise divide by the temperature, top-k by (value desc, id asc),
+ * stable probabilities over the survivors, order by (probability desc, id asc), top-p (shortest prefix whose
+ * cumulative probability is at least top_p), re-normalise, and draw u = (word >> 8) * 2^-24 from the row's
+ * PCG32 generator: the first candidate whose cumulative probability exceeds u.
+ *   logits_dev   f32 [n_rows][ld_logits] device (ld_logits >= vocab), e.g. qw3_decode_step's logits
+ *   history_dev  int32 [n_rows][n_history] device (entries outside [0, vocab) are ignored; NULL iff 0)
+ *   forbid_dev   int32 [n_forbid] device, shared by all rows (NULL iff n_forbid == 0)
+ *   stop_ids     host int32 [n_stop], n_stop <= QW3_SAMPLE_MAX_STOP: done_out_dev[r] = 1 when row r's token is
+ *                one of them (e.g. the end-of-turn token)
+ *   rng_dev      uint64 [n_rows][2] device (state, increment; see qw3_pcg32_seed); advanced by one word per row
+ *                when temperature > 0, untouched at temperature 0
+ *   token_out_dev int32 [n_rows] device; done_out_dev, status_out_dev int32 [n_rows] device or NULL.  A row
+ *                whose logits hold +inf (or overflow when divided by the temperature) or no finite value gets
+ *                token -1 and status QW3_NUMERICAL_FAILURE ("Scalar-Native ...", section 4), else QW3_OK.
+ *   workspace_dev device memory of at least qw3_sample_workspace_bytes(n_rows), 256-byte aligned, owned by
+ *                the caller; its contents need no initialisation.
+ * Host-checked errors (nothing launched): QW3_INVALID_ARGUMENT for bad pointers, sizes or parameters
+ * (penalty <= 0, temperature < 0, top_k outside 1..QW3_SAMPLE_MAX_TOP_K or top_p outside (0, 1] when
+ * temperature > 0, vocab outside 1..QW3_SAMPLE_MAX_VOCAB), QW3_ALIGNMENT for a misaligned workspace,
+ * QW3_OUT_OF_MEMORY for a workspace that is too small.  Asynchronous on `stream`; two launches. */
+int32_t qw3_sample(const float *logits_dev, int32_t n_rows, int32_t vocab, int64_t ld_logits,
+                   const qw3_sample_params_t *params, const int32_t *history_dev, int32_t n_history,
+                   const int32_t *forbid_dev, int32_t n_forbid, const int32_t *stop_ids, int32_t n_stop,
+                   uint64_t *rng_dev, int32_t *token_out_dev, int32_t *done_out_dev, int32_t *status_out_dev,
+                   void *workspace_dev, uint64_t workspace_bytes, void *stream);
 
 /* ---- test and benchmark hooks (not part of the serving path) ------------------------------------- */
 
@@ -210,8 +328,10 @@ int32_t qw3_kv_write(uint64_t handle, int32_t seq, int32_t layer, int32_t pos0, 
 int32_t qw3_kv_read(uint64_t handle, int32_t seq, int32_t layer, int32_t pos0, int32_t n_pos, uint16_t *k_dev,
                     uint16_t *v_dev, void *stream);
 
-/* Sets the committed KV length of `seq` (after qw3_kv_write).  QW3_BOUNDS when len > max_ctx. */
-int32_t qw3_set_len(uint64_t handle, int32_t seq, int32_t len, void *stream);
+/* Sets the committed KV length of `seq` (after qw3_kv_write; "Scalar-Native ...", section 6, the session's
+ * current_seq_len).  QW3_BOUNDS when len > max_ctx, QW3_INVALID_ARGUMENT for a bad seq or before
+ * qw3_load_weights. */
+int32_t qw3_kv_set_len(uint64_t handle, int32_t seq, int32_t len, void *stream);
 
 /* Dequantized f32 copy of a packed matrix as the kernels read it: kind in QW3_T_Q..QW3_T_DOWN (with
  * layer) or QW3_T_EMBED; out_dev f32 [rows, cols].  For Q8 each element is one f32 multiply code*scale. */

@@ -73,7 +73,7 @@ def test_preflight_sizes_follow_the_byte_model(L):
     (dict(n_q_heads=24, n_kv_heads=8), 13),     # group of 3: no kernel
     (dict(hidden=1280), 13),                    # not a multiple of 512 (bf16 lane slicing)
     (dict(n_seq=17), 13),
-    (dict(weight_format=3), 12),
+    (dict(weight_format=4), 12),
     (dict(input_mode=1), 1),                    # hidden mode must have vocab 0
     (dict(vocab=0), 1),
     (dict(eps=0.0), 1),
@@ -129,6 +129,8 @@ def _tensor_array(tensors):
         sc = None if t.get("scales") is None else np.ascontiguousarray(t["scales"], np.float32)
         keep += [data, sc]
         rows, cols = (1, data.shape[0]) if data.ndim == 1 else data.shape
+        if t["dtype"] == q.DT_Q8_0:
+            cols = cols // 34 * 32
         arr[i] = q.Tensor(q.KIND[t["kind"]], t.get("layer", -1), t["dtype"], 0, rows, cols, data.ctypes.data,
                           sc.ctypes.data if sc is not None else None)
     return arr, keep
@@ -189,3 +191,60 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(q, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         q.lib()
+
+
+def test_rope_table_bit_exact_with_oracle(L):
+    """The table the library uploads equals the oracle's (angle, cos, sin in double, one rounding to f32) bit
+    for bit at every position of a long context, including positions where an f32 angle would differ."""
+    import oracle
+    theta, n = 1e6, 8300
+    c, s = q.rope_table(theta, 128, n)
+    for pos in list(range(0, 64)) + list(range(2040, 2060)) + list(range(8180, 8300)):
+        oc, os_ = oracle.rope_table(theta, 128, pos)
+        assert np.array_equal(c[pos].view(np.uint32), oc.view(np.uint32)), pos
+        assert np.array_equal(s[pos].view(np.uint32), os_.view(np.uint32)), pos
+    assert np.all(c[0] == 1.0) and np.all(s[0] == 0.0)
+    with pytest.raises(q.Qw3Error):
+        q.rope_table(1.0, 128, 4)
+
+
+def test_bf16_single_token_tiles_are_accepted(L):
+    """A bf16 model whose prefill tile is one token has no MFMA prefill; it is still a valid configuration
+    (prompts run token by token through the decode kernels)."""
+    sz = q.preflight(cfg_of(replace(SMALL, max_prefill=1)))
+    assert sz.total > 0
+    h = ctypes.c_uint64(0)
+    assert L.qw3_create(ctypes.byref(cfg_of(replace(SMALL, max_prefill=1))), ctypes.c_void_p(FAKE_ARENA),
+                        sz.total, ctypes.byref(h)) == 0
+    assert L.qw3_destroy(h.value) == 0
+
+
+@pytest.mark.parametrize("mutate", ["q8_codes_for_q8_0", "scales_given", "nan_scale", "short_blocks",
+                                    "lm_head_differs"])
+def test_q8_0_inventory_cross_check(L, mutate):
+    """The Q8_0 format takes the pages' 34-byte blocks: another quantized layout, extra scales, a non-finite
+    f16 scale, truncated blocks or a differing tied lm_head are InvalidModel before any device work."""
+    shp = replace(SMALL, fmt=synth.FMT_Q8_0)
+    W = synth.make_weights(shp, seed=43)
+    tensors = synth.abi_tensors(W)
+    assert all(t["dtype"] == q.DT_Q8_0 for t in tensors if t["kind"] in ("q", "embed", "down"))
+    t = next(t for t in tensors if t["kind"] == "gate" and t["layer"] == 1)
+    if mutate == "q8_codes_for_q8_0":
+        t.update(dtype=q.DT_Q8, data=W.layers[1]["gate"].codes, scales=W.layers[1]["gate"].scales)
+    elif mutate == "scales_given":
+        t["scales"] = W.layers[1]["gate"].scales
+    elif mutate == "nan_scale":
+        blk = t["data"].copy()
+        blk[5, 34 * 3 + 1] = 0x7E   # f16 0x7Exx: NaN
+        t["data"] = blk
+    elif mutate == "short_blocks":
+        t["data"] = t["data"][:, :-34]
+    elif mutate == "lm_head_differs":
+        lm = W.embed.q8_0.copy()
+        lm[2, 40] ^= 1
+        tensors.append(dict(kind="lm_head", layer=-1, dtype=q.DT_Q8_0, data=lm))
+    rc, h = _create(L, cfg_of(shp))
+    assert rc == 0
+    arr, keep = _tensor_array(tensors)
+    assert L.qw3_load_weights(h, arr, len(tensors), None) == 10
+    L.qw3_destroy(h)

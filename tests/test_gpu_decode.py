@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from parity import argmax_ok, assert_close, build_gpu_model, sync_appended_kv
+from parity import Margins, argmax_ok, assert_close, build_gpu_model, forced_step
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def _say(*a):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("fmt", [synth.FMT_BF16, synth.FMT_Q8])
+@pytest.mark.parametrize("fmt", [synth.FMT_BF16, synth.FMT_Q8, synth.FMT_Q8_0])
 def test_dequant_bit_exact(fmt):
     torch = _torch()
     shp = replace(SMALL, fmt=fmt)
@@ -96,34 +96,32 @@ def _greedy_vs_oracle(shp, seed, steps, prefill_tokens=0, kv_fill_len=0, seqs_ch
     cur = torch.from_numpy(toks.copy()).cuda()
     am = torch.empty(S, dtype=torch.int32, device="cuda")
     logits = torch.empty((S, shp.vocab), dtype=torch.float32, device="cuda")
-    worst = (0.0, 0.0)
+    worst = Margins(f"decode {shp.fmt=} {shp.n_layers=} {shp.n_q_heads}/{shp.n_kv_heads} heads S={S} {path}")
+    kv = {}
     for step in range(steps):
         m.decode_step(cur, am, logits)
         torch.cuda.synchronize()
         g_logits = logits.cpu().numpy()
         g_am = am.cpu().numpy()
         for s in (seqs_checked if seqs_checked is not None else range(S)):
-            pos = orc.get_len(s)
-            rc, o_am, o_logits, _ = orc.step(s, int(cur[s].item()))
+            rc, o_am, o_logits, _ = forced_step(m, orc, s, int(cur[s].item()), shp.n_layers, stats=kv)
             assert rc == 0
-            mab, r = assert_close(g_logits[s], o_logits, f"step {step} seq {s}")
-            worst = (max(worst[0], mab), max(worst[1], r))
+            worst.add(assert_close(g_logits[s], o_logits, f"step {step} seq {s}"))
             assert argmax_ok(int(g_am[s]), o_logits, g_logits[s]), (step, s, int(g_am[s]), o_am)
-            sync_appended_kv(m, orc, s, pos, shp.n_layers)
         cur = am.clone()
     assert m.status() == 0
     for s in range(S):
         assert m.get_len(s) == kv_fill_len + steps
+    worst.report(kv)
     return worst
 
 
 @pytest.mark.parametrize("path", ["mega", "kernels"])
-@pytest.mark.parametrize("fmt", [synth.FMT_BF16, synth.FMT_Q8])
+@pytest.mark.parametrize("fmt", [synth.FMT_BF16, synth.FMT_Q8, synth.FMT_Q8_0])
 def test_decode_small_vs_oracle(fmt, path):
     shp = replace(SMALL, fmt=fmt)
     _say("decode small", shp, path)
-    worst = _greedy_vs_oracle(shp, seed=23, steps=12, path=path)
-    _say("worst max-abs / rel-L2", worst)
+    _greedy_vs_oracle(shp, seed=23, steps=12, path=path)
 
 
 @pytest.mark.parametrize("path", ["mega", "kernels"])

@@ -16,12 +16,12 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 _SO = os.path.join(_HERE, "libqw3.so")
-_SOURCES = ["api.hip", "decode.hip", "prefill.hip", "mega.hip", "gemv_mfma.hip"]
+_SOURCES = ["api.hip", "decode.hip", "prefill.hip", "mega.hip", "gemv_mfma.hip", "sample.hip", "loader.cpp"]
 
 ABI_VERSION = 1
-WEIGHTS_BF16, WEIGHTS_Q8 = 1, 2
+WEIGHTS_BF16, WEIGHTS_Q8, WEIGHTS_Q8_0 = 1, 2, 3
 INPUT_TOKENS, INPUT_HIDDEN = 0, 1
-DT_BF16, DT_F32, DT_Q8 = 1, 2, 3
+DT_BF16, DT_F32, DT_Q8, DT_Q8_0 = 1, 2, 3, 4
 KIND = {"embed": 0, "final_norm": 1, "lm_head": 2, "attn_norm": 3, "q": 4, "k": 5, "v": 6, "q_norm": 7,
         "k_norm": 8, "o": 9, "mlp_norm": 10, "gate": 11, "up": 12, "down": 13}
 STATUS = {0: "Ok", 1: "InvalidArgument", 2: "UnsupportedAbi", 4: "InvalidHandle", 5: "StaleHandle", 6: "Bounds",
@@ -72,9 +72,10 @@ class Tensor(ctypes.Structure):
                 ("data", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
-EXPORTS = ["qw3_abi_version", "qw3_preflight", "qw3_create", "qw3_load_weights", "qw3_prefill", "qw3_decode_step",
+EXPORTS = ["qw3_abi_version", "qw3_rope_table", "qw3_preflight", "qw3_create", "qw3_load_weights", "qw3_prefill", "qw3_decode_step",
            "qw3_reset_kv", "qw3_status_poll", "qw3_get_len", "qw3_destroy", "qw3_block_forward", "qw3_kv_write",
-           "qw3_kv_read", "qw3_set_len", "qw3_dequant", "qw3_bench_kernel"]
+           "qw3_kv_read", "qw3_kv_set_len", "qw3_dequant", "qw3_bench_kernel", "qw3_pcg32_seed",
+           "qw3_sample_workspace_bytes", "qw3_sample", "qw3_inspect_file", "qw3_load_file"]
 
 _lib = None
 
@@ -89,6 +90,7 @@ def lib():
         V, I32, U64, P = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_void_p
         sig = {
             "qw3_abi_version": (ctypes.c_uint32, []),
+            "qw3_rope_table": (I32, [ctypes.c_double, I32, I32, P, P]),
             "qw3_preflight": (I32, [ctypes.POINTER(Config), ctypes.POINTER(Sizes)]),
             "qw3_create": (I32, [ctypes.POINTER(Config), V, U64, ctypes.POINTER(U64)]),
             "qw3_load_weights": (I32, [U64, ctypes.POINTER(Tensor), I32, V]),
@@ -101,9 +103,15 @@ def lib():
             "qw3_block_forward": (I32, [U64, P, I32, P, V]),
             "qw3_kv_write": (I32, [U64, I32, I32, I32, I32, P, P, V]),
             "qw3_kv_read": (I32, [U64, I32, I32, I32, I32, P, P, V]),
-            "qw3_set_len": (I32, [U64, I32, I32, V]),
+            "qw3_kv_set_len": (I32, [U64, I32, I32, V]),
             "qw3_dequant": (I32, [U64, I32, I32, P, V]),
             "qw3_bench_kernel": (I32, [U64, I32, I32, I32, V]),
+            "qw3_pcg32_seed": (I32, [U64, U64, P]),
+            "qw3_inspect_file": (I32, [ctypes.c_char_p, ctypes.POINTER(FileReport)]),
+            "qw3_load_file": (I32, [U64, ctypes.c_char_p, V]),
+            "qw3_sample_workspace_bytes": (I32, [I32, ctypes.POINTER(U64)]),
+            "qw3_sample": (I32, [P, I32, I32, ctypes.c_int64, ctypes.POINTER(SampleParams), P, I32, P, I32, P, I32,
+                                 P, P, P, P, P, U64, V]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -111,6 +119,66 @@ def lib():
             f.argtypes = args
         _lib = L
     return _lib
+
+
+class FileReport(ctypes.Structure):
+    _fields_ = [("n_tensors", ctypes.c_int64), ("stored_params", ctypes.c_int64), ("logical_params", ctypes.c_int64),
+                ("embed_params", ctypes.c_int64), ("header_bytes", ctypes.c_int64), ("n_layers", ctypes.c_int32),
+                ("lm_head_present", ctypes.c_int32)]
+
+
+def inspect_file(path):
+    """Validates a safetensors / SLM2 weight file on the host (no device); returns its FileReport."""
+    r = FileReport()
+    check(lib().qw3_inspect_file(os.fsencode(path), ctypes.byref(r)), "qw3_inspect_file")
+    return r
+
+
+class SampleParams(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_p", ctypes.c_float), ("repetition_penalty", ctypes.c_float),
+                ("top_k", ctypes.c_int32)]
+
+
+def pcg32_seed(seed, stream_id):
+    """(state, increment) of the sampling generator for (seed, stream_id)."""
+    out = (ctypes.c_uint64 * 2)()
+    check(lib().qw3_pcg32_seed(seed, stream_id, out), "qw3_pcg32_seed")
+    return int(out[0]), int(out[1])
+
+
+class Sampler:
+    """Deterministic sampling of token ids from device logits rows (qw3_sample); owns its device workspace and
+    one PCG32 generator per row."""
+
+    def __init__(self, n_rows, seeds, stream_ids=None, device="cuda:0"):
+        import torch
+        self.n_rows = n_rows
+        self.device = torch.device(device)
+        nb = ctypes.c_uint64(0)
+        check(lib().qw3_sample_workspace_bytes(n_rows, ctypes.byref(nb)), "qw3_sample_workspace_bytes")
+        self._ws = torch.empty(int(nb.value) + 256, dtype=torch.uint8, device=self.device)
+        self._ws_ptr = (self._ws.data_ptr() + 255) & ~255
+        self._ws_bytes = int(nb.value)
+        sids = stream_ids if stream_ids is not None else list(range(n_rows))
+        st = [pcg32_seed(int(seeds[r]), int(sids[r])) for r in range(n_rows)]
+        self.rng = torch.tensor(np.array(st, np.uint64).view(np.int64), device=self.device)
+
+    def __call__(self, logits, temperature=1.0, top_k=50, top_p=1.0, penalty=1.0, history=None, forbid=None,
+                 stop=(), stream=None, status=None, done=None):
+        """logits: f32 [n_rows, ld] device tensor (the first `vocab` = logits.shape[1] columns); history int32
+        [n_rows, n] device tensor or None; forbid int32 [m] device tensor or None.  Returns token ids (int32
+        [n_rows] device tensor)."""
+        import torch
+        tok = torch.empty(self.n_rows, dtype=torch.int32, device=self.device)
+        prm = SampleParams(temperature, top_p, penalty, top_k)
+        stop_arr = (ctypes.c_int32 * max(1, len(stop)))(*stop)
+        nh = 0 if history is None else history.shape[1]
+        nf = 0 if forbid is None else forbid.numel()
+        check(lib().qw3_sample(_ptr(logits), self.n_rows, logits.shape[1], logits.stride(0), ctypes.byref(prm),
+                               _ptr(history), nh, _ptr(forbid), nf, stop_arr if stop else None, len(stop),
+                               _ptr(self.rng), _ptr(tok), _ptr(done), _ptr(status), ctypes.c_void_p(self._ws_ptr),
+                               self._ws_bytes, _stream(stream)), "qw3_sample")
+        return tok
 
 
 def check(rc, what):
@@ -128,6 +196,14 @@ def preflight(cfg: Config) -> Sizes:
     sz = Sizes()
     check(lib().qw3_preflight(ctypes.byref(cfg), ctypes.byref(sz)), "qw3_preflight")
     return sz
+
+
+def rope_table(theta, head_dim, n_pos):
+    """The library's host-built RoPE table: (cos, sin) f32 [n_pos, head_dim/2]."""
+    c = np.empty((n_pos, head_dim // 2), np.float32)
+    s = np.empty((n_pos, head_dim // 2), np.float32)
+    check(lib().qw3_rope_table(theta, head_dim, n_pos, c.ctypes.data, s.ctypes.data), "qw3_rope_table")
+    return c, s
 
 
 def _ptr(t):
@@ -172,9 +248,15 @@ class Model:
             sc = None if t.get("scales") is None else np.ascontiguousarray(t["scales"], dtype=np.float32)
             keep += [data, sc]
             rows, cols = (1, data.shape[0]) if data.ndim == 1 else data.shape
+            if t["dtype"] == DT_Q8_0:   # [rows, blocks * 34] bytes -> [rows, blocks * 32] inputs
+                cols = cols // 34 * 32
             arr[i] = Tensor(KIND[t["kind"]] if isinstance(t["kind"], str) else t["kind"], t.get("layer", -1),
                             t["dtype"], 0, rows, cols, data.ctypes.data, sc.ctypes.data if sc is not None else None)
         check(lib().qw3_load_weights(self.handle, arr, len(tensors), _stream(stream)), "qw3_load_weights")
+
+    def load_file(self, path, stream=None):
+        """Weights from a safetensors (bf16) or SLM2 (Q8_0 blocks + f32 norms) file."""
+        check(lib().qw3_load_file(self.handle, os.fsencode(path), _stream(stream)), "qw3_load_file")
 
     # -------------------------------------------------------------------------------- forward
     def prefill(self, tokens, seq=0, logits=None, argmax=None, stream=None):
@@ -215,7 +297,7 @@ class Model:
         return k, v
 
     def set_len(self, seq, n, stream=None):
-        check(lib().qw3_set_len(self.handle, seq, n, _stream(stream)), "qw3_set_len")
+        check(lib().qw3_kv_set_len(self.handle, seq, n, _stream(stream)), "qw3_kv_set_len")
 
     def dequant(self, kind, layer, rows, cols, stream=None):
         import torch

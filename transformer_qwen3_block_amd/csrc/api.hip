@@ -42,7 +42,8 @@ struct Model {
     uint64_t arena_bytes = 0;
     std::vector<int> len;       // host mirror of the committed lengths
     bool loaded = false;
-    bool poisoned = false;      // a numerical failure was observed by qw3_status_poll
+    bool poisoned = false;      // a latched device failure was observed by qw3_status_poll
+    int32_t poison_code = QW3_NUMERICAL_FAILURE;  // what every call reports while poisoned
     bool lens_dirty = false;    // host lengths changed without a device update yet
     bool status_dirty = false;  // device status word must be cleared
     // Replayable decode steps: one captured graph per (tokens, logits, argmax) pointer triple.
@@ -81,7 +82,8 @@ int32_t lookup(uint64_t h, Model **out) {
 int32_t validate(const qw3_config_t *c, Dims *d) {
     if (!c) return QW3_INVALID_ARGUMENT;
     if (c->abi_version != QW3_ABI_VERSION) return QW3_UNSUPPORTED_ABI;
-    if (c->weight_format != QW3_WEIGHTS_BF16 && c->weight_format != QW3_WEIGHTS_Q8)
+    if (c->weight_format != QW3_WEIGHTS_BF16 && c->weight_format != QW3_WEIGHTS_Q8 &&
+        c->weight_format != QW3_WEIGHTS_Q8_0)
         return QW3_UNSUPPORTED_QUANTIZATION;
     if (c->input_mode != QW3_INPUT_TOKENS && c->input_mode != QW3_INPUT_HIDDEN) return QW3_INVALID_ARGUMENT;
     if (c->hidden <= 0 || c->n_layers <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->intermediate <= 0 ||
@@ -94,7 +96,7 @@ int32_t validate(const qw3_config_t *c, Dims *d) {
     if (c->n_q_heads % c->n_kv_heads) return QW3_UNSUPPORTED_SHAPE;
     const int G = c->n_q_heads / c->n_kv_heads;
     if (G != 1 && G != 2 && G != 4) return QW3_UNSUPPORTED_SHAPE;
-    const bool q8 = c->weight_format == QW3_WEIGHTS_Q8;
+    const bool q8 = c->weight_format != QW3_WEIGHTS_BF16;  // Q8 and Q8_0 share the packed device layout
     // Q8 blocks of 32 need every contraction length to be a multiple of 32 ([P1] section 3, no tails);
     // the GEMV lane slicing needs multiples of 64 lanes x 16 bytes.
     const int unit = q8 ? 1024 : 512;
@@ -119,6 +121,7 @@ int32_t validate(const qw3_config_t *c, Dims *d) {
     d->q_dim = q_dim;
     d->Nqkv = (c->n_q_heads + 2 * c->n_kv_heads) * kHeadDim;
     d->q8 = q8;
+    d->q8_blocks = c->weight_format == QW3_WEIGHTS_Q8_0;
     d->hidden_mode = c->input_mode == QW3_INPUT_HIDDEN;
     d->mfma_prefill = !q8 && c->max_prefill > 1;
     d->eps = c->rms_eps;
@@ -233,7 +236,7 @@ inline int32_t dev(hipError_t e) { return e == hipSuccess ? QW3_OK : QW3_DEVICE_
     } while (0)
 #define QW3_HIP(expr) QW3_TRY(dev(expr))
 
-// Bring the device length array / status word in line with the host after reset_kv / set_len.
+// Bring the device length array / status word in line with the host after reset_kv / kv_set_len.
 int32_t sync_state(Model *m, hipStream_t st) {
     if (!m->lens_dirty && !m->status_dirty) return QW3_OK;
     QW3_HIP(launch_set_lens(at<int>(m, m->lay.len), m->d.S, m->len.data(), (1 << m->d.S) - 1, at<int>(m, m->lay.status),
@@ -254,7 +257,7 @@ bool is_matrix_kind(int k) {
 }
 
 Expect expected(const Dims &d, int kind) {
-    const int32_t mdt = d.q8 ? QW3_DT_Q8 : QW3_DT_BF16;
+    const int32_t mdt = d.q8_blocks ? QW3_DT_Q8_0 : (d.q8 ? QW3_DT_Q8 : QW3_DT_BF16);
     const int32_t ndt = d.q8 ? QW3_DT_F32 : QW3_DT_BF16;
     switch (kind) {
         case QW3_T_EMBED:
@@ -277,6 +280,25 @@ Expect expected(const Dims &d, int kind) {
 
 uint64_t elem_bytes(int32_t dt) { return dt == QW3_DT_F32 ? 4 : (dt == QW3_DT_BF16 ? 2 : 1); }
 
+// Bytes of a host tensor's data (a Q8_0 matrix: 34 bytes per 32 inputs).
+uint64_t data_bytes(const qw3_tensor_t &t) {
+    if (t.dtype == QW3_DT_Q8_0) return (uint64_t)t.rows * (uint64_t)(t.cols / 32) * 34;
+    return (uint64_t)t.rows * (uint64_t)t.cols * elem_bytes(t.dtype);
+}
+
+// f16 bits -> f32, exact (every binary16 value is an f32 value)
+float h16_to_f32_host(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// A Q8_0 block's f16 scale must be finite (a NaN or infinite scale would only surface later as a numerical
+// failure of every step reading that row).
+bool q8_0_scales_finite(const qw3_tensor_t &t) {
+    const uint8_t *b = (const uint8_t *)t.data;
+    const uint64_t n = (uint64_t)t.rows * (uint64_t)(t.cols / 32);
+    for (uint64_t i = 0; i < n; ++i)
+        if (((b[i * 34 + 1] << 8) & 0x7c00) == 0x7c00) return false;
+    return true;
+}
+
 // Host-side upload of a norm vector as f32 (bf16 widened exactly).
 int32_t upload_norm(Model *m, const qw3_tensor_t &t, uint64_t off, hipStream_t st, std::vector<std::vector<float>> &keep) {
     keep.emplace_back((size_t)t.cols);
@@ -295,6 +317,21 @@ int32_t upload_norm(Model *m, const qw3_tensor_t &t, uint64_t off, hipStream_t s
 
 int32_t upload_matrix(Model *m, const qw3_tensor_t &t, uint64_t w_off, uint64_t s_off, uint64_t row0, hipStream_t st) {
     const uint64_t eb = m->d.q8 ? 1 : 2;
+    if (t.dtype == QW3_DT_Q8_0) {
+        // the pages' interleaved blocks -> the packed layout: codes [rows][cols] and f32 scales [rows][cols/32]
+        const uint64_t nb = (uint64_t)t.cols / 32, n = (uint64_t)t.rows * nb;
+        std::vector<int8_t> codes((size_t)(n * 32));
+        std::vector<float> sc((size_t)n);
+        const uint8_t *b = (const uint8_t *)t.data;
+        for (uint64_t i = 0; i < n; ++i) {
+            sc[i] = h16_to_f32_host((uint16_t)(b[i * 34] | (b[i * 34 + 1] << 8)));
+            memcpy(&codes[i * 32], b + i * 34 + 2, 32);
+        }
+        QW3_HIP(hipMemcpyAsync(m->arena + w_off + row0 * (uint64_t)t.cols, codes.data(), codes.size(),
+                               hipMemcpyHostToDevice, st));
+        QW3_HIP(hipMemcpyAsync(m->arena + s_off + row0 * nb * 4, sc.data(), sc.size() * 4, hipMemcpyHostToDevice, st));
+        return dev(hipStreamSynchronize(st));  // the staging vectors die on return
+    }
     QW3_HIP(hipMemcpyAsync(m->arena + w_off + row0 * (uint64_t)t.cols * eb, t.data, (uint64_t)t.rows * t.cols * eb,
                            hipMemcpyHostToDevice, st));
     if (m->d.q8)
@@ -308,6 +345,22 @@ int32_t upload_matrix(Model *m, const qw3_tensor_t &t, uint64_t w_off, uint64_t 
 extern "C" {
 
 uint32_t qw3_abi_version(void) { return QW3_ABI_VERSION; }
+
+int32_t qw3_rope_table(double theta, int32_t head_dim, int32_t n_pos, float *cos_out, float *sin_out) {
+    if (!cos_out || !sin_out || head_dim < 2 || head_dim % 2 || n_pos < 0 || !(theta > 1.0) || !isfinite(theta))
+        return QW3_INVALID_ARGUMENT;
+    // angle pos * theta^(-2i/d) for pair i, evaluated in double; cos and sin rounded once to f32
+    const int half = head_dim / 2;
+    std::vector<double> inv(half);
+    for (int i = 0; i < half; ++i) inv[i] = pow(theta, -2.0 * (double)i / (double)head_dim);
+    for (int p = 0; p < n_pos; ++p)
+        for (int i = 0; i < half; ++i) {
+            const double ang = (double)p * inv[i];
+            cos_out[(size_t)p * half + i] = (float)cos(ang);
+            sin_out[(size_t)p * half + i] = (float)sin(ang);
+        }
+    return QW3_OK;
+}
 
 int32_t qw3_preflight(const qw3_config_t *cfg, qw3_sizes_t *out) {
     Dims d;
@@ -335,7 +388,8 @@ int32_t qw3_create(const qw3_config_t *cfg, void *arena_dev, uint64_t arena_byte
     const char *ng = getenv("QW3_NO_GRAPH");
     m->graphs_enabled = !(ng && ng[0] == '1');
     const char *nm = getenv("QW3_NO_MEGA");  // run single-sequence steps kernel by kernel
-    m->mega = mega_supported(d) && !(nm && nm[0] == '1');
+    // the single-launch decode needs its whole grid resident at once: checked against the current device
+    m->mega = mega_supported(d) && !(nm && nm[0] == '1') && mega_resident(d.q8, d.G);
     {
         // every product of a batched step must take the MFMA path, since the residual epilogues hand the
         // next RMSNorm its sums of squares
@@ -398,6 +452,7 @@ int32_t qw3_load_weights(uint64_t h, const qw3_tensor_t *t, int32_t n, void *str
         const Expect e = expected(d, x.kind);
         if (x.rows != e.rows || x.cols != e.cols || x.dtype != e.dtype || !x.data) return QW3_INVALID_MODEL;
         if (x.dtype == QW3_DT_Q8 && !x.scales) return QW3_INVALID_MODEL;
+        if (x.dtype == QW3_DT_Q8_0 && (x.scales || !q8_0_scales_finite(x))) return QW3_INVALID_MODEL;
     }
     if (!d.hidden_mode && (seen_global[QW3_T_EMBED] < 0 || seen_global[QW3_T_FINAL_NORM] < 0))
         return QW3_INVALID_MODEL;
@@ -407,9 +462,9 @@ int32_t qw3_load_weights(uint64_t h, const qw3_tensor_t *t, int32_t n, void *str
     if (!d.hidden_mode && seen_global[QW3_T_LM_HEAD] >= 0) {
         // tied: a shipped lm_head must be a byte-identical copy of the embedding ([P2] "Tied != absent")
         const qw3_tensor_t &e = t[seen_global[QW3_T_EMBED]], &lm = t[seen_global[QW3_T_LM_HEAD]];
-        const uint64_t bytes = (uint64_t)e.rows * e.cols * elem_bytes(e.dtype);
-        if (memcmp(e.data, lm.data, bytes)) return QW3_INVALID_MODEL;
-        if (d.q8 && memcmp(e.scales, lm.scales, (uint64_t)e.rows * (e.cols / 32) * 4)) return QW3_INVALID_MODEL;
+        if (memcmp(e.data, lm.data, data_bytes(e))) return QW3_INVALID_MODEL;
+        if (e.dtype == QW3_DT_Q8 && memcmp(e.scales, lm.scales, (uint64_t)e.rows * (e.cols / 32) * 4))
+            return QW3_INVALID_MODEL;
     }
     // ---- upload
     hipStream_t st = (hipStream_t)stream;
@@ -441,21 +496,13 @@ int32_t qw3_load_weights(uint64_t h, const qw3_tensor_t *t, int32_t n, void *str
             QW3_HIP(launch_bf16_to_f16(m->arena + b + L.l_wd, m->arena + b + L.l_wd16, (size_t)d.H * d.I, st));
         }
     }
-    // RoPE table: angle pos * theta^(-2i/d) for pair i, cos and sin in double rounded to f32
-    // ([P1] section 2 item 4; [P4] recommends packed RoPE tables over platform libm).
+    // RoPE table ([P1] section 2 item 4; [P4] recommends packed RoPE tables over platform libm)
     {
-        const int half = kHeadDim / 2;
-        std::vector<float> cs((size_t)d.max_ctx * half), sn((size_t)d.max_ctx * half);
-        std::vector<double> inv(half);
-        for (int i = 0; i < half; ++i) inv[i] = pow(m->cfg.rope_theta, -2.0 * (double)i / (double)kHeadDim);
-        for (int p = 0; p < d.max_ctx; ++p)
-            for (int i = 0; i < half; ++i) {
-                const double ang = (double)p * inv[i];
-                cs[(size_t)p * half + i] = (float)cos(ang);
-                sn[(size_t)p * half + i] = (float)sin(ang);
-            }
-        QW3_HIP(hipMemcpyAsync(m->arena + L.rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, st));
-        QW3_HIP(hipMemcpyAsync(m->arena + L.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, st));
+        const size_t n = (size_t)d.max_ctx * (kHeadDim / 2);
+        std::vector<float> cs(n), sn(n);
+        QW3_TRY(qw3_rope_table(m->cfg.rope_theta, kHeadDim, d.max_ctx, cs.data(), sn.data()));
+        QW3_HIP(hipMemcpyAsync(m->arena + L.rope_cos, cs.data(), n * 4, hipMemcpyHostToDevice, st));
+        QW3_HIP(hipMemcpyAsync(m->arena + L.rope_sin, sn.data(), n * 4, hipMemcpyHostToDevice, st));
         QW3_HIP(hipStreamSynchronize(st));
     }
     QW3_HIP(hipMemsetAsync(m->arena + L.kv_end, 0, L.state_end - L.kv_end, st));
@@ -478,6 +525,7 @@ int32_t qw3_reset_kv(uint64_t h, int32_t seq) {
     m->lens_dirty = true;
     m->status_dirty = true;
     m->poisoned = false;
+    m->poison_code = QW3_NUMERICAL_FAILURE;
     return QW3_OK;
 }
 
@@ -489,7 +537,7 @@ int32_t qw3_get_len(uint64_t h, int32_t seq, int32_t *len_out) {
     return QW3_OK;
 }
 
-int32_t qw3_set_len(uint64_t h, int32_t seq, int32_t len, void *stream) {
+int32_t qw3_kv_set_len(uint64_t h, int32_t seq, int32_t len, void *stream) {
     Model *m;
     QW3_TRY(lookup(h, &m));
     if (seq < 0 || seq >= m->d.S) return QW3_INVALID_ARGUMENT;
@@ -507,15 +555,20 @@ int32_t qw3_status_poll(uint64_t h, void *stream) {
     hipStream_t st = (hipStream_t)stream;
     QW3_TRY(sync_state(m, st));
     int status = 0;
+    std::vector<int> lens(m->d.S);
     QW3_HIP(hipMemcpyAsync(&status, m->arena + m->lay.status, 4, hipMemcpyDeviceToHost, st));
+    QW3_HIP(hipMemcpyAsync(lens.data(), m->arena + m->lay.len, sizeof(int) * lens.size(), hipMemcpyDeviceToHost, st));
     QW3_HIP(hipStreamSynchronize(st));
-    if (status & 1) m->poisoned = true;
-    if (status & 4) {  // a bounded device wait timed out (single-launch decode or prefill attention pairing)
+    if (status) {
+        // The failing step and every step after it committed nothing on the device: the host mirror takes
+        // the device's committed lengths, and the handle refuses further work until qw3_reset_kv.
         m->poisoned = true;
-        return QW3_DEVICE_ERROR;
+        m->len = lens;
+        if (status & kStatusTimeout) m->poison_code = QW3_DEVICE_ERROR;        // a bounded device wait gave up
+        else if (status & (kStatusNonFinite | kStatusF16Range)) m->poison_code = QW3_NUMERICAL_FAILURE;
+        else m->poison_code = QW3_INVALID_ARGUMENT;                            // a token outside [0, vocab)
     }
-    if (status & 2) return QW3_INVALID_ARGUMENT;  // a token id outside [0, vocab) reached the device
-    return m->poisoned ? QW3_NUMERICAL_FAILURE : QW3_OK;
+    return m->poisoned ? m->poison_code : QW3_OK;
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -721,7 +774,7 @@ static int32_t run_logits(Model *m, int seq0, int S, const float *xin, float *lo
 
 static int32_t check_ready(Model *m) {
     if (!m->loaded) return QW3_INVALID_ARGUMENT;
-    if (m->poisoned) return QW3_NUMERICAL_FAILURE;
+    if (m->poisoned) return m->poison_code;
     return QW3_OK;
 }
 
@@ -784,6 +837,45 @@ int32_t qw3_decode_step(uint64_t h, const int32_t *tokens_dev, float *logits_dev
     return QW3_OK;
 }
 
+// Enqueues the whole prefill of n_tokens tokens of `seq`; the caller advances the host length on success.
+static int32_t enqueue_prefill(Model *m, int32_t seq, const int32_t *tokens_dev, int32_t n_tokens, float *logits,
+                               int32_t *argmax, hipStream_t st) {
+    const Dims &d = m->d;
+    const Layout &L = m->lay;
+    if (d.mfma_prefill) {
+        // tiled bf16 prefill on MFMA, tile by tile ([P4] "Prefill versus decode")
+        for (int t0 = 0; t0 < n_tokens; t0 += d.max_prefill) {
+            const int T = n_tokens - t0 < d.max_prefill ? n_tokens - t0 : d.max_prefill;
+            const bool last = t0 + T == n_tokens;
+            QW3_HIP(launch_embed(false, m->arena + L.embed, nullptr, d.H, tokens_dev + t0, T, at<float>(m, L.x),
+                                 at<int>(m, L.status), d.V, st));
+            QW3_TRY(prefill_layers(m->arena, L, d, seq, m->len[seq] + t0, T, st));
+            if (last) {
+                QW3_TRY(run_logits(m, seq, 1, at<float>(m, L.x) + (size_t)(T - 1) * d.H, logits, argmax, T, st));
+            } else {
+                QW3_HIP(launch_commit(at<int>(m, L.len) + seq, 1, T, at<int>(m, L.status), st));
+            }
+        }
+        return QW3_OK;
+    }
+    // Q8 models, and bf16 models configured with single-token tiles: token by token through the decode kernels
+    // (only the last position computes logits)
+    for (int t = 0; t < n_tokens; ++t) {
+        if (m->mega) {
+            QW3_TRY(run_layers_mega(m, seq, tokens_dev + t, nullptr, at<float>(m, L.x), st));
+        } else {
+            QW3_HIP(launch_embed(d.q8, m->arena + L.embed, d.q8 ? at<float>(m, L.embed_scales) : nullptr, d.H,
+                                 tokens_dev + t, 1, at<float>(m, L.x), at<int>(m, L.status), d.V, st));
+            QW3_TRY(run_layers_decode(m, seq, 1, st));
+        }
+        if (t == n_tokens - 1)
+            QW3_TRY(run_logits(m, seq, 1, at<float>(m, L.x), logits, argmax, 1, st));
+        else
+            QW3_HIP(launch_commit(at<int>(m, L.len) + seq, 1, 1, at<int>(m, L.status), st));
+    }
+    return QW3_OK;
+}
+
 int32_t qw3_prefill(uint64_t h, int32_t seq, const int32_t *tokens_dev, int32_t n_tokens, float *logits_dev,
                     int32_t *argmax_dev, void *stream) {
     Model *m;
@@ -797,37 +889,50 @@ int32_t qw3_prefill(uint64_t h, int32_t seq, const int32_t *tokens_dev, int32_t 
     const Layout &L = m->lay;
     int *argmax = argmax_dev ? argmax_dev : at<int>(m, L.tokens);
     float *logits = logits_dev ? logits_dev : at<float>(m, L.logits);
-    if (!d.q8) {
-        // tiled bf16 prefill on MFMA, tile by tile ([P4] "Prefill versus decode")
-        for (int t0 = 0; t0 < n_tokens; t0 += d.max_prefill) {
-            const int T = n_tokens - t0 < d.max_prefill ? n_tokens - t0 : d.max_prefill;
-            const bool last = t0 + T == n_tokens;
-            QW3_HIP(launch_embed(false, m->arena + L.embed, nullptr, d.H, tokens_dev + t0, T, at<float>(m, L.x),
-                                 at<int>(m, L.status), d.V, st));
-            QW3_TRY(prefill_layers(m->arena, L, d, seq, m->len[seq] + t0, T, st));
-            if (last) {
-                QW3_TRY(run_logits(m, seq, 1, at<float>(m, L.x) + (size_t)(T - 1) * d.H, logits, argmax, T, st));
-            } else {
-                QW3_HIP(launch_commit(at<int>(m, L.len) + seq, 1, T, st));
-            }
-        }
-    } else {
-        // Q8: token by token through the decode kernels (only the last position computes logits)
-        for (int t = 0; t < n_tokens; ++t) {
-            if (m->mega) {
-                QW3_TRY(run_layers_mega(m, seq, tokens_dev + t, nullptr, at<float>(m, L.x), st));
-            } else {
-                QW3_HIP(launch_embed(true, m->arena + L.embed, at<float>(m, L.embed_scales), d.H, tokens_dev + t, 1,
-                                     at<float>(m, L.x), at<int>(m, L.status), d.V, st));
-                QW3_TRY(run_layers_decode(m, seq, 1, st));
-            }
-            if (t == n_tokens - 1)
-                QW3_TRY(run_logits(m, seq, 1, at<float>(m, L.x), logits, argmax, 1, st));
-            else
-                QW3_HIP(launch_commit(at<int>(m, L.len) + seq, 1, 1, st));
-        }
+    const int32_t rc = enqueue_prefill(m, seq, tokens_dev, n_tokens, logits, argmax, st);
+    if (rc != QW3_OK) {
+        // a launch failed part way: earlier chunks may have committed on the device, so the next call first
+        // puts the device lengths back to the host's (the failed prefill commits nothing)
+        m->lens_dirty = true;
+        return rc;
     }
     m->len[seq] += n_tokens;
+    return QW3_OK;
+}
+
+// Enqueues the layer stack over n_tokens caller hidden states of sequence 0 (qw3_block_forward).
+static int32_t enqueue_block_forward(Model *m, const float *hidden_in_dev, int32_t n_tokens, float *hidden_out_dev,
+                                     hipStream_t st) {
+    const Dims &d = m->d;
+    const Layout &L = m->lay;
+    float *x = at<float>(m, L.x);
+    for (int t0 = 0; t0 < n_tokens; t0 += d.max_prefill) {
+        const int T = n_tokens - t0 < d.max_prefill ? n_tokens - t0 : d.max_prefill;
+        if (!(m->mega && (T == 1 || d.q8)))
+            QW3_HIP(hipMemcpyAsync(x, hidden_in_dev + (size_t)t0 * d.H, (size_t)T * d.H * 4, hipMemcpyDeviceToDevice,
+                                   st));
+        if (m->mega && (T == 1 || d.q8)) {
+            for (int t = 0; t < T; ++t) {
+                QW3_TRY(run_layers_mega(m, 0, nullptr, hidden_in_dev + (size_t)(t0 + t) * d.H,
+                                        hidden_out_dev + (size_t)(t0 + t) * d.H, st));
+                QW3_HIP(launch_commit(at<int>(m, L.len), 1, 1, at<int>(m, L.status), st));
+            }
+        } else if (T == 1 || d.q8) {
+            for (int t = 0; t < T; ++t) {
+                if (t) QW3_HIP(hipMemcpyAsync(x, hidden_in_dev + (size_t)(t0 + t) * d.H, (size_t)d.H * 4,
+                                              hipMemcpyDeviceToDevice, st));
+                QW3_TRY(run_layers_decode(m, 0, 1, st));
+                QW3_HIP(launch_commit(at<int>(m, L.len), 1, 1, at<int>(m, L.status), st));
+                QW3_HIP(hipMemcpyAsync(hidden_out_dev + (size_t)(t0 + t) * d.H, x, (size_t)d.H * 4,
+                                       hipMemcpyDeviceToDevice, st));
+            }
+        } else {
+            QW3_TRY(prefill_layers(m->arena, L, d, 0, m->len[0] + t0, T, st));
+            QW3_HIP(launch_commit(at<int>(m, L.len), 1, T, at<int>(m, L.status), st));
+            QW3_HIP(hipMemcpyAsync(hidden_out_dev + (size_t)t0 * d.H, x, (size_t)T * d.H * 4, hipMemcpyDeviceToDevice,
+                                   st));
+        }
+    }
     return QW3_OK;
 }
 
@@ -841,34 +946,10 @@ int32_t qw3_block_forward(uint64_t h, const float *hidden_in_dev, int32_t n_toke
     if ((int64_t)m->len[0] + n_tokens > d.max_ctx) return QW3_CONTEXT_EXCEEDED;
     hipStream_t st = (hipStream_t)stream;
     QW3_TRY(sync_state(m, st));
-    const Layout &L = m->lay;
-    float *x = at<float>(m, L.x);
-    for (int t0 = 0; t0 < n_tokens; t0 += d.max_prefill) {
-        const int T = n_tokens - t0 < d.max_prefill ? n_tokens - t0 : d.max_prefill;
-        if (!(m->mega && (T == 1 || d.q8)))
-            QW3_HIP(hipMemcpyAsync(x, hidden_in_dev + (size_t)t0 * d.H, (size_t)T * d.H * 4, hipMemcpyDeviceToDevice,
-                                   st));
-        if (m->mega && (T == 1 || d.q8)) {
-            for (int t = 0; t < T; ++t) {
-                QW3_TRY(run_layers_mega(m, 0, nullptr, hidden_in_dev + (size_t)(t0 + t) * d.H,
-                                        hidden_out_dev + (size_t)(t0 + t) * d.H, st));
-                QW3_HIP(launch_commit(at<int>(m, L.len), 1, 1, st));
-            }
-        } else if (T == 1 || d.q8) {
-            for (int t = 0; t < T; ++t) {
-                if (t) QW3_HIP(hipMemcpyAsync(x, hidden_in_dev + (size_t)(t0 + t) * d.H, (size_t)d.H * 4,
-                                              hipMemcpyDeviceToDevice, st));
-                QW3_TRY(run_layers_decode(m, 0, 1, st));
-                QW3_HIP(launch_commit(at<int>(m, L.len), 1, 1, st));
-                QW3_HIP(hipMemcpyAsync(hidden_out_dev + (size_t)(t0 + t) * d.H, x, (size_t)d.H * 4,
-                                       hipMemcpyDeviceToDevice, st));
-            }
-        } else {
-            QW3_TRY(prefill_layers(m->arena, L, d, 0, m->len[0] + t0, T, st));
-            QW3_HIP(launch_commit(at<int>(m, L.len), 1, T, st));
-            QW3_HIP(hipMemcpyAsync(hidden_out_dev + (size_t)t0 * d.H, x, (size_t)T * d.H * 4, hipMemcpyDeviceToDevice,
-                                   st));
-        }
+    const int32_t rc = enqueue_block_forward(m, hidden_in_dev, n_tokens, hidden_out_dev, st);
+    if (rc != QW3_OK) {
+        m->lens_dirty = true;  // as in qw3_prefill: the failed call commits nothing
+        return rc;
     }
     m->len[0] += n_tokens;
     return QW3_OK;

@@ -14,6 +14,11 @@ constexpr int kPartStride = 2 + kHeadDim;  // per split partial: running max, ru
 constexpr int kLmMaxBlocks = 16384;    // upper bound on lm_head workgroups (argmax partials)
 constexpr int kMegaGrid = 256;         // resident workgroups of the single-launch decode kernel
 constexpr int kMegaWaves = 4;          // its waves per workgroup
+// Bits of the device status word (zeroed at load and by qw3_reset_kv).  Any set bit stops every later commit.
+constexpr int kStatusNonFinite = 1;    // a logit was NaN or infinite
+constexpr int kStatusBadToken = 2;     // a token id outside [0, vocab) reached the device (row 0 was used)
+constexpr int kStatusTimeout = 4;      // a bounded cross-workgroup wait gave up
+constexpr int kStatusF16Range = 8;     // a cached key or value overflowed the f16 range of the prefill attention
 // The single-launch decode kernel's all-gathered exchange words (hidden rows, attention output, activations)
 // sit 16 to a 128-byte line, with consecutive lines kXwLine words (1 KiB) apart: measured on gfx950, packing
 // those lines densely (each line written from four XCDs and polled by every workgroup) made the layer stack
@@ -54,7 +59,8 @@ struct Dims {
     int H, L, HQ, HKV, G, I, V, S, max_ctx, max_prefill;
     int Nqkv;        // (HQ + 2*HKV) * 128
     int q_dim;       // HQ * 128
-    bool q8;
+    bool q8;            // int8 codes + f32 scales on the device (Q8 and Q8_0 formats)
+    bool q8_blocks;     // matrices arrive as Q8_0 34-byte blocks (f16 scale), split by the packer
     bool hidden_mode;
     bool mfma_prefill;  // bf16 weights and multi-token tiles: f16 weight copies exist
     float eps;
@@ -166,7 +172,7 @@ bool gemv_mfma_supported(const GemvArgs &a, GemvEpi epi);
 hipError_t launch_gemv_mfma(GemvEpi epi, const GemvArgs &a, hipStream_t st);
 hipError_t launch_ssq_prep(const float *x, int ldx, int S, int K, float *ssq, hipStream_t st);
 hipError_t launch_argmax_finalize(const float *argpart, int nparts, int S, int *argmax_out, int *len, int commit_add,
-                                  hipStream_t st);
+                                  const int *status, hipStream_t st);
 
 struct AttnDecodeArgs {
     const float *qkv;       // raw projections [S][ldqkv]
@@ -208,13 +214,42 @@ struct MegaArgs {
     float eps;
 };
 bool mega_supported(const Dims &d);
+bool mega_resident(bool q8, int G);
 hipError_t launch_decode_mega(bool q8, int G, const MegaArgs &a, hipStream_t st);
+
+// Deterministic sampling (sample.hip): vocabulary slices of the chunk kernel, bounds of the C ABI.
+constexpr int kSampleChunks = 16;
+constexpr int kSampleMaxTopK = QW3_SAMPLE_MAX_TOP_K;
+constexpr int kSampleMaxVocab = QW3_SAMPLE_MAX_VOCAB;
+constexpr int kSampleMaxRows = QW3_SAMPLE_MAX_ROWS;
+constexpr int kSampleMaxStop = QW3_SAMPLE_MAX_STOP;
+struct SampleArgs {
+    const float *logits;    // [rows][ld]
+    long long ld;
+    int V, rows;
+    float temperature, top_p, penalty;
+    int top_k;              // 1 when temperature == 0 (greedy)
+    const int *history;     // [rows][n_history]
+    int n_history;
+    const int *forbid;      // [n_forbid]
+    int n_forbid;
+    int stop[kSampleMaxStop];
+    int n_stop;
+    uint64_t *rng;          // [rows][2]: PCG32 state, increment
+    int *token_out, *done_out, *status_out;
+    // scratch (sample_bind_scratch): per (row, chunk) candidates, counts and +inf flags
+    uint32_t *cand_key;
+    int *cand_id, *cand_cnt, *chunk_bad;
+};
+uint64_t sample_scratch_bytes(int rows);
+void sample_bind_scratch(SampleArgs &a, void *scratch);
+hipError_t launch_sample(const SampleArgs &a, hipStream_t st);
 
 hipError_t launch_embed(bool q8, const void *table, const float *scales, int H, const int *tokens, int S, float *x,
                         int *status, int vocab, hipStream_t st);
 hipError_t launch_set_lens(int *len_dev, int n, const int *vals, int mask, int *status, int clear_status,
                            uint32_t *epoch, hipStream_t st);
-hipError_t launch_commit(int *len_dev, int n, int add, hipStream_t st);
+hipError_t launch_commit(int *len_dev, int n, int add, const int *status, hipStream_t st);
 hipError_t launch_dequant(bool q8, const void *w, const float *scales, long long rows, int cols, float *out,
                           hipStream_t st);
 

@@ -312,7 +312,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a, int KC) {
                 }
             }
         }
-        if (lane == 0 && my_bad) atomicOr(a.status, 1);
+        if (lane == 0 && my_bad) atomicOr(a.status, kStatusNonFinite);
         __syncthreads();
         if (tid < S) {
             float b = -INFINITY;
@@ -333,9 +333,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a, int KC) {
 }
 
 // Final greedy choice over the logits workgroups' partials (fixed order: lowest index wins ties), then the
-// commit of the appended positions ([P4] "Cancellation": positions become valid only after the step).
+// commit of the appended positions ([P4] "Cancellation": positions become valid only after the step).  A step
+// that latched any failure in the status word (a non-finite logit, a token outside the vocabulary, a device
+// wait that gave up) commits nothing, and neither does any later step until the handle is reset ([P1] section
+// 4 "NaN/Inf Rejection": the generation loop stops at the failing step; section 8: completed steps stand).
 __global__ __launch_bounds__(256) void argmax_finalize_kernel(const float *argpart, int nparts, int S, int *argmax_out,
-                                                              int *len, int commit_add) {
+                                                              int *len, int commit_add, const int *status) {
     __shared__ float bv[4];
     __shared__ int bi[4];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const float *argpa
                 }
             // all logits NaN: no index qualifies; report 0 (the status word carries the failure)
             if (argmax_out) argmax_out[s] = bi[0] == 0x7fffffff ? 0 : bi[0];
-            if (len) len[s] += commit_add;
+            if (len && *status == 0) len[s] += commit_add;
         }
         __syncthreads();
     }
@@ -456,7 +459,7 @@ hipError_t gemv_dispatch(const GemvArgs &a, hipStream_t st) {
                             : gemv_launch_r<Q8, kMaxSeq, EPI>(R, KS, grid, a, KC, lds, st);
     if (e != hipSuccess || EPI != EPI_LOGITS) return e;
     hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(256), 0, st, a.argpart, grid, a.S, a.argmax_out, a.len,
-                       a.commit_add);
+                       a.commit_add, (const int *)a.status);
     return hipGetLastError();
 }
 
@@ -746,7 +749,7 @@ __global__ void embed_kernel(const void *table, const float *scales, int H, cons
     const int k = blockIdx.x * blockDim.x + threadIdx.x;
     int tok = tokens[s];
     if (tok < 0 || tok >= vocab) {
-        if (k == 0) atomicOr(status, 2);
+        if (k == 0) atomicOr(status, kStatusBadToken);
         tok = 0;
     }
     if (k >= H) return;
@@ -775,9 +778,11 @@ __global__ void set_lens_kernel(int *len, int n, LenVals vals, int mask, int *st
     }
 }
 
-__global__ void commit_kernel(int *len, int n, int add) {
+// Commit of positions appended without a logits step (earlier prefill chunks, hidden-state steps); like the
+// final commit, nothing is committed once the status word holds a failure.
+__global__ void commit_kernel(int *len, int n, int add, const int *status) {
     const int t = threadIdx.x;
-    if (t < n) len[t] += add;
+    if (t < n && *status == 0) len[t] += add;
 }
 
 template <int Q8>
@@ -794,9 +799,9 @@ __global__ void dequant_kernel(const void *w, const float *scales, long long tot
 }  // namespace
 
 hipError_t launch_argmax_finalize(const float *argpart, int nparts, int S, int *argmax_out, int *len, int commit_add,
-                                  hipStream_t st) {
+                                  const int *status, hipStream_t st) {
     hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(256), 0, st, argpart, nparts, S, argmax_out, len,
-                       commit_add);
+                       commit_add, status);
     return hipGetLastError();
 }
 
@@ -851,8 +856,8 @@ hipError_t launch_set_lens(int *len_dev, int n, const int *vals, int mask, int *
     return hipGetLastError();
 }
 
-hipError_t launch_commit(int *len_dev, int n, int add, hipStream_t st) {
-    hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(64), 0, st, len_dev, n, add);
+hipError_t launch_commit(int *len_dev, int n, int add, const int *status, hipStream_t st) {
+    hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(64), 0, st, len_dev, n, add, status);
     return hipGetLastError();
 }
 

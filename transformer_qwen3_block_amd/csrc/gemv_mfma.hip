@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
                     besti = oi;
                 }
             }
-            if (bad) atomicOr(a.status, 1);
+            if (bad) atomicOr(a.status, kStatusNonFinite);
             if (er == 0 && es < S) {
                 float *p = a.argpart + ((size_t)es * gridDim.x + blockIdx.x) * 2;
                 p[0] = best;
@@ -369,7 +369,7 @@ hipError_t launch_gemv_mfma(GemvEpi epi, const GemvArgs &a, hipStream_t st) {
             hipLaunchKernelGGL((gemv_mfma_kernel<4, 8, EPI_LOGITS>), dim3(grid), dim3(256), 0, st, a);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            return launch_argmax_finalize(a.argpart, grid, a.S, a.argmax_out, a.len, a.commit_add, st);
+            return launch_argmax_finalize(a.argpart, grid, a.S, a.argmax_out, a.len, a.commit_add, a.status, st);
         }
     }
     return hipGetLastError();

@@ -37,7 +37,6 @@ constexpr int kHid = 1024;               // hidden size of this kernel (= kNW: o
 // Poll bound: rounds of device-coherent loads (each at least one memory round trip, well over 0.25 us), so
 // 2^18 rounds outlast 50 ms while a legitimate wait lasts microseconds.
 constexpr int kPollRounds = 1 << 18;
-constexpr int kStatusTimeout = 4;
 constexpr int kMegaBuf = 3072;  // floats per LDS input buffer (largest phase input: intermediate <= 3072)
 
 static_assert(kHid == kNW, "one hidden row per wave");
@@ -445,7 +444,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (a.token) {
         int tok = a.token[0];
         if (tok < 0 || tok >= a.V) {
-            if (b == 0 && tid == 0) atomicOr(a.status, 2);
+            if (b == 0 && tid == 0) atomicOr(a.status, kStatusBadToken);
             tok = 0;
         }
         for (int k = tid; k < kHid; k += 256) {
@@ -744,6 +743,34 @@ bool mega_supported(const Dims &d) {
     if (d.I > 3 * kNW || d.I % (d.q8 ? 1024 : 512)) return false;
     if (d.q_dim % (d.q8 ? 1024 : 512)) return false;
     return true;
+}
+
+// The persistent grid must be resident all at once: every workgroup waits for the others' outputs.  True when
+// the current device holds at least kMegaGrid of these workgroups at one time (compute units times the
+// occupancy the kernel's registers and LDS allow).  A device that cannot (fewer compute units, a partitioned
+// GPU) takes the kernel-by-kernel path instead.
+bool mega_resident(bool q8, int G) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+    const void *fn = nullptr;
+#define QW3_MEGA_FN(Q, GG) fn = reinterpret_cast<const void *>(&decode_mega_kernel<Q, GG>)
+    if (q8) {
+        if (G == 1) QW3_MEGA_FN(1, 1);
+        else if (G == 2) QW3_MEGA_FN(1, 2);
+        else if (G == 4) QW3_MEGA_FN(1, 4);
+    } else {
+        if (G == 1) QW3_MEGA_FN(0, 1);
+        else if (G == 2) QW3_MEGA_FN(0, 2);
+        else if (G == 4) QW3_MEGA_FN(0, 4);
+    }
+#undef QW3_MEGA_FN
+    if (!fn) return false;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kMegaWaves * 64, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return (long long)per_cu * cus >= kMegaGrid;
 }
 
 hipError_t launch_decode_mega(bool q8, int G, const MegaArgs &a, hipStream_t st) {

@@ -4,7 +4,9 @@
 // projection (bf16 -> f16 is exact for |w| >= 2^-14), activations are rounded to f16 (11-bit significand,
 // eight times finer than bf16), and the bf16 K/V cache is widened to f16 while it is staged in LDS.  The
 // residual stream stays f32.  An activation beyond the f16 range becomes infinite and reaches the logits,
-// where the non-finite check latches a numerical failure.
+// where the non-finite check latches a numerical failure; a cached key or value beyond it (the attention's
+// f16 shadow of the bf16 cache) latches kStatusF16Range where it is converted, since a key converted to
+// infinity could otherwise leave the softmax with a zero weight instead of a non-finite result.
 //
 // MFMA v_mfma_f32_16x16x32_f16 lane layout (wave64): lane l supplies A[l%16][8*(l/16)+e] and
 // B[8*(l/16)+e][l%16] (e = 0..7) and receives C[4*(l/16)+r][l%16] (r = 0..3).
@@ -165,6 +167,7 @@ struct GemmArgs {
     // written for the chunk's positions from the same staged tile; null: left to kv16_convert_kernel
     uint16_t *ks16, *vt16;
     int ps;
+    int *status;        // kStatusF16Range is latched when a shadow value overflows the f16 range
 };
 
 __host__ __device__ inline int kv16_stride(int max_ctx) { return (max_ctx + 63) & ~63; }
@@ -174,6 +177,12 @@ __device__ __forceinline__ int vt_perm(int p) {
     return (p & ~31) + 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);
 }
 __device__ __forceinline__ uint32_t bf16x2_to_h16x2(uint32_t w) { return pack_h16x2(bf16_lo(w), bf16_hi(w)); }
+// A packed f16 pair holding an infinity or NaN (exponent all ones).  The bf16 cache keeps keys and values beyond
+// 65504, their f16 shadow does not: a key there would score +-inf and could silently drop out of the softmax,
+// so every shadow write checks its values and latches kStatusF16Range instead.
+__device__ __forceinline__ bool h16x2_nonfinite(uint32_t w) {
+    return (w & 0x7c00u) == 0x7c00u || (w & 0x7c000000u) == 0x7c000000u;
+}
 
 constexpr int kBK = 64;
 constexpr int kLdsPad = 16;  // 16-bit elements of padding per LDS row (32 bytes: measured fastest of 0, 8, 16, 24, 32)
@@ -440,9 +449,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
                                 : g.vc + ((size_t)(h - g.HQ - g.HKV) * g.max_ctx + g.pos0 + m) * kHeadDim + d;
             const uint4 v = *(const uint4 *)(otile + row * OLD + cc);
             *(uint4 *)dst = v;
-            if (g.ks16 && h >= g.HQ && h < g.HQ + g.HKV)  // the key row's f16 shadow (exact: bf16 values in range)
-                *(uint4 *)(g.ks16 + ((size_t)(h - g.HQ) * g.ps + g.pos0 + m) * kHeadDim + d) =
+            if (g.ks16 && h >= g.HQ && h < g.HQ + g.HKV) {  // the key row's f16 shadow (exact: bf16 values in range)
+                const uint4 hv =
                     make_uint4(bf16x2_to_h16x2(v.x), bf16x2_to_h16x2(v.y), bf16x2_to_h16x2(v.z), bf16x2_to_h16x2(v.w));
+                *(uint4 *)(g.ks16 + ((size_t)(h - g.HQ) * g.ps + g.pos0 + m) * kHeadDim + d) = hv;
+                if (h16x2_nonfinite(hv.x) || h16x2_nonfinite(hv.y) || h16x2_nonfinite(hv.z) || h16x2_nonfinite(hv.w))
+                    atomicOr(g.status, kStatusF16Range);
+            }
         }
         // V^T shadow of the tile's value heads: 16-byte chunks of 8 key slots of a 32-position group (the
         // tile's rows start at a multiple of 64 positions); rows past the chunk's last position up to the next
@@ -466,6 +479,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
                     }
                     pk[e] = pack_h16x2(f2[0], f2[1]);
                 }
+                if (h16x2_nonfinite(pk[0]) || h16x2_nonfinite(pk[1]) || h16x2_nonfinite(pk[2]) || h16x2_nonfinite(pk[3]))
+                    atomicOr(g.status, kStatusF16Range);
                 *(uint4 *)(g.vt16 + ((size_t)(h - g.HQ - g.HKV) * kHeadDim + dim) * g.ps + g.pos0 + m0 + 8 * sg) =
                     make_uint4(pk[0], pk[1], pk[2], pk[3]);
             }
@@ -545,7 +560,7 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
 // in place of their layout, V goes through LDS to be written as 128-byte V^T rows.  Positions past n in the
 // last tile get zero V.
 __global__ __launch_bounds__(256) void kv16_convert_kernel(const uint16_t *kc, const uint16_t *vc, int max_ctx,
-                                                           int n, uint16_t *ks16, uint16_t *vt16) {
+                                                           int n, uint16_t *ks16, uint16_t *vt16, int *status) {
     __shared__ __attribute__((aligned(16))) uint16_t t[kHeadDim][64 + 8];
     const int p0 = blockIdx.x * 64, hk = blockIdx.y, tid = threadIdx.x;
     const int ps = kv16_stride(max_ctx);
@@ -561,6 +576,10 @@ __global__ __launch_bounds__(256) void kv16_convert_kernel(const uint16_t *kc, c
                 kw[e] = pack_h16x2(bf16_lo(kr[e]), bf16_hi(kr[e]));
                 vw[e] = pack_h16x2(bf16_lo(vr[e]), bf16_hi(vr[e]));
             }
+            bool bad = false;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bad = bad || h16x2_nonfinite(kw[e]) || h16x2_nonfinite(vw[e]);
+            if (bad) atomicOr(status, kStatusF16Range);
             *(uint4 *)(ks16 + ((size_t)hk * ps + p) * kHeadDim + d8) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
         }
         const int pp = vt_perm(key);
@@ -665,7 +684,6 @@ struct AttnPrefillArgs {
 };
 constexpr int kPfState = 34;              // per thread: m, l, then o[32]
 constexpr unsigned kPfEmpty = 0xffffffffu;  // slot word not yet published
-constexpr int kPfStatusTimeout = 4;
 constexpr int kPfSpin = 1 << 20;          // polling rounds before giving up (far beyond any legitimate wait)
 
 __device__ __forceinline__ void pf_put(unsigned *p, float v) {
@@ -918,7 +936,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
                 o[i + 1][r] = comb(o[i + 1][r], w8[4 + r]);
             }
         }
-        if (!ok) atomicOr(a.status, kPfStatusTimeout);
+        if (!ok) atomicOr(a.status, kStatusTimeout);
     }
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
@@ -998,6 +1016,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
     const size_t seq_stride = (size_t)d.L * d.HKV * d.max_ctx * kHeadDim;
     uint16_t *ks16 = (uint16_t *)(arena + L.kv16);
     uint16_t *vt16 = ks16 + (size_t)d.HKV * kv16_stride(d.max_ctx) * kHeadDim;
+    int *status = (int *)(arena + L.status);
     for (int l = 0; l < d.L; ++l) {
         const uint64_t b = L.layer0 + (uint64_t)l * L.layer_stride;
         const uint16_t *wqkv = (const uint16_t *)(arena + b + L.l_wqkv16);
@@ -1025,7 +1044,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         const bool fused_shadow = fused && pos0 % 64 == 0;
         if (fused_shadow && pos0 > 0)
             hipLaunchKernelGGL(kv16_convert_kernel, dim3(pos0 / 64, d.HKV), dim3(256), 0, st, kc, vc, d.max_ctx, pos0,
-                               ks16, vt16);
+                               ks16, vt16, status);
         if (fused) {
             g.q_norm = (const float *)(arena + b + L.l_q_norm);
             g.k_norm = (const float *)(arena + b + L.l_k_norm);
@@ -1042,6 +1061,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
             g.ks16 = fused_shadow ? ks16 : nullptr;
             g.vt16 = fused_shadow ? vt16 : nullptr;
             g.ps = kv16_stride(d.max_ctx);
+            g.status = status;
             QW3_PF_TRY(launch_gemm<G_QKNORM>(g, st));
         } else {
             QW3_PF_TRY(launch_gemm<G_STORE16>(g, st));
@@ -1052,7 +1072,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         // every cached position of this layer (earlier chunks and the new one) into the f16 shadow
         if (!fused_shadow)
             hipLaunchKernelGGL(kv16_convert_kernel, dim3((pos0 + T + 63) / 64, d.HKV), dim3(256), 0, st, kc, vc,
-                               d.max_ctx, pos0 + T, ks16, vt16);
+                               d.max_ctx, pos0 + T, ks16, vt16, status);
         AttnPrefillArgs at{};
         at.q16 = q16;
         at.ks16 = ks16;
@@ -1065,7 +1085,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         at.out16 = attn16;
         at.part = (unsigned *)(arena + L.pf_part);
         at.cnt = (unsigned *)(arena + L.pf_cnt);
-        at.status = (int *)(arena + L.status);
+        at.status = status;
         QW3_PF_TRY(launch_attn_prefill(d.G, at, st));
         g.A = attn16;
         g.W = wo;
