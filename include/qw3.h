@@ -311,6 +311,21 @@ int32_t qw3_sample(const float *logits_dev, int32_t n_rows, int32_t vocab, int64
                    uint64_t *rng_dev, int32_t *token_out_dev, int32_t *done_out_dev, int32_t *status_out_dev,
                    void *workspace_dev, uint64_t workspace_bytes, void *stream);
 
+/* qw3_sample for callers that cannot allocate device memory -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc: the same arguments and results without the workspace.  Its scratch
+ * (2,099,200 bytes, enough for QW3_SAMPLE_MAX_ROWS rows of any supported vocabulary) is a device array inside
+ * the library, one per GPU, held until the process ends; the call itself allocates nothing.  Requests beyond
+ * QW3_SAMPLE_MAX_ROWS rows or QW3_SAMPLE_MAX_VOCAB tokens are rejected with QW3_INVALID_ARGUMENT.  Every call
+ * on a GPU uses that GPU's one array, so calls that overlap on one GPU (different streams, or host threads
+ * without ordering) race and must not be issued; calls ordered on one stream are safe.  Nothing in the array
+ * needs clearing between calls: each call writes every word it reads.  QW3_DEVICE_ERROR if the array's device
+ * address cannot be obtained. */
+int32_t qw3_sample_noalloc(const float *logits_dev, int32_t n_rows, int32_t vocab, int64_t ld_logits,
+                           const qw3_sample_params_t *params, const int32_t *history_dev, int32_t n_history,
+                           const int32_t *forbid_dev, int32_t n_forbid, const int32_t *stop_ids, int32_t n_stop,
+                           uint64_t *rng_dev, int32_t *token_out_dev, int32_t *done_out_dev, int32_t *status_out_dev,
+                           void *stream);
+
 /* ---- test and benchmark hooks (not part of the serving path) ------------------------------------- */
 
 /* Layer stack on caller hidden states (input_mode QW3_INPUT_HIDDEN, sequence 0): hidden_in_dev f32

@@ -75,7 +75,8 @@ class Tensor(ctypes.Structure):
 EXPORTS = ["qw3_abi_version", "qw3_rope_table", "qw3_preflight", "qw3_create", "qw3_load_weights", "qw3_prefill", "qw3_decode_step",
            "qw3_reset_kv", "qw3_status_poll", "qw3_get_len", "qw3_destroy", "qw3_block_forward", "qw3_kv_write",
            "qw3_kv_read", "qw3_kv_set_len", "qw3_dequant", "qw3_bench_kernel", "qw3_pcg32_seed",
-           "qw3_sample_workspace_bytes", "qw3_sample", "qw3_inspect_file", "qw3_load_file"]
+           "qw3_sample_workspace_bytes", "qw3_sample", "qw3_inspect_file", "qw3_load_file",
+           "qw3_sample_noalloc"]
 
 _lib = None
 
@@ -107,6 +108,8 @@ def lib():
             "qw3_dequant": (I32, [U64, I32, I32, P, V]),
             "qw3_bench_kernel": (I32, [U64, I32, I32, I32, V]),
             "qw3_pcg32_seed": (I32, [U64, U64, P]),
+            "qw3_sample_noalloc": (I32, [P, I32, I32, ctypes.c_int64, ctypes.POINTER(SampleParams), P, I32, P, I32,
+                                         P, I32, P, P, P, P, V]),
             "qw3_inspect_file": (I32, [ctypes.c_char_p, ctypes.POINTER(FileReport)]),
             "qw3_load_file": (I32, [U64, ctypes.c_char_p, V]),
             "qw3_sample_workspace_bytes": (I32, [I32, ctypes.POINTER(U64)]),

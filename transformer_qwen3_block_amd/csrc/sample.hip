@@ -25,6 +25,8 @@
 //   [P4] "Portable WebAssembly Runtime Architecture for TinyRustLM"
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace qw3 {
@@ -415,6 +417,42 @@ hipError_t launch_sample(const SampleArgs &a, hipStream_t st) {
 
 }  // namespace qw3
 
+// ---- allocation-free variant ---------------------------------------------------------------------------
+// For callers that cannot allocate (code under graph capture, tight serving loops, harnesses that forbid
+// hipMalloc): qw3_sample_noalloc keeps the candidate scratch in this file-scope device array, one copy per GPU
+// for as long as the process lives, sized for the largest request (QW3_SAMPLE_MAX_ROWS rows; the layout does
+// not depend on the vocabulary).  Host code never passes the array's name to a kernel: the device address of
+// each GPU's copy comes from hipGetSymbolAddress, taken once per device with that device current.
+constexpr uint64_t kNoAllocScratchBytes =
+    (((uint64_t)qw3::kSampleChunks * qw3::kSampleMaxTopK * 8 + (uint64_t)qw3::kSampleChunks * 8) *
+         qw3::kSampleMaxRows +
+     255) &
+    ~uint64_t(255);
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's copy of `scratch` (looked up on the first call on that device).
+int32_t noalloc_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QW3_DEVICE_ERROR;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return QW3_DEVICE_ERROR;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return QW3_OK;
+}
+}  // namespace
+
 // ---- C ABI ------------------------------------------------------------------------------------------------
 namespace {
 
@@ -491,6 +529,23 @@ int32_t qw3_sample(const float *logits_dev, int32_t n_rows, int32_t vocab, int64
     if ((uintptr_t)workspace_dev & 255u) return QW3_ALIGNMENT;
     if (workspace_bytes < sample_scratch_bytes(n_rows)) return QW3_OUT_OF_MEMORY;
     sample_bind_scratch(a, workspace_dev);
+    return launch_sample(a, (hipStream_t)stream) == hipSuccess ? QW3_OK : QW3_DEVICE_ERROR;
+}
+
+int32_t qw3_sample_noalloc(const float *logits_dev, int32_t n_rows, int32_t vocab, int64_t ld_logits,
+                           const qw3_sample_params_t *params, const int32_t *history_dev, int32_t n_history,
+                           const int32_t *forbid_dev, int32_t n_forbid, const int32_t *stop_ids, int32_t n_stop,
+                           uint64_t *rng_dev, int32_t *token_out_dev, int32_t *done_out_dev, int32_t *status_out_dev,
+                           void *stream) {
+    SampleArgs a;
+    const int32_t rc = sample_args(a, logits_dev, n_rows, vocab, ld_logits, params, history_dev, n_history, forbid_dev,
+                                   n_forbid, stop_ids, n_stop, rng_dev, token_out_dev, done_out_dev, status_out_dev);
+    if (rc != QW3_OK) return rc;  // rows beyond QW3_SAMPLE_MAX_ROWS or a vocabulary beyond QW3_SAMPLE_MAX_VOCAB
+    if (sample_scratch_bytes(n_rows) > kNoAllocScratchBytes) return QW3_OUT_OF_MEMORY;
+    void *ws = nullptr;
+    const int32_t src = noalloc_scratch(&ws);
+    if (src != QW3_OK) return src;
+    sample_bind_scratch(a, ws);
     return launch_sample(a, (hipStream_t)stream) == hipSuccess ? QW3_OK : QW3_DEVICE_ERROR;
 }
 
