@@ -21,7 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+F16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense f16 / bf16 MFMA (the prefill's operands are f16)
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_q8_b1_ctx2048_hbm_traffic.json")
@@ -46,11 +46,89 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def percentiles(xs):
+    import numpy as np
+    a = np.asarray(xs, np.float64)
+    return {"median": round(float(np.median(a)), 3), "p10": round(float(np.percentile(a, 10)), 3),
+            "p90": round(float(np.percentile(a, 90)), 3), "n": int(a.size)}
+
+
+def timed(torch, stream, fn, reps):
+    """Per-call durations (us) of `reps` calls of fn, HIP events on the launch stream around each."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)]
+
+
+def run_env(torch):
+    """What the numbers were measured on: device, ROCm / HIP / compiler versions, clocks."""
+    import subprocess
+    env = {"device": torch.cuda.get_device_name(0), "torch": torch.__version__, "hip_runtime": torch.version.hip}
+    try:
+        env["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    for key, cmd in (("hipcc", ["/opt/rocm/bin/hipcc", "--version"]),
+                     ("clocks", ["rocm-smi", "--showclocks"])):
+        try:
+            outp = subprocess.run(cmd, capture_output=True, text=True, timeout=30).stdout
+            lines = [ln.strip() for ln in outp.splitlines() if ln.strip() and not ln.startswith("=")]
+            if key == "hipcc":
+                env[key] = next((ln for ln in lines if "clang version" in ln or "HIP version" in ln), None)
+            else:
+                env[key] = [ln for ln in lines if "Mhz" in ln or "MHz" in ln][:6]
+        except (OSError, subprocess.SubprocessError):
+            env[key] = None
+    import transformer_qwen3_block_amd as q
+    env["hipcc_flags"] = " ".join(q.HIPCC_FLAGS)
+    return env
+
+
+def run_probes(torch, q, stream):
+    """Attainable peaks on this machine: a plain HBM read stream over 4 GiB (16 times the MALL) and a loop of
+    independent f16 MFMA instructions, each timed with HIP events."""
+    import ctypes
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    buf[:: 1 << 20] = 1
+    grid = 256 * 8
+    out = torch.empty(65536, dtype=torch.int32, device="cuda:0")
+    L = q.lib()
+    s = ctypes.c_void_p(stream.cuda_stream)
+
+    def hbm():
+        q.check(L.qw3_probe_hbm_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()), grid,
+                                     s), "qw3_probe_hbm_read")
+    for _ in range(2):
+        hbm()
+    t_hbm = timed(torch, stream, hbm, 5)
+    del buf
+    iters, mgrid = 4096, 256 * 8
+    outf = torch.empty(mgrid * 4, dtype=torch.float32, device="cuda:0")
+
+    def mfma():
+        q.check(L.qw3_probe_mfma_f16(iters, mgrid, ctypes.c_void_p(outf.data_ptr()), s), "qw3_probe_mfma_f16")
+    mfma()
+    t_mfma = timed(torch, stream, mfma, 5)
+    flops = mgrid * 4 * iters * 4 * (2 * 16 * 16 * 32)
+    torch.cuda.empty_cache()
+    med = lambda t: sorted(t)[len(t) // 2]
+    return {"hbm_read_GBps": round(nbytes / med(t_hbm) / 1e3, 1),
+            "f16_mfma_TFLOPs": round(flops / med(t_mfma) / 1e6, 1),
+            "about": "hand-written probes in the same run: 16-byte nontemporal read stream over 4 GiB (2048 "
+                     "workgroups), and 4 independent v_mfma_f32_16x16x32_f16 chains per wave (2048 workgroups "
+                     "x 4 waves)"}
+
+
 def decode_kernel_bytes(shp, ctx):
     """Algorithmic HBM bytes of one launch of each decode kernel at batch 1 (weights incl. Q8 scales,
     KV positions read, activation vectors in/out)."""
     H, I, Q, KV, V = shp.hidden, shp.inter, shp.q_dim, shp.kv_dim, shp.vocab
-    q8 = shp.fmt == 2
+    q8 = shp.fmt in (2, 3)   # Q8 and Q8_0 weights stream the same device layout (int8 codes + f32 scales)
 
     def w(rows, cols):
         return rows * cols + rows * (cols // 32) * 4 if q8 else rows * cols * 2
@@ -91,16 +169,20 @@ def run_decode(args, torch, q, synth):
     for _ in range(args.warmup - 1):
         m.decode_step(am, am)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: the first-to-last span times exactly `steps` steps, and the spans
+    # between neighbours give the per-step distribution
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     wall0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         m.decode_step(am, am)
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    step_us = percentiles([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(args.steps)])
     assert m.status() == 0, "numerical failure latched during the timed decode"
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ctx_mid = ctx0 + args.warmup + args.steps // 2
     log(f"decode: {ms * 1e3:.1f} us/token (wall {wall / args.steps * 1e6:.1f} us/token)")
 
@@ -129,7 +211,134 @@ def run_decode(args, torch, q, synth):
     del m
     torch.cuda.empty_cache()
     return dict(shp=shp, wl=wl, W=W, ms=ms, wall_us=wall / args.steps * 1e6, kernels=kernels, dominant=dom,
-                step_bytes=step_bytes, ctx_mid=ctx_mid)
+                step_bytes=step_bytes, ctx_mid=ctx_mid, step_us=step_us)
+
+
+def decode_steps_timed(torch, m, stream, tok, warmup, steps):
+    """Greedy decode steps replayed from the argmax buffer; returns the per-step durations (us)."""
+    am = torch.empty(1, dtype=torch.int32, device="cuda:0")
+    m.decode_step(tok, am)
+    for _ in range(warmup - 1):
+        m.decode_step(am, am)
+    torch.cuda.synchronize()
+    t = timed(torch, stream, lambda: m.decode_step(am, am), steps)
+    assert m.status() == 0
+    return t
+
+
+def run_bf16_decode(args, torch, q, synth, stream):
+    """The 28-layer bf16 workload at batch 1: prefill of its 128-token prompt (HBM-bound at this length), then
+    greedy decode from context 128 (contexts 129..)."""
+    wl = synth.BF16_DECODE
+    shp = wl.shape
+    W = synth.make_weights(shp, seed=wl.seed)
+    m = q.Model(q.make_config(**synth.abi_config_kwargs(shp)), device="cuda:0")
+    m.load_weights(synth.abi_tensors(W))
+    del W
+    toks = torch.tensor(synth.tokens(wl.seed, 0, wl.prefill, shp.vocab), dtype=torch.int32, device="cuda:0")
+    am = torch.empty(1, dtype=torch.int32, device="cuda:0")
+
+    def pre():
+        m.reset_kv(0)
+        m.prefill(toks, 0, None, am)
+    for _ in range(2):
+        pre()
+    torch.cuda.synchronize()
+    tp = timed(torch, stream, pre, 5)
+    m.reset_kv(0)
+    m.prefill(toks, 0, None, am)
+    td = decode_steps_timed(torch, m, stream, am.clone(), 8, min(args.steps, wl.decode - 8))
+    H, I, Q, KV, V, L = shp.hidden, shp.inter, shp.q_dim, shp.kv_dim, shp.vocab, shp.n_layers
+    wbytes = 2 * (L * (Q * H + 2 * KV * H + H * Q + 3 * I * H) + V * H)
+    ctx_mid = wl.prefill + 8 + len(td) // 2
+    step_bytes = wbytes + L * KV * 2 * 2 * ctx_mid
+    pre_bytes = 2 * L * (Q * H + 2 * KV * H + H * Q + 3 * I * H) + 2 * V * H
+    del m
+    torch.cuda.empty_cache()
+    pd, dd = percentiles(tp), percentiles(td)
+    c0 = wl.prefill + 8
+    return {"workload": "28-layer Qwen3-0.6B-shape bf16, batch 1: prefill 128 tokens, then greedy decode "
+                        f"(timed steps at contexts {c0}..{c0 + len(td) - 1})",
+            "decode_tok_s": round(1e6 / dd["median"], 1), "decode_step_us": dd,
+            "decode_hbm_GBps": round(step_bytes / dd["median"] / 1e3, 1),
+            "decode_frac_hbm_peak": round(step_bytes / dd["median"] / 1e3 / HBM_PEAK_GBS, 4),
+            "prefill128_tok_s": round(wl.prefill / pd["median"] * 1e6, 1), "prefill128_us": pd,
+            "prefill128_hbm_GBps": round(pre_bytes / pd["median"] / 1e3, 1)}
+
+
+def run_q8_0_decode(args, torch, q, synth, stream):
+    """The 28-layer decode at KV context 2048 with the weights given as Q8_0 blocks (f16 scales)."""
+    wl = synth.Q8_DECODE
+    from dataclasses import replace
+    shp = replace(wl.shape, fmt=synth.FMT_Q8_0)
+    W = synth.make_weights(shp, seed=wl.seed)
+    m = q.Model(q.make_config(**synth.abi_config_kwargs(shp)), device="cuda:0")
+    m.load_weights(synth.abi_tensors(W))
+    del W
+    for l in range(shp.n_layers):
+        k, v = synth.kv_fill(wl.seed, 0, l, shp.n_kv_heads, wl.kv_prefill, shp.head_dim)
+        m.kv_write(0, l, 0, torch.from_numpy(k.view("int16")).cuda(), torch.from_numpy(v.view("int16")).cuda())
+    m.set_len(0, wl.kv_prefill)
+    tok = torch.tensor(synth.tokens(wl.seed, 1, 1, shp.vocab), dtype=torch.int32, device="cuda:0")
+    td = decode_steps_timed(torch, m, stream, tok, args.warmup, args.steps)
+    del m
+    torch.cuda.empty_cache()
+    d = percentiles(td)
+    return {"workload": "as the headline, weights given as Q8_0 34-byte blocks (f16 scale); the packer widens "
+                        "the scales to f32, so the device streams the same bytes",
+            "tok_s": round(1e6 / d["median"], 1), "step_us": d}
+
+
+def run_single_block(args, torch, q, synth, stream):
+    """The single-block bf16 workload (hidden 1024, one layer, hidden-state input): prefill of 16 positions
+    and per-kernel decode times.  Its 31.5 MB of weights stay in the 256 MB MALL between launches, so these
+    are cache-resident times, not HBM-bound ones."""
+    wl = synth.SINGLE_BLOCK
+    shp = wl.shape
+    W = synth.make_weights(shp, seed=wl.seed)
+    m = q.Model(q.make_config(**synth.abi_config_kwargs(shp)), device="cuda:0")
+    m.load_weights(synth.abi_tensors(W))
+    hin = torch.from_numpy(synth.hidden_inputs(wl.seed, 0, wl.prefill + 1, shp.hidden)).cuda()
+    out = torch.empty((wl.prefill, shp.hidden), dtype=torch.float32, device="cuda:0")
+
+    def pre():
+        m.reset_kv(0)
+        m.block_forward(hin[:wl.prefill], out)
+    for _ in range(2):
+        pre()
+    torch.cuda.synchronize()
+    tp = percentiles(timed(torch, stream, pre, 10))
+    res = {"workload": "single Qwen3-0.6B-shape block, bf16, hidden-state input (cache-resident)",
+           "prefill16_us": tp}
+    names = {1: "qkv_gemv", 2: "attn_decode", 3: "o_gemv", 4: "gateup_gemv", 5: "down_gemv", 7: "block_persistent"}
+    kern = {}
+    for kid, name in names.items():
+        try:
+            m.bench_kernel(kid, 0, 3)
+        except q.Qw3Error:
+            continue
+        torch.cuda.synchronize()
+        kern[name] = percentiles(timed(torch, stream, lambda: m.bench_kernel(kid, 0, 1), 20))["median"]
+    res["decode_kernel_us"] = kern
+    del m
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_sampler(torch, q, synth, stream):
+    """Deterministic sampling over Qwen3's 151,936 logits: top-k 50, top-p 0.9, temperature 0.8, repetition
+    penalty 1.1 over a 64-token history, for 1 and 16 rows."""
+    res = {}
+    for rows in (1, 16):
+        lg = torch.from_numpy(synth.logits_rows(9, 0, rows, 151936, 3.0)).cuda()
+        hist = torch.from_numpy(synth.tokens(9, 1, rows * 64, 151936).reshape(rows, 64)).cuda()
+        smp = q.Sampler(rows, list(range(rows)))
+        fn = lambda: smp(lg, 0.8, 50, 0.9, 1.1, hist)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        res[f"rows{rows}_us"] = percentiles(timed(torch, stream, fn, 20))["median"]
+    return res
 
 
 def run_prefill(args, torch, q, synth):
@@ -254,6 +463,9 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-batched", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the attainable-peak probes and the secondary workloads (bf16, Q8_0, single block, "
+                         "sampler)")
     ap.add_argument("--batched-iters", type=int, default=16)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle decode (0 = skip)")
     ap.add_argument("--kernel-path", action="store_true",
@@ -280,6 +492,17 @@ def main():
     side = torch.cuda.Stream(device="cuda:0")
     with torch.cuda.stream(side):
         res = run_decode(args, torch, q, synth)
+    extra = {}
+    if not args.no_extra:
+        with torch.cuda.stream(side):
+            for key, fn in (("probes", lambda: run_probes(torch, q, side)),
+                            ("bf16_b1", lambda: run_bf16_decode(args, torch, q, synth, side)),
+                            ("q8_0_b1", lambda: run_q8_0_decode(args, torch, q, synth, side)),
+                            ("single_block", lambda: run_single_block(args, torch, q, synth, side)),
+                            ("sampler", lambda: run_sampler(torch, q, synth, side))):
+                t0 = time.time()
+                extra[key] = fn()
+                log(f"{key}: {json.dumps(extra[key])} ({time.time() - t0:.1f}s)")
     if args.copy_probe:
         with torch.cuda.stream(side):
             src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
@@ -329,6 +552,7 @@ def main():
                                "KV context 2048 (bf16)",
                    "hidden": 1024, "layers": 28, "q_heads": 16, "kv_heads": 8, "head_dim": 128, "mlp": 3072,
                    "vocab": 151936, "kv_context_start": res["wl"].kv_prefill},
+        "step_us": res["step_us"],
         "hbm_GBps": round(res["step_bytes"] / ms / 1e6, 1),
         "step_bytes": res["step_bytes"],
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -337,15 +561,25 @@ def main():
         "cpu_baseline": cpu,
     }
     if pre is not None:
-        out["prefill"] = {"workload": "28-layer Qwen3-0.6B-shape bf16 prefill of 2048 tokens, batch 1",
+        out["prefill"] = {"workload": "28-layer Qwen3-0.6B-shape bf16-weight prefill of 2048 tokens, batch 1, on "
+                                      "f16-operand MFMA (f32 accumulation)",
                           "tok_s": round(pre["tok_s"], 1), "ms": round(pre["ms"], 4),
                           "TFLOPs": round(pre["tflops"], 2), "flop": pre["flops"],
-                          "frac_bf16_mfma_peak": round(pre["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)}
+                          "frac_f16_mfma_peak": round(pre["tflops"] / F16_MFMA_PEAK_TFLOPS, 4)}
     if bat is not None:
         out["batched"] = {"workload": "28-layer Qwen3-0.6B-shape Q8 decode, 16 sequences x KV context 8192",
                           "tok_s": round(bat["tok_s"], 1), "ms_per_iteration": round(bat["ms"], 4),
                           "hbm_GBps": round(bat["GBps"], 1), "attn_us_per_layer": round(bat["attn_us"], 2),
                           "attn_GBps": round(bat["attn_GBps"], 1), "iterations": bat["iters"]}
+    probes = extra.pop("probes", None)
+    if probes:
+        out["roofline"]["attainable_peak"] = probes["hbm_read_GBps"]
+        out["roofline"]["frac_attainable"] = round(dk["GBps"] / probes["hbm_read_GBps"], 4)
+        out["probes"] = probes
+        if pre is not None:
+            out["prefill"]["frac_attainable_mfma"] = round(pre["tflops"] / probes["f16_mfma_TFLOPs"], 4)
+    out.update(extra)
+    out["env"] = run_env(torch)
     print(json.dumps(out), flush=True)
 
 

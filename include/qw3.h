@@ -361,6 +361,16 @@ int32_t qw3_dequant(uint64_t handle, int32_t kind, int32_t layer, float *out_dev
  * continuation of the previous one. */
 int32_t qw3_bench_kernel(uint64_t handle, int32_t kernel, int32_t layer, int32_t reps, void *stream);
 
+/* Measurement probes (not part of the forward pass): attainable peaks on the current device, so that roofline
+ * fractions can be stated against both the nominal peak and what a plain kernel reaches.
+ * qw3_probe_hbm_read streams `bytes` (16-byte aligned device buffer) once with 16-byte nontemporal loads on
+ * `grid` workgroups of 256 threads, writing one word per workgroup to out_dev (uint32 [grid]).
+ * qw3_probe_mfma_f16 runs `iters` rounds of four independent v_mfma_f32_16x16x32_f16 per wave on `grid`
+ * workgroups of four waves (16384 flops per instruction), writing one float per wave to out_dev
+ * (float [grid * 4]).  QW3_INVALID_ARGUMENT for null or misaligned pointers, grid outside 1..65536. */
+int32_t qw3_probe_hbm_read(const void *buf_dev, uint64_t bytes, uint32_t *out_dev, int32_t grid, void *stream);
+int32_t qw3_probe_mfma_f16(int32_t iters, int32_t grid, float *out_dev, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,7 +16,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 _SO = os.path.join(_HERE, "libqw3.so")
-_SOURCES = ["api.hip", "decode.hip", "prefill.hip", "mega.hip", "gemv_mfma.hip", "sample.hip", "loader.cpp"]
+_SOURCES = ["api.hip", "decode.hip", "prefill.hip", "mega.hip", "gemv_mfma.hip", "sample.hip", "loader.cpp",
+            "probe.hip"]
 
 ABI_VERSION = 1
 WEIGHTS_BF16, WEIGHTS_Q8, WEIGHTS_Q8_0 = 1, 2, 3
@@ -76,7 +77,7 @@ EXPORTS = ["qw3_abi_version", "qw3_rope_table", "qw3_preflight", "qw3_create", "
            "qw3_reset_kv", "qw3_status_poll", "qw3_get_len", "qw3_destroy", "qw3_block_forward", "qw3_kv_write",
            "qw3_kv_read", "qw3_kv_set_len", "qw3_dequant", "qw3_bench_kernel", "qw3_pcg32_seed",
            "qw3_sample_workspace_bytes", "qw3_sample", "qw3_inspect_file", "qw3_load_file",
-           "qw3_sample_noalloc"]
+           "qw3_sample_noalloc", "qw3_probe_hbm_read", "qw3_probe_mfma_f16"]
 
 _lib = None
 
@@ -110,6 +111,8 @@ def lib():
             "qw3_pcg32_seed": (I32, [U64, U64, P]),
             "qw3_sample_noalloc": (I32, [P, I32, I32, ctypes.c_int64, ctypes.POINTER(SampleParams), P, I32, P, I32,
                                          P, I32, P, P, P, P, V]),
+            "qw3_probe_hbm_read": (I32, [P, U64, P, I32, V]),
+            "qw3_probe_mfma_f16": (I32, [I32, I32, P, V]),
             "qw3_inspect_file": (I32, [ctypes.c_char_p, ctypes.POINTER(FileReport)]),
             "qw3_load_file": (I32, [U64, ctypes.c_char_p, V]),
             "qw3_sample_workspace_bytes": (I32, [I32, ctypes.POINTER(U64)]),

@@ -41,6 +41,25 @@ constexpr int kMegaBuf = 3072;  // floats per LDS input buffer (largest phase in
 
 static_assert(kHid == kNW, "one hidden row per wave");
 
+// Phase timing (diagnostic builds only, -DQW3_MEGA_STAMPS): thread 0 of every workgroup records the 100 MHz
+// s_memrealtime clock when a phase's inputs have all arrived (k = 0) and when it has published its outputs
+// (k = 1), per (layer, phase); qw3_mega_stamps copies the table out.  The clock is global to the device, so
+// stamps of different workgroups compare directly.
+#ifdef QW3_MEGA_STAMPS
+constexpr int kStampLayers = 64;
+__device__ uint64_t g_mega_stamps[kStampLayers * 6 * 2 * kMegaGrid + kMegaGrid];
+#define QW3_STAMP(l, ph, k)                                                                                   \
+    do {                                                                                                      \
+        if (threadIdx.x == 0 && (l) < kStampLayers)                                                           \
+            __builtin_nontemporal_store((uint64_t)__builtin_amdgcn_s_memrealtime(),                            \
+                                        &g_mega_stamps[(((l) * 6 + (ph)) * 2 + (k)) * kMegaGrid + blockIdx.x]); \
+    } while (0)
+#else
+#define QW3_STAMP(l, ph, k) \
+    do {                    \
+    } while (0)
+#endif
+
 __device__ __forceinline__ void put(uint64_t *p, float v, uint32_t tag) {
     __hip_atomic_store(p, ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -473,6 +492,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const bool ok = poll<4>([&](int i) { return src + xw_index(i); }, kHid, tag(l - 1, 5), xs, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
         }
+        QW3_STAMP(l, 0, 0);
         {
             float xr[CH][E];
             rms_slice<Q8, CH>(xs, nq, a.eps, lane, xr);
@@ -483,6 +503,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int j = 0; j < RQ_MAX; ++j)
                 if (lane == j && rqv[j]) put(a.qkv + rq[j], d[j], tag(l, 0));
         }
+        QW3_STAMP(l, 0, 1);
         {  // attention-phase loads: QK-Norm weights, this position's RoPE row, the first cached group
             const float *qnw = (const float *)(lb + a.q_norm), *knw = (const float *)(lb + a.k_norm);
             qkn[0] = qnw[lane];
@@ -513,6 +534,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             };
             const bool ok = poll<3>(src, (G + 2) * kHeadDim, tag(l, 0), raw, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
+            QW3_STAMP(l, 1, 0);
 
             // QK-Norm ([P1] item 3, one 128-weight vector per projection) then RoPE on pairs (i, i + 64) at
             // `pos` (item 4).  Every wave normalises the G query heads into LDS rows of its own (read back by the
@@ -620,6 +642,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 put(ph + 2 + d, O, tag(l, 1));
             }
         }
+        QW3_STAMP(l, 1, 1);
         load_rows<Q8, 1, KO_MAX>(lb + a.wo, (const float *)(lb + a.so), q_dim, ro, rov, KO, lane, wo, so);
 
         // ================= M: merge of the context splits of one query head, dpw output dims per workgroup
@@ -638,6 +661,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             };
             const bool ok = poll<kMegaBuf / 256>(src, SP * per, tag(l, 1), big, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
+            QW3_STAMP(l, 2, 0);
             // exact combination (split order fixed by the reduction tree): M = max m_s,
             // o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, scores in log2 units
             if (SP <= 32 && dpw == 2 * kWaves) {
@@ -672,6 +696,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 }
             }
         }
+        QW3_STAMP(l, 2, 1);
         load_rows<Q8, 2 * RU_MAX, CH>(lb + a.wgu, (const float *)(lb + a.sgu), kHid, ru, ruv, CH, lane, wu, su);
         load_slice<Q8, CH>((const float *)(lb + a.mlp_norm), lane, nu);
 
@@ -680,10 +705,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const uint64_t *src = a.attn;
             const bool ok = poll<8>([&](int i) { return src + xw_index(i); }, q_dim, tag(l, 2), big, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
+            QW3_STAMP(l, 3, 0);
             const float d = wave_sum_fast(dot_lds<Q8, KO_MAX>(wo[0], so[0], big, KO, lane));
             x_own = x_own + d;
             if (lane == 0) put(a.xo + xw_index(gw), x_own, tag(l, 3));
         }
+        QW3_STAMP(l, 3, 1);
         load_rows<Q8, 1, KD_MAX>(lb + a.wd, (const float *)(lb + a.sd), I, ro, rov, KD, lane, wd, sd);
 
         // ================= U: RMSNorm + gate/up + SwiGLU
@@ -691,6 +718,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const uint64_t *src = a.xo;
             const bool ok = poll<4>([&](int i) { return src + xw_index(i); }, kHid, tag(l, 3), xs, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
+            QW3_STAMP(l, 4, 0);
             float xr[CH][E];
             rms_slice<Q8, CH>(xs, nu, a.eps, lane, xr);
             float av[RU_MAX];
@@ -707,6 +735,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int j = 0; j < RU_MAX; ++j)
                 if (lane == j && ruv[2 * j]) put(a.act + xw_index(ru[2 * j]), av[j], tag(l, 4));
         }
+        QW3_STAMP(l, 4, 1);
         if (l + 1 < a.L) {
             const uint8_t *nb = lblock(l + 1);
             load_rows<Q8, RQ_MAX, CH>(nb + a.wqkv, (const float *)(nb + a.sqkv), kHid, rq, rqv, CH, lane, wq, sq);
@@ -718,6 +747,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const uint64_t *src = a.act;
             const bool ok = poll<kMegaBuf / 256>([&](int i) { return src + xw_index(i); }, I, tag(l, 4), big, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
+            QW3_STAMP(l, 5, 0);
             const float d = wave_sum_fast(dot_lds<Q8, KD_MAX>(wd[0], sd[0], big, KD, lane));
             x_own = x_own + d;
             if (lane == 0) {
@@ -727,11 +757,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     a.x_out[gw] = x_own;
             }
         }
+        QW3_STAMP(l, 5, 1);
     }
     // Every workgroup read the epoch before its first phase, and workgroup 0 has consumed every workgroup's
     // output since, so the next launch's tag base can be published now.
     if (b == 0 && tid == 0) a.epoch[0] = ep + (uint32_t)(8 * a.L + 8);
 }
+
+#ifdef QW3_MEGA_STAMPS
+// Copies the phase-stamp table of the last launch (layers x 6 phases x 2 x kMegaGrid uint64, 100 MHz ticks).
+extern "C" int32_t qw3_mega_stamps(void *host_out, uint64_t bytes) {
+    if (!host_out || bytes < sizeof(uint64_t) * (uint64_t)kStampLayers * 6 * 2 * kMegaGrid) return QW3_INVALID_ARGUMENT;
+    return hipMemcpyFromSymbol(host_out, HIP_SYMBOL(g_mega_stamps), sizeof(uint64_t) * (size_t)kStampLayers * 6 * 2 *
+                               kMegaGrid) == hipSuccess ? QW3_OK : QW3_DEVICE_ERROR;
+}
+#endif
 
 bool mega_supported(const Dims &d) {
     if (d.H != kHid || d.S < 1) return false;
