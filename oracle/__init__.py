@@ -73,6 +73,8 @@ def lib():
             "orc_q8_dot": (ctypes.c_float, [_F, _F, _F, ctypes.c_int32]),
             "orc_q8_0_dot": (ctypes.c_float, [_F, _F, ctypes.c_int32]),
             "orc_f16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
+            "orc_quantize_act8": (None, [_F, ctypes.c_int32, _F, _F]),
+            "orc_q8q8_dot": (ctypes.c_float, [_F, _F, _F, _F, ctypes.c_int32]),
             "orc_bf16_dot": (ctypes.c_float, [_F, _F, ctypes.c_int32]),
             "orc_dequant_row": (None, [ctypes.POINTER(Mat), ctypes.c_int32, _F]),
             "orc_matvec": (None, [ctypes.POINTER(Mat), _F, _F]),
@@ -180,6 +182,21 @@ def q8_0_dot(blocks, act):
     blocks = np.ascontiguousarray(blocks, np.uint8)
     act = f32(act)
     return np.float32(lib().orc_q8_0_dot(_p(blocks), _p(act), act.size))
+
+
+def quantize_act8(x):
+    """Per-32-block int8 codes and f32 scales of an activation vector."""
+    x = f32(x)
+    q = np.empty(x.size, np.int8)
+    d = np.empty(x.size // 32, np.float32)
+    lib().orc_quantize_act8(_p(x), x.size, _p(q), _p(d))
+    return q, d
+
+
+def q8q8_dot(codes, scales, aq, ad):
+    codes = np.ascontiguousarray(codes, np.int8)
+    aq = np.ascontiguousarray(aq, np.int8)
+    return np.float32(lib().orc_q8q8_dot(_p(codes), _p(f32(scales)), _p(aq), _p(f32(ad)), codes.size))
 
 
 def f16_to_f32(bits):

@@ -213,6 +213,63 @@ float orc_q8_0_dot(const uint8_t *blocks, const float *act, int32_t n) {
     return acc;
 }
 
+/* Dynamic int8 quantization of an activation vector, per block of 32 ([P3] section 5 "Q8_0 Mixed-Precision
+ * Matrix Multiplication": the f32 activations are quantized to the Q8_0 form per row before the dot, the
+ * integers bounded to [-127, 127]): d = max|x| / 127 over the block (f32 division), q = x / d rounded to
+ * nearest with ties away from zero and clamped to [-127, 127].  A block with d = 0 gets zero codes; a block
+ * whose d is not finite (a NaN or infinite input) gets zero codes and keeps d, so the non-finite value
+ * reaches the dot product instead of being repaired. */
+void orc_quantize_act8(const float *x, int32_t n, int8_t *q, float *d) {
+    for (int32_t b = 0; b < n / 32; ++b) {
+        float amax = 0.0f;
+        for (int32_t i = 0; i < 32; ++i) {
+            const float a = fabsf(x[b * 32 + i]);
+            if (isnan(a)) { /* a NaN makes the block's scale NaN */
+                amax = a;
+                break;
+            }
+            if (a > amax) amax = a;
+        }
+        const float db = amax / 127.0f;
+        d[b] = db;
+        for (int32_t i = 0; i < 32; ++i) {
+            float v = 0.0f;
+            if (db > 0.0f && isfinite(db)) {
+                v = roundf(x[b * 32 + i] / db);
+                if (v > 127.0f) v = 127.0f;
+                if (v < -127.0f) v = -127.0f;
+            }
+            q[b * 32 + i] = (int8_t)v;
+        }
+    }
+}
+
+/* q8 x q8 dot ([P3] section 5 "Floating Reduction Order"; [P4] "SIMD128 q8 design"): per block the 32
+ * products of int8 weight and activation codes are summed in int32 -- at most 32 * 127 * 127 = 516,128 in
+ * magnitude, inside the [P4] "Integer-overflow rule" bound 2^31 - 1 -- then converted to f32 and multiplied by
+ * the product of the two block scales, acc = acc + f32(isum) * (ws * da), blocks in order. */
+float orc_q8q8_dot(const int8_t *wq, const float *ws, const int8_t *aq, const float *ad, int32_t n) {
+    float acc = 0.0f;
+    for (int32_t b = 0; b < n / 32; ++b) {
+        int32_t isum = 0;
+        for (int32_t i = 0; i < 32; ++i) isum += (int32_t)wq[b * 32 + i] * (int32_t)aq[b * 32 + i];
+        acc = acc + (float)isum * (ws[b] * ad[b]);
+    }
+    return acc;
+}
+
+/* y = W x with x quantized to int8 per block first (Q8 weights, q8 x q8 dots). */
+static void matvec_act8(const orc_mat_t *m, const float *x, float *out) {
+    int8_t *q = (int8_t *)malloc((size_t)m->cols);
+    float *d = (float *)malloc(sizeof(float) * (size_t)(m->cols / 32));
+    orc_quantize_act8(x, m->cols, q, d);
+#pragma omp parallel for schedule(static)
+    for (int32_t r = 0; r < m->rows; ++r)
+        out[r] = orc_q8q8_dot(m->codes + (size_t)r * m->cols, m->scales + (size_t)r * (m->cols / 32), q, d, m->cols);
+    free(q);
+    free(d);
+}
+
 /* bf16 weight row dot: acc = acc + act_i * w_i in index order, w_i widened exactly. */
 float orc_bf16_dot(const uint16_t *w, const float *act, int32_t n) {
     float acc = 0.0f;
@@ -470,7 +527,7 @@ orc_model_t *orc_create(const orc_cfg_t *cfg, const orc_mat_t *embed, const void
                         const orc_layer_t *layers) {
     if (!cfg || cfg->n_q_heads <= 0 || cfg->n_kv_heads <= 0 || cfg->n_q_heads % cfg->n_kv_heads) return NULL;
     if (cfg->head_dim % 2 || cfg->max_ctx <= 0 || cfg->n_seq <= 0) return NULL;
-    if (cfg->fmt != ORC_FMT_BF16 && cfg->fmt != ORC_FMT_Q8 && cfg->fmt != ORC_FMT_Q8_0) return NULL;
+    if (cfg->fmt < ORC_FMT_BF16 || cfg->fmt > ORC_FMT_Q8_ACT8) return NULL;
     /* quantized blocks of 32 along every contraction: no tail groups ([P1] section 3, a shape failing the
      * modulo-32 check is an initialisation fault) */
     if (cfg->fmt != ORC_FMT_BF16 &&
@@ -554,6 +611,13 @@ static void load_norm(const void *w, int32_t fmt, int32_t n, float *out) {
 
 /* One decoder layer for one token at position pos, following the step order of [P1] section 5
  * "Transformer Layer Execution Loop" (and section 2 items 1-6). x is updated in place. */
+/* A layer projection: q8 x q8 with dynamically quantized activations in the Q8_ACT8 format, else the f32
+ * activation dot of the weight format. */
+static void layer_matvec(const orc_cfg_t *c, const orc_mat_t *m, const float *x, float *out) {
+    if (c->fmt == ORC_FMT_Q8_ACT8) matvec_act8(m, x, out);
+    else orc_matvec(m, x, out);
+}
+
 /* force / own: NULL, or this layer's [2][HKV][D] bf16 bits (K heads, then V heads) of the appended position:
  * `own` receives the oracle's own rounded values, `force` replaces them in the cache (teacher forcing of the
  * current position; the caller checks that the two differ by rounding only). */
@@ -583,9 +647,9 @@ static int32_t decode_layer(orc_model_t *m, int32_t seq, int32_t l, int32_t pos,
     orc_rmsnorm(x, w, H, c->eps, xn);
 
     /* 2. Q, K, V projections (no bias) */
-    orc_matvec(&W->q, xn, q);
-    orc_matvec(&W->k, xn, k);
-    orc_matvec(&W->v, xn, v);
+    layer_matvec(c, &W->q, xn, q);
+    layer_matvec(c, &W->k, xn, k);
+    layer_matvec(c, &W->v, xn, v);
 
     /* 3. QK-Norm: RMSNorm over each head_dim slice, one shared weight per projection */
     float *hw = w; /* reuse: head_dim <= hidden */
@@ -636,20 +700,20 @@ static int32_t decode_layer(orc_model_t *m, int32_t seq, int32_t l, int32_t pos,
     if (rc != ORC_OK) goto done;
 
     /* 7. output projection and residual */
-    orc_matvec(&W->o, attn, proj);
+    layer_matvec(c, &W->o, attn, proj);
     for (int32_t i = 0; i < H; ++i) x[i] = residual[i] + proj[i];
     memcpy(residual, x, sizeof(float) * H);
 
     /* 8. post-attention RMSNorm, SwiGLU MLP, residual */
     load_norm(W->mlp_norm, c->fmt, H, w);
     orc_rmsnorm(x, w, H, c->eps, xn);
-    orc_matvec(&W->gate, xn, gate);
-    orc_matvec(&W->up, xn, up);
+    layer_matvec(c, &W->gate, xn, gate);
+    layer_matvec(c, &W->up, xn, up);
     for (int32_t i = 0; i < c->inter; ++i) {
         float sig = 1.0f / (1.0f + orc_exp(-gate[i]));
         act[i] = (gate[i] * sig) * up[i];
     }
-    orc_matvec(&W->down, act, proj);
+    layer_matvec(c, &W->down, act, proj);
     for (int32_t i = 0; i < H; ++i) x[i] = residual[i] + proj[i];
 
 done:

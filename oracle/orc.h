@@ -30,10 +30,10 @@ extern "C" {
 
 enum { ORC_OK = 0, ORC_INVALID_ARGUMENT = 1, ORC_UNSUPPORTED_QUANT = 12, ORC_UNSUPPORTED_SHAPE = 13,
        ORC_CONTEXT_EXCEEDED = 14, ORC_NUMERICAL_FAILURE = 18 };
-enum { ORC_FMT_BF16 = 1, ORC_FMT_Q8 = 2, ORC_FMT_Q8_0 = 3 };
+enum { ORC_FMT_BF16 = 1, ORC_FMT_Q8 = 2, ORC_FMT_Q8_0 = 3, ORC_FMT_Q8_ACT8 = 4 };
 
 typedef struct {
-    int32_t fmt;        /* ORC_FMT_BF16, ORC_FMT_Q8 or ORC_FMT_Q8_0 */
+    int32_t fmt;        /* ORC_FMT_BF16, ORC_FMT_Q8, ORC_FMT_Q8_0, or ORC_FMT_Q8_ACT8 (Q8 weights, int8 activations) */
     int32_t input_mode; /* 0: token ids, 1: fp32 hidden vectors (no embedding / final norm / logits) */
     int32_t vocab, hidden, n_layers, n_q_heads, n_kv_heads, head_dim, inter, max_ctx, n_seq;
     int32_t kv_f32;     /* 0: cache holds bf16-rounded K/V (default); 1: cache keeps f32 K/V */
@@ -79,6 +79,8 @@ void orc_matvec(const orc_mat_t *m, const float *x, float *out);
 int32_t orc_argmax(const float *v, int32_t n, int32_t *idx);
 float orc_f16_to_f32(uint16_t h);
 float orc_q8_0_dot(const uint8_t *blocks, const float *act, int32_t n);
+void orc_quantize_act8(const float *x, int32_t n, int8_t *q, float *d);
+float orc_q8q8_dot(const int8_t *wq, const float *ws, const int8_t *aq, const float *ad, int32_t n);
 
 /* Deterministic sampling ([P1] section 7; [P4] "Deterministic sampling contract", "Sampling order"). */
 typedef struct {

@@ -28,6 +28,7 @@ SYN_NORMAL_F32, SYN_NORMAL_BF16, SYN_UNIFORM_F32, SYN_INT8, SYN_INT32 = range(5)
 FMT_BF16 = 1
 FMT_Q8 = 2
 FMT_Q8_0 = 3     # Q8 with the pages' block layout: per 32 codes a 34-byte block led by a little-endian f16 scale
+FMT_Q8_ACT8 = 4  # Q8 weights (codes + f32 scales) whose products quantize the activations to int8 on the fly
 INPUT_TOKENS = 0
 INPUT_HIDDEN = 1
 
@@ -189,7 +190,7 @@ def _matrix(shape: ModelShape, seed: int, tid: int, rows: int, cols: int, std: f
     assert cols % 32 == 0
     codes = int8_uniform(seed, tid, (rows, cols), -127, 127)
     scales = uniform_f32(seed, tid + SCALE_ID, (rows, cols // 32), 1e-3, 1e-2)
-    if shape.fmt == FMT_Q8:
+    if shape.fmt in (FMT_Q8, FMT_Q8_ACT8):
         return Matrix(rows, cols, codes=codes, scales=scales)
     return q8_0_matrix(codes, scales.astype(np.float16))
 
@@ -298,7 +299,7 @@ def abi_config_kwargs(shape: ModelShape) -> dict:
 def abi_tensors(w: Weights, with_lm_head: bool = False) -> list:
     """Tensor list (kind name, layer, dtype code, arrays) in the order of the inventory; dtype codes
     1 = bf16 bits, 2 = f32, 3 = int8 codes + f32 scales, 4 = Q8_0 34-byte blocks."""
-    q8 = w.shape.fmt in (FMT_Q8, FMT_Q8_0)
+    q8 = w.shape.fmt in (FMT_Q8, FMT_Q8_0, FMT_Q8_ACT8)
     out = []
 
     def mat(kind, layer, m):

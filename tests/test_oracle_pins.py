@@ -509,3 +509,88 @@ def test_step_with_its_own_kv_forced_is_the_plain_step():
     assert c.step_forced(0, int(toks[0]), kv_force=forced)[0] == 0
     _, k, v = c.kv_read(0, 0, 0, 1)
     assert v[0, 0, 3] == forced[0, 1, 0, 3] and np.array_equal(k[:, 0], forced[0, 0])
+
+
+# ---------------------------------------------------------------------------------------------------------
+# q8 x q8 with dynamically quantized int8 activations ("Real-Browser WASM Qwen3 Execution ...", section 5
+# "Q8_0 Mixed-Precision Matrix Multiplication"; "Portable WebAssembly ...", "Integer-overflow rule")
+# ---------------------------------------------------------------------------------------------------------
+def test_act8_block_scale_and_ties_away_from_zero():
+    """A block whose largest magnitude is 127 has scale 1, so the codes are the inputs rounded to nearest
+    with ties away from zero (0.5 -> 1, 2.5 -> 3, -0.5 -> -1), not to even."""
+    x = np.zeros(32, np.float32)
+    x[:8] = [127.0, 0.5, 1.5, 2.5, -0.5, -2.5, 3.49, -126.6]
+    q, d = oracle.quantize_act8(x)
+    assert d[0] == 1.0
+    assert list(q[:8]) == [127, 1, 2, 3, -1, -3, 3, -127]
+    assert np.all(q[8:] == 0)
+
+
+def test_act8_codes_on_the_grid_round_trip_and_rounding_bound():
+    rng = np.random.default_rng(11)
+    codes = rng.integers(-127, 128, 64).astype(np.int8)
+    codes[0], codes[32] = 127, -127                          # each block reaches the bound
+    d = np.array([0.037, 1e-30], np.float32)                  # a normal and a tiny scale
+    x = (codes.astype(np.float32) * np.repeat(d, 32)).astype(np.float32)
+    q, dd = oracle.quantize_act8(x)
+    assert np.array_equal(q, codes)
+    y = (3 * rng.standard_normal(4096)).astype(np.float32)
+    q, dd = oracle.quantize_act8(y)
+    err = np.abs(q.astype(np.float64) * np.repeat(dd.astype(np.float64), 32) - y)
+    assert np.all(err <= np.repeat(dd, 32) * 0.5 * (1 + 1e-6)) and np.all(np.abs(q) <= 127)
+
+
+def test_act8_zero_and_non_finite_blocks():
+    x = np.zeros(64, np.float32)
+    x[40] = np.nan
+    q, d = oracle.quantize_act8(x)
+    assert d[0] == 0.0 and np.all(q[:32] == 0)
+    assert np.isnan(d[1]) and np.all(q[32:] == 0)            # the NaN stays in the scale, codes are inert
+    w = np.ones(64, np.int8)
+    assert oracle.q8q8_dot(w, np.ones(2, np.float32), q, d) != oracle.q8q8_dot(w, np.ones(2, np.float32), q, d)
+
+
+def test_q8q8_dot_integer_bound_and_exact_block_sums():
+    """The worst block, all codes +-127 on both sides, sums to 32 * 127 * 127 = 516,128 (< 2^31 - 1, the
+    integer-overflow rule), exactly; with scales that are powers of two the whole dot is exact."""
+    assert 32 * 127 * 127 == 516128 < 2 ** 31 - 1
+    w = np.full(64, -127, np.int8)
+    a = np.full(64, -127, np.int8)
+    a[32:] = 127
+    got = oracle.q8q8_dot(w, np.array([0.5, 0.25], np.float32), a, np.array([2.0, 4.0], np.float32))
+    assert got == 516128 * 1.0 - 516128 * 1.0
+    a[:] = 127
+    assert oracle.q8q8_dot(w, np.array([0.5, 0.25], np.float32), a, np.array([2.0, 4.0], np.float32)) == -2 * 516128.0
+
+
+def test_q8q8_dot_equals_fp64_of_the_quantized_values():
+    """Against the exact fp64 dot of the dequantized weights and the dequantized activation codes, within the
+    f32 summation bound over the blocks."""
+    rng = np.random.default_rng(12)
+    n = 1024
+    wq = rng.integers(-127, 128, n).astype(np.int8)
+    ws = rng.uniform(1e-3, 1e-2, n // 32).astype(np.float32)
+    x = rng.standard_normal(n).astype(np.float32)
+    aq, ad = oracle.quantize_act8(x)
+    got = float(oracle.q8q8_dot(wq, ws, aq, ad))
+    terms = [float(np.dot(wq[32 * b:32 * b + 32].astype(np.int64), aq[32 * b:32 * b + 32].astype(np.int64)))
+             * float(ws[b]) * float(ad[b]) for b in range(n // 32)]
+    exact = sum(terms)
+    nb = n // 32
+    gamma = (nb + 2) * 2.0 ** -24 / (1 - (nb + 2) * 2.0 ** -24)
+    assert abs(got - exact) <= gamma * sum(abs(t) for t in terms)
+
+
+def test_act8_model_tracks_the_f32_activation_model():
+    """The whole model in the q8 x q8 format against the same weights with f32 activations: the logits differ
+    by the activation quantization error only (small but not zero), and every step stays finite."""
+    shp = replace(TINY, fmt=synth.FMT_Q8_ACT8)
+    W = synth.make_weights(shp, seed=14)
+    Wf = synth.Weights(replace(shp, fmt=synth.FMT_Q8), W.embed, W.final_norm, W.layers)
+    a, b = oracle.Model(W), oracle.Model(Wf)
+    for t in synth.tokens(14, 0, 6, shp.vocab):
+        ra, _, la, _ = a.step(0, int(t))
+        rb, _, lb, _ = b.step(0, int(t))
+        assert ra == rb == 0
+        r = np.linalg.norm(la - lb) / np.linalg.norm(lb)
+        assert 1e-5 < r < 5e-2, r
