@@ -60,7 +60,7 @@ typedef enum {
     QW3_DEVICE_ERROR = 21
 } qw3_status_t;
 
-enum { QW3_WEIGHTS_BF16 = 1, QW3_WEIGHTS_Q8 = 2, QW3_WEIGHTS_Q8_0 = 3 };
+enum { QW3_WEIGHTS_BF16 = 1, QW3_WEIGHTS_Q8 = 2, QW3_WEIGHTS_Q8_0 = 3, QW3_WEIGHTS_Q8_ACT8 = 4 };
 enum { QW3_INPUT_TOKENS = 0, QW3_INPUT_HIDDEN = 1 };
 
 /* Model and session shape.  Every field is explicit; nothing is defaulted ("M1 — Load the weights",
@@ -73,8 +73,15 @@ enum { QW3_INPUT_TOKENS = 0, QW3_INPUT_HIDDEN = 1 };
  * "Mixed-Q8 Quantization Definition", with the scale widened to f32).  QW3_WEIGHTS_Q8_0 takes the same
  * matrices in that section's own Q8_0 block layout (QW3_DT_Q8_0 tensors: per 32 inputs one 34-byte block,
  * a little-endian f16 scale then 32 int8 codes); the packer splits the blocks into codes and scales widened
- * exactly to f32, so both formats run the same kernels and dequantize to the same f32 values.  Norm weights
- * are bf16 in the bf16 format and f32 in the Q8 formats.
+ * exactly to f32, so both formats run the same kernels and dequantize to the same f32 values.
+ * QW3_WEIGHTS_Q8_ACT8 takes QW3_DT_Q8 matrices like QW3_WEIGHTS_Q8 but computes every layer projection as a
+ * q8 x q8 product ("Real-Browser WASM Qwen3 Execution Under Honest Memory And Isolation Limits", section 5
+ * "Q8_0 Mixed-Precision Matrix Multiplication"): the projection's input is quantized to int8 per block of 32
+ * (scale max|x| / 127, codes rounded to nearest with ties away from zero, clamped to [-127, 127]), the int8
+ * products of a block are summed in int32 and scaled by both block scales.  Attention, norms and the tied
+ * logits keep f32.  It needs n_seq == 1 (else QW3_UNSUPPORTED_SHAPE from qw3_preflight) and the single-launch
+ * decode (qw3_create returns QW3_UNSUPPORTED_SHAPE when the device cannot hold its grid).  Norm weights are
+ * bf16 in the bf16 format and f32 in the Q8 formats.
  * input_mode QW3_INPUT_HIDDEN runs the layer stack on caller-supplied f32 hidden states (no embedding,
  * no final norm, no logits; vocab_size must be 0). */
 typedef struct qw3_config {

@@ -126,6 +126,35 @@ def forced_step(gpu_model, orc, seq, tok, n_layers, orc_seq=None, stats=None):
     return rc, am, lg, hid
 
 
+# The q8 x q8 format's deep tier (two or more layers).  Its activation codes are integers decided on f32 inputs
+# that differ from the oracle's by reassociation only; a code that lands on the other side of a rounding
+# boundary moves its input by one quantization step (max|x|/127 of the block), and the layers after it amplify
+# that.  So past one layer the comparison is the pages' conformance measures per step: the greedy choice (equal,
+# or a near-tie within the observed logit difference) and the cosine similarity of the logits.
+ACT8_COS = 0.99
+ACT8_KV_REL = 0.1
+
+
+def cosine(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.dot(a, b) / max(np.linalg.norm(a) * np.linalg.norm(b), 1e-300))
+
+
+def forced_step_act8(gpu_model, orc, seq, tok, n_layers, stats=None):
+    """forced_step for the deep q8 x q8 tier: the GPU's appended K/V (of every layer, within ACT8_KV_REL
+    relative L2 of the oracle's own) replaces the oracle's for this step."""
+    pos = orc.get_len(seq)
+    g = read_appended_kv(gpu_model, seq, pos, n_layers)
+    rc, am, lg, hid, own = orc.step_forced(seq, tok, kv_force=g)
+    if rc == 0:
+        worst = max(rel_l2(bf16_to_f32(g[l]), bf16_to_f32(own[l])) for l in range(n_layers))
+        assert worst <= ACT8_KV_REL, f"position {pos}: appended K/V rel-L2 {worst:.3e}"
+        if stats is not None:
+            stats["kv_rel"] = max(stats.get("kv_rel", 0.0), worst)
+    return rc, am, lg, hid
+
+
 def sync_prefilled_kv(gpu_model, orc, seq, n_pos, n_layers, orc_seq=None):
     """KV teacher forcing of a whole prompt.  The tiled prefill feeds MFMA f16 operands, so its cache is close
     to the oracle's (relative L2 within the hidden-state tolerance per layer) but not one-ulp close; decode

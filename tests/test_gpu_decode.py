@@ -12,7 +12,8 @@ import pytest
 
 import oracle
 import synth
-from parity import Margins, argmax_ok, assert_close, build_gpu_model, forced_step
+from parity import (ACT8_COS, ACT8_KV_REL, Margins, argmax_ok, assert_close, build_gpu_model, cosine, forced_step,
+                    forced_step_act8, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -98,20 +99,36 @@ def _greedy_vs_oracle(shp, seed, steps, prefill_tokens=0, kv_fill_len=0, seqs_ch
     logits = torch.empty((S, shp.vocab), dtype=torch.float32, device="cuda")
     worst = Margins(f"decode {shp.fmt=} {shp.n_layers=} {shp.n_q_heads}/{shp.n_kv_heads} heads S={S} {path}")
     kv = {}
+    act8 = shp.fmt == synth.FMT_Q8_ACT8   # q8 x q8: greedy agreement and logits cosine per step
+    worst_cos, worst_abs, worst_rel = 1.0, 0.0, 0.0
     for step in range(steps):
         m.decode_step(cur, am, logits)
         torch.cuda.synchronize()
         g_logits = logits.cpu().numpy()
         g_am = am.cpu().numpy()
         for s in (seqs_checked if seqs_checked is not None else range(S)):
-            rc, o_am, o_logits, _ = forced_step(m, orc, s, int(cur[s].item()), shp.n_layers, stats=kv)
-            assert rc == 0
-            worst.add(assert_close(g_logits[s], o_logits, f"step {step} seq {s}"))
+            if act8:
+                rc, o_am, o_logits, _ = forced_step_act8(m, orc, s, int(cur[s].item()), shp.n_layers, stats=kv)
+                assert rc == 0
+                c = cosine(g_logits[s], o_logits)
+                worst_cos = min(worst_cos, c)
+                d = np.abs(g_logits[s].astype(np.float64) - o_logits)
+                worst_abs, worst_rel = max(worst_abs, float(d.max())), max(worst_rel, rel_l2(g_logits[s], o_logits))
+                assert c >= ACT8_COS, f"step {step} seq {s}: logits cosine {c:.6f}"
+            else:
+                rc, o_am, o_logits, _ = forced_step(m, orc, s, int(cur[s].item()), shp.n_layers, stats=kv)
+                assert rc == 0
+                worst.add(assert_close(g_logits[s], o_logits, f"step {step} seq {s}"))
             assert argmax_ok(int(g_am[s]), o_logits, g_logits[s]), (step, s, int(g_am[s]), o_am)
         cur = am.clone()
     assert m.status() == 0
     for s in range(S):
         assert m.get_len(s) == kv_fill_len + steps
+    if act8:
+        _say(f"MARGIN q8 x q8 decode {shp.n_layers} layer(s) {shp.n_q_heads}/{shp.n_kv_heads} heads: worst logits "
+             f"cosine {worst_cos:.6f} (bound {ACT8_COS}); for information worst max-abs {worst_abs:.3e}, worst "
+             f"rel-L2 {worst_rel:.3e}, worst appended K/V rel-L2 {kv.get('kv_rel', 0):.3e} (bound {ACT8_KV_REL})")
+        return None
     worst.report(kv)
     return worst
 
@@ -231,3 +248,26 @@ def test_graph_replay_matches_eager_bitwise():
         cur_g.copy_(am_g)
         torch.cuda.synchronize()
     assert graphed.get_len(0) == 6 and graphed.status() == 0
+
+
+@pytest.mark.parametrize("layers,heads", [(1, (8, 4)), (1, (8, 8)), (1, (8, 2)), (1, (16, 4)), (2, (8, 4))])
+def test_decode_q8_act8_vs_oracle(layers, heads):
+    """q8 x q8 products (activations quantized to int8 per 32-block on the fly) in the single-launch decode,
+    against the oracle's q8 x q8 format: greedy agreement and logits cosine per step, appended K/V within
+    relative L2 of the oracle's."""
+    shp = replace(SMALL, fmt=synth.FMT_Q8_ACT8, n_q_heads=heads[0], n_kv_heads=heads[1], n_layers=layers)
+    _say("q8 x q8", layers, heads)
+    _greedy_vs_oracle(shp, seed=29, steps=12 if heads == (8, 4) else 5, kv_fill_len=20, path="mega")
+
+
+def test_q8_act8_needs_the_single_launch_decode():
+    import os
+    import transformer_qwen3_block_amd as q
+    W = synth.make_weights(replace(SMALL, fmt=synth.FMT_Q8_ACT8), seed=30)
+    os.environ["QW3_NO_MEGA"] = "1"
+    try:
+        with pytest.raises(q.Qw3Error) as e:
+            build_gpu_model(W)
+    finally:
+        os.environ.pop("QW3_NO_MEGA", None)
+    assert e.value.code == 13

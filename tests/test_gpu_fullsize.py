@@ -75,6 +75,37 @@ def test_q8_0_blocks_decode_context_2048_full():
     assert m.status() == 0
 
 
+@pytest.mark.timeout(300)
+def test_q8_act8_decode_context_2048_full():
+    """The 28-layer decode at KV context 2048 with q8 x q8 layer products (int8 activations), against the
+    oracle's q8 x q8 format in the deep tier: greedy agreement and logits cosine >= 0.99 per step, 8 steps."""
+    from parity import ACT8_COS, cosine, forced_step_act8
+    torch = _torch()
+    wl = synth.Q8_DECODE
+    shp = replace(wl.shape, fmt=synth.FMT_Q8_ACT8)
+    W = synth.make_weights(shp, seed=wl.seed)
+    m = build_gpu_model(W)
+    orc = oracle.Model(W, n_seq=1)
+    _fill_kv(m, {0: orc}, wl.seed, shp, [0], wl.kv_prefill)
+    cur = torch.tensor(synth.tokens(wl.seed, 1, 1, shp.vocab), dtype=torch.int32, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    lg = torch.empty((1, shp.vocab), dtype=torch.float32, device="cuda")
+    worst_cos, st = 1.0, {}
+    for step in range(8):
+        m.decode_step(cur, am, lg)
+        torch.cuda.synchronize()
+        rc, _, o_lg, _ = forced_step_act8(m, orc, 0, int(cur.item()), shp.n_layers, stats=st)
+        assert rc == 0
+        g = lg.cpu().numpy()[0]
+        c = cosine(g, o_lg)
+        worst_cos = min(worst_cos, c)
+        assert c >= ACT8_COS and argmax_ok(int(am.item()), o_lg, g), (step, c)
+        cur = am.clone()
+    _say(f"MARGIN 28-layer q8 x q8 decode: worst logits cosine {worst_cos:.6f} (bound {ACT8_COS}), worst appended "
+         f"K/V rel-L2 {st.get('kv_rel', 0):.3e}")
+    assert m.status() == 0
+
+
 @pytest.mark.timeout(600)
 def test_q8_decode_context_2048_full():
     """28-layer Q8 B=1 decode over a 2048-position KV cache: 64 greedy steps, every step checked against the

@@ -86,12 +86,13 @@ def test_prefill_several_tiles():
     _prefill_vs_oracle(replace(SMALL, max_prefill=48), seed=32, T=130, decode_steps=2)
 
 
-@pytest.mark.parametrize("chunk,T", [(128, 300), (100, 290)])
-def test_prefill_chunks_fused_projection_paths(chunk, T):
-    """Chunked prefill through every projection path: chunks of more than 64 tokens starting on a 64-position
-    boundary (the projection epilogue writes the attention's f16 K/V shadow), or off it (the shadow is
-    converted from the cache afterwards), and a last chunk of 64 tokens or fewer (separate QK-Norm kernel)."""
-    _prefill_vs_oracle(replace(SMALL, max_prefill=chunk), seed=36, T=T, decode_steps=2)
+@pytest.mark.parametrize("chunk,T", [(300, 610), (128, 300), (100, 290)])
+def test_prefill_chunks_every_projection_path(chunk, T):
+    """Chunked prefill through every projection path: chunks of more than 64 tokens take the fused Q/K/V
+    epilogue, which writes the attention's f16 K/V shadow when the chunk starts on a 64-position boundary (0,
+    128) and leaves it to the conversion kernel when not (300, 100, 200); the last chunks of 64 tokens or fewer
+    (10, 44) take the plain products and the separate QK-Norm kernel."""
+    _prefill_vs_oracle(replace(SMALL, max_prefill=chunk, max_ctx=640), seed=36, T=T, decode_steps=2)
 
 
 @pytest.mark.parametrize("heads", [(8, 8), (8, 2)])

@@ -20,7 +20,7 @@ _SOURCES = ["api.hip", "decode.hip", "prefill.hip", "mega.hip", "gemv_mfma.hip",
             "probe.hip"]
 
 ABI_VERSION = 1
-WEIGHTS_BF16, WEIGHTS_Q8, WEIGHTS_Q8_0 = 1, 2, 3
+WEIGHTS_BF16, WEIGHTS_Q8, WEIGHTS_Q8_0, WEIGHTS_Q8_ACT8 = 1, 2, 3, 4
 INPUT_TOKENS, INPUT_HIDDEN = 0, 1
 DT_BF16, DT_F32, DT_Q8, DT_Q8_0 = 1, 2, 3, 4
 KIND = {"embed": 0, "final_norm": 1, "lm_head": 2, "attn_norm": 3, "q": 4, "k": 5, "v": 6, "q_norm": 7,

@@ -83,7 +83,7 @@ int32_t validate(const qw3_config_t *c, Dims *d) {
     if (!c) return QW3_INVALID_ARGUMENT;
     if (c->abi_version != QW3_ABI_VERSION) return QW3_UNSUPPORTED_ABI;
     if (c->weight_format != QW3_WEIGHTS_BF16 && c->weight_format != QW3_WEIGHTS_Q8 &&
-        c->weight_format != QW3_WEIGHTS_Q8_0)
+        c->weight_format != QW3_WEIGHTS_Q8_0 && c->weight_format != QW3_WEIGHTS_Q8_ACT8)
         return QW3_UNSUPPORTED_QUANTIZATION;
     if (c->input_mode != QW3_INPUT_TOKENS && c->input_mode != QW3_INPUT_HIDDEN) return QW3_INVALID_ARGUMENT;
     if (c->hidden <= 0 || c->n_layers <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->intermediate <= 0 ||
@@ -103,6 +103,8 @@ int32_t validate(const qw3_config_t *c, Dims *d) {
     const int q_dim = c->n_q_heads * kHeadDim;
     if (c->hidden % unit || q_dim % unit || c->intermediate % unit) return QW3_UNSUPPORTED_SHAPE;
     if (c->n_seq > kMaxSeq) return QW3_UNSUPPORTED_SHAPE;
+    // q8 x q8 products exist only in the single-launch decode of one sequence
+    if (c->weight_format == QW3_WEIGHTS_Q8_ACT8 && c->n_seq != 1) return QW3_UNSUPPORTED_SHAPE;
     if (c->input_mode == QW3_INPUT_TOKENS && c->vocab_size < 1) return QW3_INVALID_ARGUMENT;
     if (c->input_mode == QW3_INPUT_HIDDEN && c->vocab_size != 0) return QW3_INVALID_ARGUMENT;
     if (c->max_ctx > (1 << 24) || c->max_prefill > (1 << 16)) return QW3_UNSUPPORTED_SHAPE;
@@ -122,6 +124,7 @@ int32_t validate(const qw3_config_t *c, Dims *d) {
     d->Nqkv = (c->n_q_heads + 2 * c->n_kv_heads) * kHeadDim;
     d->q8 = q8;
     d->q8_blocks = c->weight_format == QW3_WEIGHTS_Q8_0;
+    d->act8 = c->weight_format == QW3_WEIGHTS_Q8_ACT8;
     d->hidden_mode = c->input_mode == QW3_INPUT_HIDDEN;
     d->mfma_prefill = !q8 && c->max_prefill > 1;
     d->eps = c->rms_eps;
@@ -229,6 +232,7 @@ T *at(Model *m, uint64_t off) {
 }
 
 inline int32_t dev(hipError_t e) { return e == hipSuccess ? QW3_OK : QW3_DEVICE_ERROR; }
+inline int weight_mode(const Dims &d) { return d.act8 ? 2 : (d.q8 ? 1 : 0); }
 #define QW3_TRY(expr)                      \
     do {                                   \
         const int32_t _rc = (expr);        \
@@ -389,7 +393,11 @@ int32_t qw3_create(const qw3_config_t *cfg, void *arena_dev, uint64_t arena_byte
     m->graphs_enabled = !(ng && ng[0] == '1');
     const char *nm = getenv("QW3_NO_MEGA");  // run single-sequence steps kernel by kernel
     // the single-launch decode needs its whole grid resident at once: checked against the current device
-    m->mega = mega_supported(d) && !(nm && nm[0] == '1') && mega_resident(d.q8, d.G);
+    m->mega = mega_supported(d) && !(nm && nm[0] == '1') && mega_resident(weight_mode(d), d.G);
+    if (d.act8 && !m->mega) {  // the q8 x q8 products are implemented in the single-launch decode only
+        delete m;
+        return QW3_UNSUPPORTED_SHAPE;
+    }
     {
         // every product of a batched step must take the MFMA path, since the residual epilogues hand the
         // next RMSNorm its sums of squares
@@ -740,7 +748,7 @@ static int32_t run_layers_mega(Model *m, int seq, const int *token, const float 
     a.I = d.I;
     a.V = d.V;
     a.eps = d.eps;
-    return dev(launch_decode_mega(d.q8, d.G, a, st));
+    return dev(launch_decode_mega(weight_mode(d), d.G, a, st));
 }
 
 static int32_t run_logits(Model *m, int seq0, int S, const float *xin, float *logits, int *argmax, int commit_add,
@@ -1035,6 +1043,7 @@ int32_t qw3_bench_kernel(uint64_t h, int32_t kernel, int32_t layer, int32_t reps
     if (layer < 0 || layer >= d.L || reps < 1) return QW3_INVALID_ARGUMENT;
     if (kernel < DK_QKV || kernel > 7 || (kernel == 6 && d.hidden_mode)) return QW3_INVALID_ARGUMENT;
     if (kernel == 7 && !(m->mega && d.S == 1)) return QW3_INVALID_ARGUMENT;
+    if (d.act8 && kernel <= DK_DOWN) return QW3_INVALID_ARGUMENT;  // those kernels keep f32 activations
     for (int s = 0; s < d.S; ++s)
         if (m->len[s] >= d.max_ctx) return QW3_CONTEXT_EXCEEDED;
     hipStream_t st = (hipStream_t)stream;

@@ -61,6 +61,7 @@ struct Dims {
     int q_dim;       // HQ * 128
     bool q8;            // int8 codes + f32 scales on the device (Q8 and Q8_0 formats)
     bool q8_blocks;     // matrices arrive as Q8_0 34-byte blocks (f16 scale), split by the packer
+    bool act8;          // layer products quantize their activations to int8 per 32-block (q8 x q8)
     bool hidden_mode;
     bool mfma_prefill;  // bf16 weights and multi-token tiles: f16 weight copies exist
     float eps;
@@ -214,8 +215,9 @@ struct MegaArgs {
     float eps;
 };
 bool mega_supported(const Dims &d);
-bool mega_resident(bool q8, int G);
-hipError_t launch_decode_mega(bool q8, int G, const MegaArgs &a, hipStream_t st);
+// weight mode: 0 bf16, 1 Q8 (f32 activations), 2 Q8 with int8-quantized activations (q8 x q8)
+bool mega_resident(int wmode, int G);
+hipError_t launch_decode_mega(int wmode, int G, const MegaArgs &a, hipStream_t st);
 
 // Deterministic sampling (sample.hip): vocabulary slices of the chunk kernel, bounds of the C ABI.
 constexpr int kSampleChunks = 16;

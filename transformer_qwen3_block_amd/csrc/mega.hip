@@ -248,6 +248,70 @@ __device__ __forceinline__ void rms_slice(const float *xs, const float (&w)[CH][
         for (int e = 0; e < E; ++e) xr[c][e] = w[c][e] * (xs[c * 64 * E + lane * E + e] * inv);
 }
 
+// ---- q8 x q8 products (weight mode 2): activations quantized to int8 per 32-block on the fly ([P3] section 5
+// "Q8_0 Mixed-Precision Matrix Multiplication") -------------------------------------------------------------
+// A lane holds 16 consecutive activations, half of a 32-block (lane ^ 1 holds the other half): the block scale is
+// d = max|x| / 127 over both halves, each code rounds x / d to nearest (ties away from zero) and is clamped to
+// [-127, 127].  A NaN in the block makes d NaN; a block whose d is zero or not finite gets zero codes, so a
+// non-finite input reaches the products through d instead of being repaired.
+__device__ __forceinline__ void quant16(const float (&x)[16], uint32_t (&q)[4], float &d) {
+    float m = 0.f, nan = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float a = fabsf(x[e]);
+        nan = a != a ? 1.f : nan;
+        m = fmaxf(m, a);
+    }
+    m = fmaxf(m, dpp_mov<0xB1>(m));  // the partner lane's half of the block
+    nan = fmaxf(nan, dpp_mov<0xB1>(nan));
+    d = nan != 0.f ? __builtin_nanf("") : m / 127.0f;
+    const bool ok = d > 0.f && d < INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float v = ok ? fminf(fmaxf(roundf(x[4 * j + b] / d), -127.f), 127.f) : 0.f;
+            w |= ((uint32_t)(int)v & 0xffu) << (8 * b);
+        }
+        q[j] = w;
+    }
+}
+
+// One lane's 16 products of int8 weight codes and activation codes summed in int32 (at most 16 * 127 * 127),
+// converted to f32 and scaled by both block scales.
+__device__ __forceinline__ float dot16_a8(const uint4 &w, const uint32_t (&q)[4], float sw, float da) {
+    int acc = __builtin_amdgcn_sdot4((int)w.x, (int)q[0], 0, false);
+    acc = __builtin_amdgcn_sdot4((int)w.y, (int)q[1], acc, false);
+    acc = __builtin_amdgcn_sdot4((int)w.z, (int)q[2], acc, false);
+    acc = __builtin_amdgcn_sdot4((int)w.w, (int)q[3], acc, false);
+    return (float)acc * (sw * da);
+}
+
+// dot_lds for q8 x q8: the lane's 16-element slices of the LDS input vector quantized, then int8 products.
+template <int C>
+__device__ __forceinline__ float dot_lds_a8(const uint4 (&wv)[C], const float (&sc)[C], const float *xl, int nch,
+                                            int lane) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        if (c < nch) {
+            const float4 *xp = (const float4 *)(xl + c * 64 * 16 + lane * 16);
+            float xv[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = xp[q];
+                xv[4 * q] = v.x, xv[4 * q + 1] = v.y, xv[4 * q + 2] = v.z, xv[4 * q + 3] = v.w;
+            }
+            uint32_t aq[4];
+            float ad;
+            quant16(xv, aq, ad);
+            acc += dot16_a8(wv[c], aq, sc[c], ad);
+        }
+    }
+    return acc;
+}
+
 // Cached K/V of one chunk of four 4-position quads for this lane: positions 4*(q0 + i) + lane/16, dims
 // (lane%16)*8..+8.  Always eight loads: slots of quads at or after qe, or of positions at or after `pos` (the new
 // position is written in this launch and taken from LDS), read position 0 and are never used.
@@ -497,8 +561,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             float xr[CH][E];
             rms_slice<Q8, CH>(xs, nq, a.eps, lane, xr);
             float d[RQ_MAX];
+            if constexpr (Q8 == 2) {
+                uint32_t aq[CH][4];
+                float ad[CH];
 #pragma unroll
-            for (int j = 0; j < RQ_MAX; ++j) d[j] = wave_sum_fast(dot_reg<Q8, CH>(wq[j], sq[j], xr));
+                for (int c = 0; c < CH; ++c) quant16(xr[c], aq[c], ad[c]);
+#pragma unroll
+                for (int j = 0; j < RQ_MAX; ++j) {
+                    float t = 0.f;
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) t += dot16_a8(wq[j][c], aq[c], sq[j][c], ad[c]);
+                    d[j] = wave_sum_fast(t);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < RQ_MAX; ++j) d[j] = wave_sum_fast(dot_reg<Q8, CH>(wq[j], sq[j], xr));
+            }
 #pragma unroll
             for (int j = 0; j < RQ_MAX; ++j)
                 if (lane == j && rqv[j]) put(a.qkv + rq[j], d[j], tag(l, 0));
@@ -706,7 +784,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const bool ok = poll<8>([&](int i) { return src + xw_index(i); }, q_dim, tag(l, 2), big, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
             QW3_STAMP(l, 3, 0);
-            const float d = wave_sum_fast(dot_lds<Q8, KO_MAX>(wo[0], so[0], big, KO, lane));
+            const float d = wave_sum_fast(Q8 == 2 ? dot_lds_a8<KO_MAX>(wo[0], so[0], big, KO, lane)
+                                                  : dot_lds<Q8, KO_MAX>(wo[0], so[0], big, KO, lane));
             x_own = x_own + d;
             if (lane == 0) put(a.xo + xw_index(gw), x_own, tag(l, 3));
         }
@@ -722,10 +801,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             float xr[CH][E];
             rms_slice<Q8, CH>(xs, nu, a.eps, lane, xr);
             float av[RU_MAX];
+            uint32_t aq[CH][4];
+            float ad[CH];
+            if constexpr (Q8 == 2) {
+#pragma unroll
+                for (int c = 0; c < CH; ++c) quant16(xr[c], aq[c], ad[c]);
+            }
+            auto udot = [&](int r) {
+                if constexpr (Q8 == 2) {
+                    float t = 0.f;
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) t += dot16_a8(wu[r][c], aq[c], su[r][c], ad[c]);
+                    return t;
+                } else {
+                    return dot_reg<Q8, CH>(wu[r], su[r], xr);
+                }
+            };
 #pragma unroll
             for (int j = 0; j < RU_MAX; ++j) {
-                const float gt = wave_sum_fast(dot_reg<Q8, CH>(wu[2 * j], su[2 * j], xr));
-                const float up = wave_sum_fast(dot_reg<Q8, CH>(wu[2 * j + 1], su[2 * j + 1], xr));
+                const float gt = wave_sum_fast(udot(2 * j));
+                const float up = wave_sum_fast(udot(2 * j + 1));
                 // SwiGLU, [P1] section 5: (g * sigmoid(g)) * u with sigmoid(g) = 1 / (1 + exp(-g)), on the
                 // transcendental unit (2^x and reciprocal, each within about 1 ulp)
                 const float sig = __builtin_amdgcn_rcpf(1.0f + exp2_hw(-gt * 1.4426950408889634f));
@@ -748,7 +843,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const bool ok = poll<kMegaBuf / 256>([&](int i) { return src + xw_index(i); }, I, tag(l, 4), big, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
             QW3_STAMP(l, 5, 0);
-            const float d = wave_sum_fast(dot_lds<Q8, KD_MAX>(wd[0], sd[0], big, KD, lane));
+            const float d = wave_sum_fast(Q8 == 2 ? dot_lds_a8<KD_MAX>(wd[0], sd[0], big, KD, lane)
+                                                  : dot_lds<Q8, KD_MAX>(wd[0], sd[0], big, KD, lane));
             x_own = x_own + d;
             if (lane == 0) {
                 if (l + 1 < a.L)
@@ -789,13 +885,17 @@ bool mega_supported(const Dims &d) {
 // the current device holds at least kMegaGrid of these workgroups at one time (compute units times the
 // occupancy the kernel's registers and LDS allow).  A device that cannot (fewer compute units, a partitioned
 // GPU) takes the kernel-by-kernel path instead.
-bool mega_resident(bool q8, int G) {
+bool mega_resident(int wmode, int G) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return false;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
     const void *fn = nullptr;
 #define QW3_MEGA_FN(Q, GG) fn = reinterpret_cast<const void *>(&decode_mega_kernel<Q, GG>)
-    if (q8) {
+    if (wmode == 2) {
+        if (G == 1) QW3_MEGA_FN(2, 1);
+        else if (G == 2) QW3_MEGA_FN(2, 2);
+        else if (G == 4) QW3_MEGA_FN(2, 4);
+    } else if (wmode == 1) {
         if (G == 1) QW3_MEGA_FN(1, 1);
         else if (G == 2) QW3_MEGA_FN(1, 2);
         else if (G == 4) QW3_MEGA_FN(1, 4);
@@ -813,10 +913,17 @@ bool mega_resident(bool q8, int G) {
     return (long long)per_cu * cus >= kMegaGrid;
 }
 
-hipError_t launch_decode_mega(bool q8, int G, const MegaArgs &a, hipStream_t st) {
+hipError_t launch_decode_mega(int wmode, int G, const MegaArgs &a, hipStream_t st) {
     const dim3 grid(kMegaGrid), block(kWaves * 64);
 #define QW3_MEGA(Q, GG) hipLaunchKernelGGL((decode_mega_kernel<Q, GG>), grid, block, 0, st, a)
-    if (q8) {
+    if (wmode == 2) {
+        switch (G) {
+            case 1: QW3_MEGA(2, 1); break;
+            case 2: QW3_MEGA(2, 2); break;
+            case 4: QW3_MEGA(2, 4); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else if (wmode == 1) {
         switch (G) {
             case 1: QW3_MEGA(1, 1); break;
             case 2: QW3_MEGA(1, 2); break;
