@@ -266,11 +266,11 @@ def run_bf16_decode(args, torch, q, synth, stream):
             "prefill128_hbm_GBps": round(pre_bytes / pd["median"] / 1e3, 1)}
 
 
-def run_q8_0_decode(args, torch, q, synth, stream):
-    """The 28-layer decode at KV context 2048 with the weights given as Q8_0 blocks (f16 scales)."""
+def run_q8_variant_decode(args, torch, q, synth, stream, fmt, workload):
+    """The 28-layer decode at KV context 2048 with the Q8 weights in another weight format."""
     wl = synth.Q8_DECODE
     from dataclasses import replace
-    shp = replace(wl.shape, fmt=synth.FMT_Q8_0)
+    shp = replace(wl.shape, fmt=fmt)
     W = synth.make_weights(shp, seed=wl.seed)
     m = q.Model(q.make_config(**synth.abi_config_kwargs(shp)), device="cuda:0")
     m.load_weights(synth.abi_tensors(W))
@@ -284,9 +284,7 @@ def run_q8_0_decode(args, torch, q, synth, stream):
     del m
     torch.cuda.empty_cache()
     d = percentiles(td)
-    return {"workload": "as the headline, weights given as Q8_0 34-byte blocks (f16 scale); the packer widens "
-                        "the scales to f32, so the device streams the same bytes",
-            "tok_s": round(1e6 / d["median"], 1), "step_us": d}
+    return {"workload": workload, "tok_s": round(1e6 / d["median"], 1), "step_us": d}
 
 
 def run_single_block(args, torch, q, synth, stream):
@@ -497,7 +495,14 @@ def main():
         with torch.cuda.stream(side):
             for key, fn in (("probes", lambda: run_probes(torch, q, side)),
                             ("bf16_b1", lambda: run_bf16_decode(args, torch, q, synth, side)),
-                            ("q8_0_b1", lambda: run_q8_0_decode(args, torch, q, synth, side)),
+                            ("q8_0_b1", lambda: run_q8_variant_decode(
+                                args, torch, q, synth, side, synth.FMT_Q8_0,
+                                "as the headline, weights given as Q8_0 34-byte blocks (f16 scale); the packer "
+                                "widens the scales to f32, so the device streams the same bytes")),
+                            ("q8xq8_b1", lambda: run_q8_variant_decode(
+                                args, torch, q, synth, side, synth.FMT_Q8_ACT8,
+                                "as the headline, with q8 x q8 layer products: activations quantized to int8 "
+                                "per 32-block, int8 dot products (lm_head keeps f32 activations)")),
                             ("single_block", lambda: run_single_block(args, torch, q, synth, side)),
                             ("sampler", lambda: run_sampler(torch, q, synth, side))):
                 t0 = time.time()

@@ -26,7 +26,11 @@ constexpr int kStatusF16Range = 8;     // a cached key or value overflowed the f
 // dense.
 constexpr int kXwLine = 128;
 __host__ __device__ inline int xw_index(int i) { return (i >> 4) * kXwLine + (i & 15); }  // 32-bit: keeps the poll addressing in 32-bit offsets
-inline uint64_t xw_words(int n) { return (uint64_t)((n + 15) / 16) * kXwLine; }
+// Those words are written in kXwReps copies, one per XCD: every workgroup polls its own XCD's copy, so a line
+// is polled by 32 workgroups instead of 256.  Copy r of an n-word vector starts r * xw_rep(n) words in.
+constexpr int kXwReps = 8;
+__host__ __device__ inline int xw_rep(int n) { return ((n + 15) / 16) * kXwLine; }
+inline uint64_t xw_words(int n) { return (uint64_t)xw_rep(n) * kXwReps; }
 
 // Byte offsets of every region inside the caller's arena.  Per-layer weight blocks repeat with a fixed
 // stride, so layer l's block starts at layer0 + l * layer_stride.

@@ -439,6 +439,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int KD_MAX = Q8 ? 3 : 6;   // intermediate <= 3072
     constexpr int RQ_MAX = 4;            // Q/K/V rows per wave (<= 4096 rows)
     constexpr int RU_MAX = 3;            // gate/up units per wave (<= 3072 units)
+    static_assert(kXwReps <= 32, "one lane of a half wave per copy of a published word");
     constexpr int PW = 2 + kHeadDim;     // words of one attention partial (max, sum, o[128])
 
     __shared__ __attribute__((aligned(16))) float xs[kHid];
@@ -483,6 +484,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // places on XCD g), the Q/K/V rows of KV head g and the split merge of its query heads go to the same
     // workgroups' XCD: measured slightly faster.  Placement only: every exchange stays device-coherent.
     const bool xcd_local = HKV == 8 && G == 2;
+    const int xrep = b & (kXwReps - 1);  // the copy of the all-gathered words this workgroup polls (its XCD's)
     int rq[RQ_MAX];
     bool rqv[RQ_MAX];
 #pragma unroll
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const uint16_t *vb = a.vcache + (size_t)l * a.kv_layer_stride + kv_head_off;
         // ================= Q: RMSNorm + Q/K/V rows
         if (l > 0) {
-            const uint64_t *src = a.xd;
+            const uint64_t *src = a.xd + xrep * xw_rep(kHid);
             const bool ok = poll<4>([&](int i) { return src + xw_index(i); }, kHid, tag(l - 1, 5), xs, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
         }
@@ -737,7 +739,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 const size_t base = ((size_t)(gh * SP + s) * G + hh) * PW;
                 return part + base + (j < 2 ? j : 2 + dc * dpw + (j - 2));
             };
-            const bool ok = poll<kMegaBuf / 256>(src, SP * per, tag(l, 1), big, a.status);
+            // SP * per = 512 / HKV + 128 G words at most (one KV head): (512 + 128 G) / 256 per thread
+            static_assert(512 + 128 * G <= kMegaBuf, "merge inputs fit the LDS buffer");
+            const bool ok = poll<(512 + 128 * G + 255) / 256>(src, SP * per, tag(l, 1), big, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
             QW3_STAMP(l, 2, 0);
             // exact combination (split order fixed by the reduction tree): M = max m_s,
@@ -755,7 +759,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 const float rl = row16_sum(f * ls), ro = row16_sum(f * os);
                 const float Ls = hi ? lane_get(rl, 32) + lane_get(rl, 48) : lane_get(rl, 0) + lane_get(rl, 16);
                 const float O = hi ? lane_get(ro, 32) + lane_get(ro, 48) : lane_get(ro, 0) + lane_get(ro, 16);
-                if ((lane & 31) == 0) put(a.attn + xw_index(h * kHeadDim + dc * dpw + e), O / Ls, tag(l, 2));
+                if ((lane & 31) < kXwReps)
+                    put(a.attn + (lane & 31) * xw_rep(q_dim) + xw_index(h * kHeadDim + dc * dpw + e), O / Ls, tag(l, 2));
             } else {
                 for (int e = wave; e < dpw; e += kWaves) {
                     float M = -INFINITY;
@@ -770,7 +775,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     }
                     Ls = wave_sum_fast(Ls);
                     O = wave_sum_fast(O);
-                    if (lane == 0) put(a.attn + xw_index(h * kHeadDim + dc * dpw + e), O / Ls, tag(l, 2));
+                    if (lane < kXwReps)
+                        put(a.attn + lane * xw_rep(q_dim) + xw_index(h * kHeadDim + dc * dpw + e), O / Ls, tag(l, 2));
                 }
             }
         }
@@ -780,21 +786,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
         // ================= O: o_proj + residual on the owned row
         {
-            const uint64_t *src = a.attn;
+            const uint64_t *src = a.attn + xrep * xw_rep(q_dim);
             const bool ok = poll<8>([&](int i) { return src + xw_index(i); }, q_dim, tag(l, 2), big, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
             QW3_STAMP(l, 3, 0);
             const float d = wave_sum_fast(Q8 == 2 ? dot_lds_a8<KO_MAX>(wo[0], so[0], big, KO, lane)
                                                   : dot_lds<Q8, KO_MAX>(wo[0], so[0], big, KO, lane));
             x_own = x_own + d;
-            if (lane == 0) put(a.xo + xw_index(gw), x_own, tag(l, 3));
+            if (lane < kXwReps) put(a.xo + lane * xw_rep(kHid) + xw_index(gw), x_own, tag(l, 3));
         }
         QW3_STAMP(l, 3, 1);
         load_rows<Q8, 1, KD_MAX>(lb + a.wd, (const float *)(lb + a.sd), I, ro, rov, KD, lane, wd, sd);
 
         // ================= U: RMSNorm + gate/up + SwiGLU
         {
-            const uint64_t *src = a.xo;
+            const uint64_t *src = a.xo + xrep * xw_rep(kHid);
             const bool ok = poll<4>([&](int i) { return src + xw_index(i); }, kHid, tag(l, 3), xs, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
             QW3_STAMP(l, 4, 0);
@@ -828,7 +834,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
 #pragma unroll
             for (int j = 0; j < RU_MAX; ++j)
-                if (lane == j && ruv[2 * j]) put(a.act + xw_index(ru[2 * j]), av[j], tag(l, 4));
+                if (lane < kXwReps && ruv[2 * j]) put(a.act + lane * xw_rep(I) + xw_index(ru[2 * j]), av[j], tag(l, 4));
         }
         QW3_STAMP(l, 4, 1);
         if (l + 1 < a.L) {
@@ -839,18 +845,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
         // ================= D: down + residual on the owned row
         {
-            const uint64_t *src = a.act;
+            const uint64_t *src = a.act + xrep * xw_rep(I);
             const bool ok = poll<kMegaBuf / 256>([&](int i) { return src + xw_index(i); }, I, tag(l, 4), big, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
             QW3_STAMP(l, 5, 0);
             const float d = wave_sum_fast(Q8 == 2 ? dot_lds_a8<KD_MAX>(wd[0], sd[0], big, KD, lane)
                                                   : dot_lds<Q8, KD_MAX>(wd[0], sd[0], big, KD, lane));
             x_own = x_own + d;
-            if (lane == 0) {
-                if (l + 1 < a.L)
-                    put(a.xd + xw_index(gw), x_own, tag(l, 5));
-                else
-                    a.x_out[gw] = x_own;
+            if (l + 1 < a.L) {
+                if (lane < kXwReps) put(a.xd + lane * xw_rep(kHid) + xw_index(gw), x_own, tag(l, 5));
+            } else if (lane == 0) {
+                a.x_out[gw] = x_own;
             }
         }
         QW3_STAMP(l, 5, 1);
