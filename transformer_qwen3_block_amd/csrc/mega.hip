@@ -38,6 +38,12 @@ constexpr int kHid = 1024;               // hidden size of this kernel (= kNW: o
 // 2^18 rounds outlast 50 ms while a legitimate wait lasts microseconds.
 constexpr int kPollRounds = 1 << 18;
 constexpr int kMegaBuf = 3072;  // floats per LDS input buffer (largest phase input: intermediate <= 3072)
+// Quads (4 positions) per attention chunk.  With G <= 2 query heads per KV head a pass covers 20 positions per
+// wave, so up to 2560 cached positions (128 wave slots) take a single online-softmax pass in every wave, and
+// past 2048 no wave needs a second pass for the one quad left over from an even share of four.  Four query heads
+// per KV head keep chunks of four quads (registers).
+template <int G>
+constexpr int chunk_quads() { return G <= 2 ? 5 : 4; }
 
 static_assert(kHid == kNW, "one hidden row per wave");
 
@@ -312,14 +318,15 @@ __device__ __forceinline__ float dot_lds_a8(const uint4 (&wv)[C], const float (&
     return acc;
 }
 
-// Cached K/V of one chunk of four 4-position quads for this lane: positions 4*(q0 + i) + lane/16, dims
-// (lane%16)*8..+8.  Always eight loads: slots of quads at or after qe, or of positions at or after `pos` (the new
-// position is written in this launch and taken from LDS), read position 0 and are never used.
+// Cached K/V of one chunk of CQ 4-position quads for this lane: positions 4*(q0 + i) + lane/16, dims
+// (lane%16)*8..+8.  Always 2 * CQ loads: slots of quads at or after qe, or of positions at or after `pos`
+// (the new position is written in this launch and taken from LDS), read position 0 and are never used.
+template <int CQ>
 __device__ __forceinline__ void load_chunk(const uint16_t *kb, const uint16_t *vb, int q0, int qe, int pos,
-                                           int lane, uint4 (&kr)[4], uint4 (&vr)[4]) {
+                                           int lane, uint4 (&kr)[CQ], uint4 (&vr)[CQ]) {
     const int dsub = (lane & 15) * 8, prow = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CQ; ++i) {
         const int p = 4 * (q0 + i) + prow;
         const size_t pc = (q0 + i < qe && p < pos) ? (size_t)p : 0;
         kr[i] = load_nt16(kb + pc * kHeadDim + dsub);
@@ -330,11 +337,11 @@ __device__ __forceinline__ void load_chunk(const uint16_t *kb, const uint16_t *v
 // 2^x on the transcendental unit (one v_exp_f32; exactly 0 at -inf).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Online-softmax update with one chunk of cached positions: NQ quads (1..4) starting at quad q0 ([P1] section 2
+// Online-softmax update with one chunk of cached positions: NQ quads (1..5) starting at quad q0 ([P1] section 2
 // item 5; running max m, running sum l, unnormalised accumulator acc; each lane row keeps its own l and acc).
 // Scores are in log2 units (the scale sl2 carries log2(e)), so every exponential is a single 2^x.
-template <int G, int NQ>
-__device__ __forceinline__ void attend_chunk(uint4 (&kr)[4], uint4 (&vr)[4], int q0, int pos, int lane,
+template <int G, int NQ, int CQ>
+__device__ __forceinline__ void attend_chunk(uint4 (&kr)[CQ], uint4 (&vr)[CQ], int q0, int pos, int lane,
                                              const float (&qr)[G][8], float sl2, float (&m)[G], float (&l)[G],
                                              float (&acc)[G][8]) {
     const int prow = lane >> 4;
@@ -387,16 +394,18 @@ __device__ __forceinline__ void attend_chunk(uint4 (&kr)[4], uint4 (&vr)[4], int
     }
 }
 
-// attend_chunk for a run of nq quads (the same in every lane): full chunks take the four-quad form, the last
+// attend_chunk for a run of nq quads (the same in every lane): full chunks take the CQ-quad form, the last
 // chunk of a run its own length
-template <int G>
-__device__ __forceinline__ void attend_run(uint4 (&kr)[4], uint4 (&vr)[4], int q0, int nq, int pos, int lane,
+template <int G, int CQ>
+__device__ __forceinline__ void attend_run(uint4 (&kr)[CQ], uint4 (&vr)[CQ], int q0, int nq, int pos, int lane,
                                            const float (&qr)[G][8], float sl2, float (&m)[G], float (&l)[G],
                                            float (&acc)[G][8]) {
-    if (nq >= 4) attend_chunk<G, 4>(kr, vr, q0, pos, lane, qr, sl2, m, l, acc);
-    else if (nq == 3) attend_chunk<G, 3>(kr, vr, q0, pos, lane, qr, sl2, m, l, acc);
-    else if (nq == 2) attend_chunk<G, 2>(kr, vr, q0, pos, lane, qr, sl2, m, l, acc);
-    else if (nq == 1) attend_chunk<G, 1>(kr, vr, q0, pos, lane, qr, sl2, m, l, acc);
+    static_assert(CQ == 4 || CQ == 5, "chunks of four or five quads");
+    if (nq >= CQ) attend_chunk<G, CQ, CQ>(kr, vr, q0, pos, lane, qr, sl2, m, l, acc);
+    else if (CQ == 5 && nq == 4) attend_chunk<G, 4, CQ>(kr, vr, q0, pos, lane, qr, sl2, m, l, acc);
+    else if (nq == 3) attend_chunk<G, 3, CQ>(kr, vr, q0, pos, lane, qr, sl2, m, l, acc);
+    else if (nq == 2) attend_chunk<G, 2, CQ>(kr, vr, q0, pos, lane, qr, sl2, m, l, acc);
+    else if (nq == 1) attend_chunk<G, 1, CQ>(kr, vr, q0, pos, lane, qr, sl2, m, l, acc);
 }
 
 // Online-softmax update with the new position (key kn, value vn in LDS, already rounded to bf16); lane row 0
@@ -462,7 +471,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // this workgroup's attention share: KV head g, split sp.  The cached positions [0, pos) form quads of four;
     // wave slot ws = 4 sp + wave takes a contiguous run of quads [qa, qe), floor(quads / nslot) of them plus one
     // for the first quads % nslot slots, so no wave holds more than one quad beyond the others.  The runs are
-    // processed four quads (16 positions) at a time.  The new position goes to the last slot, which never holds
+    // processed chunk_quads<G>() quads (20 or 16 positions) at a time.  The new position goes to the last slot, which never holds
     // an extra quad, and its workgroup appends it to the cache.
     const int g = b % HKV, sp = b / HKV;
     const int nslot = kWaves * SP, ws = __builtin_amdgcn_readfirstlane(sp * kWaves + wave);
@@ -519,7 +528,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float su[2 * RU_MAX][CH];
     uint4 wd[1][KD_MAX];
     float sd[1][KD_MAX];
-    uint4 kA[4], vA[4], kB[4], vB[4];  // cached K/V of the wave's first two chunks
+    constexpr int CQ = chunk_quads<G>();
+    uint4 kA[CQ], vA[CQ], kB[CQ], vB[CQ];  // cached K/V of the wave's first two chunks
     float nq[CH][E], nu[CH][E];  // RMSNorm weight slices of the Q and U phases
     float qkn[4], rcs[2];        // QK-Norm weights (q: lane, lane + 64; k: same) and this position's cos/sin
 
@@ -593,9 +603,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             rcs[0] = a.rope_cos[(size_t)pos * (kHeadDim / 2) + lane];
             rcs[1] = a.rope_sin[(size_t)pos * (kHeadDim / 2) + lane];
             load_chunk(kb, vb, qa, qe, pos, lane, kA, vA);
-            // a second chunk (contexts past 16 positions per wave slot) is in flight before the poll too, so no
+            // a second chunk (contexts past one chunk per wave slot) is in flight before the poll too, so no
             // wave waits for a load after its inputs arrive
-            if (qa + 4 < qe) load_chunk(kb, vb, qa + 4, qe, pos, lane, kB, vB);
+            if (qa + CQ < qe) load_chunk(kb, vb, qa + CQ, qe, pos, lane, kB, vB);
         }
 
         // ================= A: QK-Norm + RoPE + append + attention over this split
@@ -666,17 +676,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
             }
-            // the first two chunks were prefetched; later chunks (contexts past 32 positions per wave slot)
+            // the first two chunks were prefetched; later chunks (contexts past two chunks per wave slot)
             // stream one ahead
             attend_run<G>(kA, vA, qa, qe - qa, pos, lane, qr, sl2, m, lsum, acc);
-            for (int q0 = qa + 4; q0 < qe; q0 += 4) {
-                const bool more = q0 + 4 < qe;
-                uint4 kN[4], vN[4];
-                if (more) load_chunk(kb, vb, q0 + 4, qe, pos, lane, kN, vN);
+            for (int q0 = qa + CQ; q0 < qe; q0 += CQ) {
+                const bool more = q0 + CQ < qe;
+                uint4 kN[CQ], vN[CQ];
+                if (more) load_chunk(kb, vb, q0 + CQ, qe, pos, lane, kN, vN);
                 attend_run<G>(kB, vB, q0, qe - q0, pos, lane, qr, sl2, m, lsum, acc);
                 if (!more) break;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < CQ; ++i) {
                     kB[i] = kN[i];
                     vB[i] = vN[i];
                 }
