@@ -65,24 +65,26 @@ def timed(torch, stream, fn, reps):
 
 
 def run_env(torch):
-    """What the numbers were measured on: device, ROCm / HIP / compiler versions, clocks."""
-    import subprocess
-    env = {"device": torch.cuda.get_device_name(0), "torch": torch.__version__, "hip_runtime": torch.version.hip}
+    """What the numbers were measured on: device, ROCm / HIP versions, build flags and the device's clock levels
+    (files only: no helper program is started from this GPU process)."""
+    import glob
+    props = torch.cuda.get_device_properties(0)
+    env = {"device": torch.cuda.get_device_name(0), "arch": props.gcnArchName, "cus": props.multi_processor_count,
+           "torch": torch.__version__, "hip_runtime": torch.version.hip}
     try:
-        env["rocm"] = open("/opt/rocm/.info/version").read().strip()
+        env["rocm"] = open("/opt/rocm/.info/version-dev").read().strip()
     except OSError:
         pass
-    for key, cmd in (("hipcc", ["/opt/rocm/bin/hipcc", "--version"]),
-                     ("clocks", ["rocm-smi", "--showclocks"])):
+    # current engine / memory clock levels ('*' marks the active one) of the card on this PCI bus
+    bus = f"{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}"
+    for dev in glob.glob("/sys/class/drm/card*/device"):
         try:
-            outp = subprocess.run(cmd, capture_output=True, text=True, timeout=30).stdout
-            lines = [ln.strip() for ln in outp.splitlines() if ln.strip() and not ln.startswith("=")]
-            if key == "hipcc":
-                env[key] = next((ln for ln in lines if "clang version" in ln or "HIP version" in ln), None)
-            else:
-                env[key] = [ln for ln in lines if "Mhz" in ln or "MHz" in ln][:6]
-        except (OSError, subprocess.SubprocessError):
-            env[key] = None
+            if bus not in open(dev + "/uevent").read():
+                continue
+            env["clocks"] = {k: [ln.strip() for ln in open(f"{dev}/pp_dpm_{k}") if "*" in ln]
+                             for k in ("sclk", "mclk")}
+        except OSError:
+            pass
     import transformer_qwen3_block_amd as q
     env["hipcc_flags"] = " ".join(q.HIPCC_FLAGS)
     return env
