@@ -86,7 +86,7 @@ enum { QW3_INPUT_TOKENS = 0, QW3_INPUT_HIDDEN = 1 };
  * no final norm, no logits; vocab_size must be 0). */
 typedef struct qw3_config {
     uint32_t abi_version;   /* must equal QW3_ABI_VERSION */
-    uint32_t weight_format; /* QW3_WEIGHTS_BF16 or QW3_WEIGHTS_Q8 */
+    uint32_t weight_format; /* QW3_WEIGHTS_BF16, QW3_WEIGHTS_Q8, QW3_WEIGHTS_Q8_0 or QW3_WEIGHTS_Q8_ACT8 */
     uint32_t input_mode;    /* QW3_INPUT_TOKENS or QW3_INPUT_HIDDEN */
     int32_t vocab_size;
     int32_t hidden;
