@@ -86,6 +86,12 @@ def test_prefill_several_tiles():
     _prefill_vs_oracle(replace(SMALL, max_prefill=48), seed=32, T=130, decode_steps=2)
 
 
+def test_prefill_single_token_tiles_bf16():
+    """A bf16 model configured with one-token prefill tiles has no MFMA prefill: its prompt runs token by token
+    through the decode path (f32 activations), and the logits and cache still match the oracle."""
+    _prefill_vs_oracle(replace(SMALL, max_prefill=1), seed=37, T=12, decode_steps=2)
+
+
 @pytest.mark.parametrize("chunk,T", [(300, 610), (128, 300), (100, 290)])
 def test_prefill_chunks_every_projection_path(chunk, T):
     """Chunked prefill through every projection path: chunks of more than 64 tokens take the fused Q/K/V

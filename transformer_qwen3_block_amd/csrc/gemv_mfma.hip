@@ -345,12 +345,16 @@ hipError_t launch_gemv_mfma(GemvEpi epi, const GemvArgs &a, hipStream_t st) {
     if (!gemv_mfma_supported(a, epi)) return hipErrorInvalidValue;
     switch (epi) {
         case EPI_STORE: {
+            // one tile per workgroup while the tiles fit the compute units in one round (Q/K/V: 256 tiles,
+            // measured 7.5 us against 8.8 us for two tiles per workgroup); two beyond that
             const int ntiles = (a.N + 15) / 16;
-            hipLaunchKernelGGL((gemv_mfma_kernel<4, 8, EPI_STORE>), dim3(ntiles > 128 ? (ntiles + 1) / 2 : ntiles),
+            hipLaunchKernelGGL((gemv_mfma_kernel<4, 8, EPI_STORE>), dim3(ntiles > 256 ? (ntiles + 1) / 2 : ntiles),
                                dim3(256), 0, st, a);
             break;
         }
         case EPI_SWIGLU: {
+            // 384 tiles for the 3072-unit MLP: two per workgroup (one per workgroup, 384 workgroups on 256 compute
+            // units, measured 11.4 us against 9.2 us)
             const int ntiles = a.N / 8;
             hipLaunchKernelGGL((gemv_mfma_kernel<4, 8, EPI_SWIGLU>), dim3(ntiles > 128 ? (ntiles + 1) / 2 : ntiles),
                                dim3(256), 0, st, a);
