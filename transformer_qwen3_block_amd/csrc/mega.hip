@@ -256,33 +256,9 @@ __device__ __forceinline__ void rms_slice(const float *xs, const float (&w)[CH][
 
 // ---- q8 x q8 products (weight mode 2): activations quantized to int8 per 32-block on the fly ([P3] section 5
 // "Q8_0 Mixed-Precision Matrix Multiplication") -------------------------------------------------------------
-// A lane holds 16 consecutive activations, half of a 32-block (lane ^ 1 holds the other half): the block scale is
-// d = max|x| / 127 over both halves, each code rounds x / d to nearest (ties away from zero) and is clamped to
-// [-127, 127].  A NaN in the block makes d NaN; a block whose d is zero or not finite gets zero codes, so a
-// non-finite input reaches the products through d instead of being repaired.
-__device__ __forceinline__ void quant16(const float (&x)[16], uint32_t (&q)[4], float &d) {
-    float m = 0.f, nan = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const float a = fabsf(x[e]);
-        nan = a != a ? 1.f : nan;
-        m = fmaxf(m, a);
-    }
-    m = fmaxf(m, dpp_mov<0xB1>(m));  // the partner lane's half of the block
-    nan = fmaxf(nan, dpp_mov<0xB1>(nan));
-    d = nan != 0.f ? __builtin_nanf("") : m / 127.0f;
-    const bool ok = d > 0.f && d < INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const float v = ok ? fminf(fmaxf(roundf(x[4 * j + b] / d), -127.f), 127.f) : 0.f;
-            w |= ((uint32_t)(int)v & 0xffu) << (8 * b);
-        }
-        q[j] = w;
-    }
-}
+// The block scale is d = max|x| / 127 over the block's 32 inputs, each code rounds x / d to nearest (ties away
+// from zero) and is clamped to [-127, 127].  A NaN in the block makes d NaN; a block whose d is zero or not
+// finite gets zero codes, so a non-finite input reaches the products through d instead of being repaired.
 
 // One lane's 16 products of int8 weight codes and activation codes summed in int32 (at most 16 * 127 * 127),
 // converted to f32 and scaled by both block scales.
@@ -294,28 +270,77 @@ __device__ __forceinline__ float dot16_a8(const uint4 &w, const uint32_t (&q)[4]
     return (float)acc * (sw * da);
 }
 
-// dot_lds for q8 x q8: the lane's 16-element slices of the LDS input vector quantized, then int8 products.
+// The workgroup quantizes an n-element input (n a multiple of 1024) once, for all four waves: in each pass of
+// 1024 elements thread t takes elements 4t..4t+3, so a 32-block spans eight lanes of a row, whose max (and NaN
+// flag) three DPP steps share.  With NORM the elements are the RMSNorm outputs nw * (x * inv) of the pass, else
+// x itself.  Writes codes[k / 4] = the int8 codes of elements k..k+3 (lowest element in the lowest byte) and
+// dsc[k / 32] = the block scale.
+template <bool NORM>
+__device__ __forceinline__ void quant_wg(const float *x, int n, const float4 &nw, float inv, uint32_t *codes,
+                                         float *dsc) {
+    const int t = threadIdx.x;
+    for (int base = 0; base < n; base += 1024) {
+        const float4 r = *(const float4 *)(x + base + 4 * t);
+        float v[4] = {r.x, r.y, r.z, r.w};
+        if constexpr (NORM) {
+            v[0] = nw.x * (v[0] * inv);
+            v[1] = nw.y * (v[1] * inv);
+            v[2] = nw.z * (v[2] * inv);
+            v[3] = nw.w * (v[3] * inv);
+        }
+        float m = 0.f, nan = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a = fabsf(v[e]);
+            nan = a != a ? 1.f : nan;
+            m = fmaxf(m, a);
+        }
+        m = fmaxf(m, dpp_mov<0xB1>(m));   // quad_perm [1,0,3,2]
+        m = fmaxf(m, dpp_mov<0x4E>(m));   // quad_perm [2,3,0,1]
+        m = fmaxf(m, dpp_mov<0x141>(m));  // row_half_mirror: the other quad of the eight lanes
+        nan = fmaxf(nan, dpp_mov<0xB1>(nan));
+        nan = fmaxf(nan, dpp_mov<0x4E>(nan));
+        nan = fmaxf(nan, dpp_mov<0x141>(nan));
+        const float d = nan != 0.f ? __builtin_nanf("") : m / 127.0f;
+        const bool ok = d > 0.f && d < INFINITY;
+        uint32_t w = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float c = ok ? fminf(fmaxf(roundf(v[b] / d), -127.f), 127.f) : 0.f;
+            w |= ((uint32_t)(int)c & 0xffu) << (8 * b);
+        }
+        codes[(base >> 2) + t] = w;
+        if ((t & 7) == 0) dsc[(base >> 5) + (t >> 3)] = d;
+    }
+}
+
+// Lane's share of a q8 x q8 row product with the codes quant_wg left in LDS: chunk c holds elements
+// c*1024 + lane*16 .. +16, one 16-byte code read and the scale of their block.
 template <int C>
-__device__ __forceinline__ float dot_lds_a8(const uint4 (&wv)[C], const float (&sc)[C], const float *xl, int nch,
-                                            int lane) {
+__device__ __forceinline__ float dot_codes(const uint4 (&wv)[C], const float (&sc)[C], const uint32_t *codes,
+                                           const float *dsc, int nch, int lane) {
     float acc = 0.f;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         if (c < nch) {
-            const float4 *xp = (const float4 *)(xl + c * 64 * 16 + lane * 16);
-            float xv[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 v = xp[q];
-                xv[4 * q] = v.x, xv[4 * q + 1] = v.y, xv[4 * q + 2] = v.z, xv[4 * q + 3] = v.w;
-            }
-            uint32_t aq[4];
-            float ad;
-            quant16(xv, aq, ad);
-            acc += dot16_a8(wv[c], aq, sc[c], ad);
+            const uint4 q4 = *(const uint4 *)(codes + c * 256 + lane * 4);
+            const uint32_t q[4] = {q4.x, q4.y, q4.z, q4.w};
+            acc += dot16_a8(wv[c], q, sc[c], dsc[c * 32 + (lane >> 1)]);
         }
     }
     return acc;
+}
+
+// 1 / sqrt(mean(x^2) + eps) of the 1024-vector xs (LDS), the factor rms_slice applies, in every lane.
+__device__ __forceinline__ float rms_inv(const float *xs, float eps, int lane) {
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < kHid / 64; ++k) {
+        const float v = xs[lane + 64 * k];
+        ss += v * v;
+    }
+    ss = wave_sum_fast(ss);
+    return 1.0f / sqrtf(ss / (float)kHid + eps);
 }
 
 // Cached K/V of one chunk of CQ 4-position quads for this lane: positions 4*(q0 + i) + lane/16, dims
@@ -456,6 +481,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __shared__ __attribute__((aligned(16))) float wacc[kWaves * 4 * G * kHeadDim];  // [wave][lane row][G][128]
     __shared__ float wm[kWaves][G], wl[kWaves][4][G];
     __shared__ int s_fail;
+    // q8 x q8 (Q8 == 2): the workgroup's int8 codes and block scales of the current phase input
+    __shared__ __attribute__((aligned(16))) uint32_t qcode[kMegaBuf / 4];
+    __shared__ float qdsc[kMegaBuf / 32];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int b = blockIdx.x;
@@ -531,11 +559,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int CQ = chunk_quads<G>();
     uint4 kA[CQ], vA[CQ], kB[CQ], vB[CQ];  // cached K/V of the wave's first two chunks
     float nq[CH][E], nu[CH][E];  // RMSNorm weight slices of the Q and U phases
+    float4 nq4, nu4;             // q8 x q8: the same weights for elements 4 tid .. 4 tid + 3 (quant_wg)
     float qkn[4], rcs[2];        // QK-Norm weights (q: lane, lane + 64; k: same) and this position's cos/sin
 
     // ---- prologue: layer-0 Q/K/V weights in flight, then the input vector (every workgroup builds it all)
     load_rows<Q8, RQ_MAX, CH>(a.layer0 + a.wqkv, (const float *)(a.layer0 + a.sqkv), kHid, rq, rqv, CH, lane, wq, sq);
-    load_slice<Q8, CH>((const float *)(a.layer0 + a.attn_norm), lane, nq);
+    if constexpr (Q8 == 2)
+        nq4 = *((const float4 *)(a.layer0 + a.attn_norm) + tid);
+    else
+        load_slice<Q8, CH>((const float *)(a.layer0 + a.attn_norm), lane, nq);
     if (a.token) {
         int tok = a.token[0];
         if (tok < 0 || tok >= a.V) {
@@ -570,22 +602,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         QW3_STAMP(l, 0, 0);
         {
-            float xr[CH][E];
-            rms_slice<Q8, CH>(xs, nq, a.eps, lane, xr);
             float d[RQ_MAX];
             if constexpr (Q8 == 2) {
-                uint32_t aq[CH][4];
-                float ad[CH];
+                quant_wg<true>(xs, kHid, nq4, rms_inv(xs, a.eps, lane), qcode, qdsc);
+                __syncthreads();
 #pragma unroll
-                for (int c = 0; c < CH; ++c) quant16(xr[c], aq[c], ad[c]);
-#pragma unroll
-                for (int j = 0; j < RQ_MAX; ++j) {
-                    float t = 0.f;
-#pragma unroll
-                    for (int c = 0; c < CH; ++c) t += dot16_a8(wq[j][c], aq[c], sq[j][c], ad[c]);
-                    d[j] = wave_sum_fast(t);
-                }
+                for (int j = 0; j < RQ_MAX; ++j) d[j] = wave_sum_fast(dot_codes<CH>(wq[j], sq[j], qcode, qdsc, CH, lane));
             } else {
+                float xr[CH][E];
+                rms_slice<Q8, CH>(xs, nq, a.eps, lane, xr);
 #pragma unroll
                 for (int j = 0; j < RQ_MAX; ++j) d[j] = wave_sum_fast(dot_reg<Q8, CH>(wq[j], sq[j], xr));
             }
@@ -792,7 +817,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         QW3_STAMP(l, 2, 1);
         load_rows<Q8, 2 * RU_MAX, CH>(lb + a.wgu, (const float *)(lb + a.sgu), kHid, ru, ruv, CH, lane, wu, su);
-        load_slice<Q8, CH>((const float *)(lb + a.mlp_norm), lane, nu);
+        if constexpr (Q8 == 2)
+            nu4 = *((const float4 *)(lb + a.mlp_norm) + tid);
+        else
+            load_slice<Q8, CH>((const float *)(lb + a.mlp_norm), lane, nu);
 
         // ================= O: o_proj + residual on the owned row
         {
@@ -800,7 +828,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const bool ok = poll<8>([&](int i) { return src + xw_index(i); }, q_dim, tag(l, 2), big, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
             QW3_STAMP(l, 3, 0);
-            const float d = wave_sum_fast(Q8 == 2 ? dot_lds_a8<KO_MAX>(wo[0], so[0], big, KO, lane)
+            if constexpr (Q8 == 2) {
+                quant_wg<false>(big, q_dim, float4{}, 0.f, qcode, qdsc);
+                __syncthreads();
+            }
+            const float d = wave_sum_fast(Q8 == 2 ? dot_codes<KO_MAX>(wo[0], so[0], qcode, qdsc, KO, lane)
                                                   : dot_lds<Q8, KO_MAX>(wo[0], so[0], big, KO, lane));
             x_own = x_own + d;
             if (lane < kXwReps) put(a.xo + lane * xw_rep(kHid) + xw_index(gw), x_own, tag(l, 3));
@@ -815,20 +847,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (!all_ok(ok, s_fail, a.status)) return;
             QW3_STAMP(l, 4, 0);
             float xr[CH][E];
-            rms_slice<Q8, CH>(xs, nu, a.eps, lane, xr);
-            float av[RU_MAX];
-            uint32_t aq[CH][4];
-            float ad[CH];
             if constexpr (Q8 == 2) {
-#pragma unroll
-                for (int c = 0; c < CH; ++c) quant16(xr[c], aq[c], ad[c]);
+                quant_wg<true>(xs, kHid, nu4, rms_inv(xs, a.eps, lane), qcode, qdsc);
+                __syncthreads();
+            } else {
+                rms_slice<Q8, CH>(xs, nu, a.eps, lane, xr);
             }
+            float av[RU_MAX];
             auto udot = [&](int r) {
                 if constexpr (Q8 == 2) {
-                    float t = 0.f;
-#pragma unroll
-                    for (int c = 0; c < CH; ++c) t += dot16_a8(wu[r][c], aq[c], su[r][c], ad[c]);
-                    return t;
+                    return dot_codes<CH>(wu[r], su[r], qcode, qdsc, CH, lane);
                 } else {
                     return dot_reg<Q8, CH>(wu[r], su[r], xr);
                 }
@@ -850,7 +878,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (l + 1 < a.L) {
             const uint8_t *nb = lblock(l + 1);
             load_rows<Q8, RQ_MAX, CH>(nb + a.wqkv, (const float *)(nb + a.sqkv), kHid, rq, rqv, CH, lane, wq, sq);
-            load_slice<Q8, CH>((const float *)(nb + a.attn_norm), lane, nq);
+            if constexpr (Q8 == 2)
+                nq4 = *((const float4 *)(nb + a.attn_norm) + tid);
+            else
+                load_slice<Q8, CH>((const float *)(nb + a.attn_norm), lane, nq);
         }
 
         // ================= D: down + residual on the owned row
@@ -859,7 +890,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const bool ok = poll<kMegaBuf / 256>([&](int i) { return src + xw_index(i); }, I, tag(l, 4), big, a.status);
             if (!all_ok(ok, s_fail, a.status)) return;
             QW3_STAMP(l, 5, 0);
-            const float d = wave_sum_fast(Q8 == 2 ? dot_lds_a8<KD_MAX>(wd[0], sd[0], big, KD, lane)
+            if constexpr (Q8 == 2) {
+                quant_wg<false>(big, I, float4{}, 0.f, qcode, qdsc);
+                __syncthreads();
+            }
+            const float d = wave_sum_fast(Q8 == 2 ? dot_codes<KD_MAX>(wd[0], sd[0], qcode, qdsc, KD, lane)
                                                   : dot_lds<Q8, KD_MAX>(wd[0], sd[0], big, KD, lane));
             x_own = x_own + d;
             if (l + 1 < a.L) {
