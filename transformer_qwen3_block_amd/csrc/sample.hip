@@ -156,6 +156,93 @@ __host__ __device__ __forceinline__ uint32_t pcg32_next(uint64_t &state, uint64_
     return (xs >> rot) | (xs << ((32u - rot) & 31u));
 }
 
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64), hi = (uint32_t)__shfl_xor((int)(v >> 32), m, 64);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// The 64 values of a wave (one per lane) sorted in descending order across the lanes: the bitonic network of
+// bitonic_desc with each compare-exchange between lane i and lane i ^ stride done in registers.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const uint64_t o = shfl_xor64(v, stride);
+            const bool keep_max = ((lane & size) == 0) == ((lane & stride) == 0);
+            v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+        }
+    return v;
+}
+
+// The steps after the top-k selection for up to 64 survivors, in wave 0: lane j holds candidate v = (key << 32 |
+// ~id) (0 past the survivors).  The same operations in the same order as the workgroup path below: every sum
+// runs over the candidates one by one (readlane), so the drawn token is the same.
+__device__ void finish_in_wave(const SampleArgs &a, int row, int k, uint64_t v) {
+    const int lane = threadIdx.x & 63;
+    v = wave_sort_desc(v);  // (value desc, id asc)
+    auto set_outputs = [&](int tok) {
+        if (lane == 0) {
+            a.token_out[row] = tok;
+            int done = 0;
+            for (int j = 0; j < a.n_stop; ++j) done |= a.stop[j] == tok;
+            if (a.done_out) a.done_out[row] = done;
+            if (a.status_out) a.status_out[row] = QW3_OK;
+        }
+    };
+    if (a.temperature == 0.f) {  // greedy: the greatest logit, lowest id on ties; no draw
+        set_outputs((int)(0xffffffffu - (uint32_t)readlane64(v, 0)));
+        return;
+    }
+    // stable probabilities over the k survivors ([P1] section 7)
+    const float m = key2f((uint32_t)(readlane64(v, 0) >> 32));
+    float e = 0.f;
+    const uint32_t id = 0xffffffffu - (uint32_t)v;
+    if (lane < k) e = (float)exp((double)(key2f((uint32_t)(v >> 32)) - m));
+    float s = 0.f;
+    for (int j = 0; j < k; ++j) s = s + readlane_f(e, j);
+    uint64_t w = lane < k ? ((uint64_t)__float_as_uint(e / s) << 32) | (uint64_t)(0xffffffffu - id) : 0ull;
+    w = wave_sort_desc(w);  // (probability desc, id asc)
+    const float pw = __uint_as_float((uint32_t)(w >> 32));
+    // top-p: the shortest prefix whose cumulative probability is at least p ([P4] "Sampling order")
+    float cum = 0.f;
+    int keep = k;
+    for (int j = 0; j < k; ++j) {
+        cum = cum + readlane_f(pw, j);
+        if (cum >= a.top_p) {
+            keep = j + 1;
+            break;
+        }
+    }
+    float s2 = 0.f;
+    for (int j = 0; j < keep; ++j) s2 = s2 + readlane_f(pw, j);
+    const float pr = lane < keep ? pw / s2 : 0.f;
+    uint64_t st = a.rng[2 * row];
+    const uint64_t inc = a.rng[2 * row + 1];
+    const float u = (float)(pcg32_next(st, inc) >> 8) * (1.0f / 16777216.0f);
+    float c2 = 0.f;
+    int pick = keep - 1;
+    for (int j = 0; j < keep; ++j) {
+        c2 = c2 + readlane_f(pr, j);
+        if (c2 > u) {
+            pick = j;
+            break;
+        }
+    }
+    const uint64_t chosen = readlane64(w, pick);
+    if (lane == 0) a.rng[2 * row] = st;
+    set_outputs((int)(0xffffffffu - (uint32_t)chosen));
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kThreads) void sample_chunk_kernel(SampleArgs a) {
@@ -254,15 +341,15 @@ __global__ __launch_bounds__(kThreads) void sample_finish_kernel(SampleArgs a) {
     const int tid = threadIdx.x, row = blockIdx.x;
     const uint32_t *ck = a.cand_key + (size_t)row * kSampleChunks * kSampleMaxTopK;
     const int *ci = a.cand_id + (size_t)row * kSampleChunks * kSampleMaxTopK;
-    if (tid == 0) {
-        int o = 0, bad = 0;
-        for (int c = 0; c < kSampleChunks; ++c) {
-            off[c] = o;
-            o += a.cand_cnt[row * kSampleChunks + c];
-            bad |= a.chunk_bad[row * kSampleChunks + c];
-        }
-        off[kSampleChunks] = o;
-        s_res[0] = bad;
+    static_assert(kSampleChunks <= 64, "one wave gathers the slices' counts");
+    if (tid < 64) {  // candidate counts of the slices -> offsets (a scan in slice order), and any failure
+        const int cnt = tid < kSampleChunks ? a.cand_cnt[row * kSampleChunks + tid] : 0;
+        const int bad = tid < kSampleChunks ? a.chunk_bad[row * kSampleChunks + tid] : 0;
+        const int inc = wave_incl_scan(cnt);
+        if (tid < kSampleChunks) off[tid] = inc - cnt;
+        if (tid == kSampleChunks - 1) off[kSampleChunks] = inc;
+        const uint64_t any_bad = __ballot(bad != 0);
+        if (tid == 0) s_res[0] = any_bad != 0;
     }
     __syncthreads();
     const int n = off[kSampleChunks];
@@ -275,8 +362,12 @@ __global__ __launch_bounds__(kThreads) void sample_finish_kernel(SampleArgs a) {
         return;
     }
     // the slices' candidates, slice after slice: ascending token id
-    for (int c = 0; c < kSampleChunks; ++c)
-        for (int j = tid; j < off[c + 1] - off[c]; j += kThreads) keys[off[c] + j] = ck[(size_t)c * kSampleMaxTopK + j];
+    for (int i = tid; i < n; i += kThreads) {
+        int c = 0;  // the slice holding merged position i
+#pragma unroll
+        for (int j = 1; j < kSampleChunks; ++j) c += off[j] <= i;
+        keys[i] = ck[(size_t)c * kSampleMaxTopK + (i - off[c])];
+    }
     __syncthreads();
     const int k = min(a.top_k, n);
     uint32_t T;
@@ -317,6 +408,10 @@ __global__ __launch_bounds__(kThreads) void sample_finish_kernel(SampleArgs a) {
         }
     }
     __syncthreads();
+    if (P <= 64) {  // up to 64 survivors: the rest runs in wave 0, one candidate per lane, no barriers
+        if (tid < 64) finish_in_wave(a, row, k, tid < P ? srt[tid] : 0ull);
+        return;
+    }
     bitonic_desc(srt, P);  // (value desc, id asc)
     if (a.temperature == 0.f) {  // greedy: the greatest logit, lowest id on ties; no draw
         if (tid == 0) {
