@@ -168,8 +168,10 @@ def run_decode(args, torch, q, synth):
     tok = torch.tensor(synth.tokens(wl.seed, 1, 1, shp.vocab), dtype=torch.int32, device="cuda:0")
     am = torch.empty(1, dtype=torch.int32, device="cuda:0")
     m.decode_step(tok, am)
+    token_ids = [int(tok.item()), int(am.item())]   # the warm-up's greedy ids, recorded (untimed)
     for _ in range(args.warmup - 1):
         m.decode_step(am, am)
+        token_ids.append(int(am.item()))
     torch.cuda.synchronize()
     # one event between consecutive steps: the first-to-last span times exactly `steps` steps, and the spans
     # between neighbours give the per-step distribution
@@ -213,7 +215,7 @@ def run_decode(args, torch, q, synth):
     del m
     torch.cuda.empty_cache()
     return dict(shp=shp, wl=wl, W=W, ms=ms, wall_us=wall / args.steps * 1e6, kernels=kernels, dominant=dom,
-                step_bytes=step_bytes, ctx_mid=ctx_mid, step_us=step_us)
+                step_bytes=step_bytes, ctx_mid=ctx_mid, step_us=step_us, token_ids=token_ids)
 
 
 def decode_steps_timed(torch, m, stream, tok, warmup, steps):
@@ -560,6 +562,7 @@ def main():
                    "hidden": 1024, "layers": 28, "q_heads": 16, "kv_heads": 8, "head_dim": 128, "mlp": 3072,
                    "vocab": 151936, "kv_context_start": res["wl"].kv_prefill},
         "step_us": res["step_us"],
+        "token_ids": res["token_ids"],
         "hbm_GBps": round(res["step_bytes"] / ms / 1e6, 1),
         "step_bytes": res["step_bytes"],
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
