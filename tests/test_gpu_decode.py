@@ -159,10 +159,21 @@ def test_decode_over_prefilled_cache_ragged_context(path):
 
 def test_decode_uneven_position_split_long_context():
     """Eight KV heads over 2301 cached positions: 576 four-position quads over 128 wave slots per KV head, so
-    half the slots take five quads (one past a full chunk) and the rest four."""
+    half the slots take five quads (one whole five-quad chunk) and the rest four."""
     shp = replace(SMALL, fmt=synth.FMT_Q8, n_q_heads=16, n_kv_heads=8, n_layers=1, max_ctx=2400)
     _say("uneven split", shp)
     _greedy_vs_oracle(shp, seed=27, steps=3, kv_fill_len=2301, path="mega")
+
+
+@pytest.mark.parametrize("heads,ctx", [((16, 8), 6000), ((16, 4), 4200)])
+def test_decode_long_context_several_chunks(heads, ctx):
+    """Contexts long enough that every wave slot walks several attention chunks, the next chunk's K/V in flight
+    while the current one is scored: 6000 positions over 128 wave slots of a KV head (about 12 quads each:
+    passes of five, five and two) with two query heads per KV head, and 4200 positions over 256 slots (four-quad
+    chunks) with four."""
+    shp = replace(SMALL, fmt=synth.FMT_Q8, n_q_heads=heads[0], n_kv_heads=heads[1], n_layers=1, max_ctx=ctx + 8)
+    _say("long context", heads, ctx)
+    _greedy_vs_oracle(shp, seed=41, steps=3, kv_fill_len=ctx, path="mega")
 
 
 def test_decode_batched_sequences():
