@@ -343,6 +343,40 @@ def run_sampler(torch, q, synth, stream):
     return res
 
 
+def run_file_load(torch, q, synth):
+    """The weight-file path: the 28-layer model written as a Q8_0 SLM2 file (safetensors container, Q8_0
+    matrices and f32 norms, tied lm_head omitted) to a temporary directory, then qw3_inspect_file (header
+    validation) and qw3_load_file (validation, read-only mapping, block unpacking and packing, upload) timed.
+    The file was just written, so it is read from the page cache: these are not disk figures."""
+    import tempfile
+    from dataclasses import replace
+    from synth import stfile
+    wl = synth.Q8_DECODE
+    shp = replace(wl.shape, fmt=synth.FMT_Q8_0)
+    W = synth.make_weights(shp, seed=wl.seed)
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "qwen3-0.6b-shape.q8_0.slm2")
+        stfile.write(path, stfile.model_entries(W, with_lm_head=False), metadata={"format": "pt"})
+        del W
+        nbytes = os.path.getsize(path)
+        t0 = time.perf_counter()
+        rep = q.inspect_file(path)
+        t_inspect = time.perf_counter() - t0
+        m = q.Model(q.make_config(**synth.abi_config_kwargs(shp)), device="cuda:0")
+        loads = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            m.load_file(path)
+            torch.cuda.synchronize()
+            loads.append(time.perf_counter() - t0)
+        del m
+        torch.cuda.empty_cache()
+    t_load = sorted(loads)[1]
+    return {"workload": "28-layer Qwen3-0.6B-shape Q8_0 SLM2 file from the page cache", "file_bytes": nbytes,
+            "tensors": rep.n_tensors, "inspect_ms": round(t_inspect * 1e3, 2), "load_ms": round(t_load * 1e3, 1),
+            "load_GBps": round(nbytes / t_load / 1e9, 2)}
+
+
 def run_prefill(args, torch, q, synth):
     wl = synth.BF16_PREFILL
     shp = wl.shape
@@ -508,7 +542,8 @@ def main():
                                 "as the headline, with q8 x q8 layer products: activations quantized to int8 "
                                 "per 32-block, int8 dot products (lm_head keeps f32 activations)")),
                             ("single_block", lambda: run_single_block(args, torch, q, synth, side)),
-                            ("sampler", lambda: run_sampler(torch, q, synth, side))):
+                            ("sampler", lambda: run_sampler(torch, q, synth, side)),
+                            ("file_load", lambda: run_file_load(torch, q, synth))):
                 t0 = time.time()
                 extra[key] = fn()
                 log(f"{key}: {json.dumps(extra[key])} ({time.time() - t0:.1f}s)")

@@ -1,11 +1,12 @@
-"""A minimal writer of safetensors containers for the loader tests (test infrastructure).
+"""A minimal writer of safetensors containers: synthetic weight files for the loader tests and the loader's
+benchmark line (test and benchmark infrastructure, like the rest of this package).
 
 Layout ("Scalar-Native Qwen3 Reference Runtime As The Numerical Authority", section 3 "File Layout and Safe
 Metadata Parsing"; "M1 — Load the weights", "The safetensors format -- three regions"): an 8-byte little-endian
 header length, the JSON header, then the data blob.  The header is padded with spaces so the blob starts on an
 8-byte boundary, and tensors are laid out back to back in the order given, each padded to a multiple of 8
 bytes by the next tensor's start -- unless a test asks for something else.  Its output is checked against the
-reference `safetensors` reader in the tests.
+`safetensors` package's reader in the tests.
 """
 import json
 import struct

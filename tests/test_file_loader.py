@@ -12,7 +12,7 @@ from dataclasses import replace
 import numpy as np
 import pytest
 
-import stfile
+from synth import stfile
 import synth
 import transformer_qwen3_block_amd as q
 

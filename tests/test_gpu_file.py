@@ -6,7 +6,7 @@ from dataclasses import replace
 import numpy as np
 import pytest
 
-import stfile
+from synth import stfile
 import synth
 from parity import build_gpu_model
 
