@@ -414,10 +414,12 @@ def run_prefill(args, torch, q, synth):
     return dict(tokens=T, ms=ms, tok_s=T / ms * 1e3, flops=flops, tflops=flops / ms / 1e9)
 
 
-def run_batched(args, torch, q, synth):
-    """16 sequences x 8192-position caches, Q8: one greedy step per sequence per iteration."""
+def run_batched(args, torch, q, synth, fmt=None):
+    """16 sequences x 8192-position caches, Q8 (or another Q8 weight format): one greedy step per sequence per
+    iteration."""
+    from dataclasses import replace
     wl = synth.Q8_BATCHED
-    shp = wl.shape
+    shp = wl.shape if fmt is None else replace(wl.shape, fmt=fmt)
     t0 = time.time()
     W = synth.make_weights(shp, seed=wl.seed)
     m = q.Model(q.make_config(**synth.abi_config_kwargs(shp)), device="cuda:0")
@@ -449,6 +451,10 @@ def run_batched(args, torch, q, synth):
     mats = Q * H + 2 * KV * H + H * Q + 3 * I * H
     wbytes = (L * mats + V * H) * (1 + 4 / 32)
     kvbytes = shp.n_seq * L * shp.n_kv_heads * shp.head_dim * 2 * 2 * (ctx_mid + 1)
+    if fmt is not None:  # a variant line: the iteration only
+        del m
+        torch.cuda.empty_cache()
+        return dict(ms=ms, tok_s=shp.n_seq / ms * 1e3, GBps=(wbytes + kvbytes) / ms / 1e6, iters=iters)
     # attention kernel alone (the dominant kernel of this workload)
     m.bench_kernel(2, 0, 3)
     torch.cuda.synchronize()
@@ -543,7 +549,12 @@ def main():
                                 "per 32-block, int8 dot products (lm_head keeps f32 activations)")),
                             ("single_block", lambda: run_single_block(args, torch, q, synth, side)),
                             ("sampler", lambda: run_sampler(torch, q, synth, side)),
-                            ("file_load", lambda: run_file_load(torch, q, synth))):
+                            ("file_load", lambda: run_file_load(torch, q, synth)),
+                            ("q8xq8_batched", lambda: dict(
+                                workload="16 sequences x KV context 8192 with q8 x q8 layer products (int8 "
+                                         "activations, int8 MFMA per 32-block)",
+                                **{k: round(v, 4) if isinstance(v, float) else v for k, v in
+                                   run_batched(args, torch, q, synth, synth.FMT_Q8_ACT8).items()}))):
                 t0 = time.time()
                 extra[key] = fn()
                 log(f"{key}: {json.dumps(extra[key])} ({time.time() - t0:.1f}s)")

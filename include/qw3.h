@@ -79,9 +79,11 @@ enum { QW3_INPUT_TOKENS = 0, QW3_INPUT_HIDDEN = 1 };
  * "Q8_0 Mixed-Precision Matrix Multiplication"): the projection's input is quantized to int8 per block of 32
  * (scale max|x| / 127, codes rounded to nearest with ties away from zero, clamped to [-127, 127]), the int8
  * products of a block are summed in int32 and scaled by both block scales.  Attention, norms and the tied
- * logits keep f32.  It needs n_seq == 1 (else QW3_UNSUPPORTED_SHAPE from qw3_preflight) and the single-launch
- * decode (qw3_create returns QW3_UNSUPPORTED_SHAPE when the device cannot hold its grid).  Norm weights are
- * bf16 in the bf16 format and f32 in the Q8 formats.
+ * logits keep f32 (the logits of a step of several sequences take the same f16-pair operands as in the Q8
+ * format).  Steps of one sequence (every prefill, and decode with n_seq == 1) run in the single-launch decode;
+ * decode steps of 2..16 sequences run the batched products with one int8 MFMA per block.  qw3_create returns
+ * QW3_UNSUPPORTED_SHAPE when the device cannot hold the single-launch grid or, for n_seq >= 2, the shape has
+ * no batched MFMA products.  Norm weights are bf16 in the bf16 format and f32 in the Q8 formats.
  * input_mode QW3_INPUT_HIDDEN runs the layer stack on caller-supplied f32 hidden states (no embedding,
  * no final norm, no logits; vocab_size must be 0). */
 typedef struct qw3_config {

@@ -141,12 +141,13 @@ def cosine(a, b):
     return float(np.dot(a, b) / max(np.linalg.norm(a) * np.linalg.norm(b), 1e-300))
 
 
-def forced_step_act8(gpu_model, orc, seq, tok, n_layers, stats=None):
+def forced_step_act8(gpu_model, orc, seq, tok, n_layers, orc_seq=None, stats=None):
     """forced_step for the deep q8 x q8 tier: the GPU's appended K/V (of every layer, within ACT8_KV_REL
     relative L2 of the oracle's own) replaces the oracle's for this step."""
-    pos = orc.get_len(seq)
+    oseq = seq if orc_seq is None else orc_seq
+    pos = orc.get_len(oseq)
     g = read_appended_kv(gpu_model, seq, pos, n_layers)
-    rc, am, lg, hid, own = orc.step_forced(seq, tok, kv_force=g)
+    rc, am, lg, hid, own = orc.step_forced(oseq, tok, kv_force=g)
     if rc == 0:
         worst = max(rel_l2(bf16_to_f32(g[l]), bf16_to_f32(own[l])) for l in range(n_layers))
         assert worst <= ACT8_KV_REL, f"position {pos}: appended K/V rel-L2 {worst:.3e}"

@@ -74,7 +74,7 @@ def test_preflight_sizes_follow_the_byte_model(L):
     (dict(hidden=1280), 13),                    # not a multiple of 512 (bf16 lane slicing)
     (dict(n_seq=17), 13),
     (dict(weight_format=5), 12),
-    (dict(weight_format=4, n_seq=2), 13),       # q8 x q8 products: one sequence only
+    (dict(weight_format=4, hidden=1536), 13),   # q8 x q8: contractions in multiples of 1024, as for Q8
     (dict(input_mode=1), 1),                    # hidden mode must have vocab 0
     (dict(vocab=0), 1),
     (dict(eps=0.0), 1),

@@ -271,6 +271,17 @@ def test_decode_q8_act8_vs_oracle(layers, heads):
     _greedy_vs_oracle(shp, seed=29, steps=12 if heads == (8, 4) else 5, kv_fill_len=20, path="mega")
 
 
+@pytest.mark.parametrize("n_seq", [2, 5, 16])
+def test_decode_q8_act8_batched_vs_oracle(n_seq):
+    """q8 x q8 decode of several sequences: the batched products quantize each sequence's activations per
+    32-block and run one int8 MFMA per block (the lm_head keeps its f16-pair operands), against the oracle's
+    q8 x q8 format in its tier."""
+    shp = replace(SMALL, fmt=synth.FMT_Q8_ACT8, n_seq=n_seq, max_ctx=96)
+    _say("q8 x q8 batched", n_seq)
+    _greedy_vs_oracle(shp, seed=31, steps=4, kv_fill_len=30,
+                      seqs_checked=None if n_seq <= 5 else (0, 7, n_seq - 1))
+
+
 def test_q8_act8_needs_the_single_launch_decode():
     import os
     import transformer_qwen3_block_amd as q

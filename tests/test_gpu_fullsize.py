@@ -142,12 +142,16 @@ def test_q8_decode_context_2048_full():
     assert m.get_len(0) == wl.kv_prefill + steps and m.status() == 0
 
 
-def test_batched_16_sequences_context_8192_full():
-    """16 sequences x 8192-position caches, Q8, one greedy step per sequence per iteration; sequences 0 and
-    15 are replayed through the oracle (sequences are independent)."""
+@pytest.mark.parametrize("fmt", [synth.FMT_Q8, synth.FMT_Q8_ACT8])
+def test_batched_16_sequences_context_8192_full(fmt):
+    """16 sequences x 8192-position caches, Q8 (and the q8 x q8 format: int8 activations on int8 MFMA), one
+    greedy step per sequence per iteration; sequences 0 and 15 are replayed through the oracle (sequences are
+    independent).  The q8 x q8 format is compared in its tier: greedy agreement and logits cosine."""
+    from parity import ACT8_COS, cosine, forced_step_act8
     torch = _torch()
     wl = synth.Q8_BATCHED
-    shp = wl.shape
+    shp = replace(wl.shape, fmt=fmt)
+    act8 = fmt == synth.FMT_Q8_ACT8
     _say("batched full size", shp)
     t0 = time.time()
     W = synth.make_weights(shp, seed=wl.seed)
@@ -160,21 +164,34 @@ def test_batched_16_sequences_context_8192_full():
     am = torch.empty(shp.n_seq, dtype=torch.int32, device="cuda")
     lg = torch.empty((shp.n_seq, shp.vocab), dtype=torch.float32, device="cuda")
     side = torch.cuda.Stream()
-    worst = Margins("16 x 8192 batched Q8, sequences 0 and 15")
+    worst = Margins(f"16 x 8192 batched {'q8 x q8' if act8 else 'Q8'}, sequences 0 and 15")
     kv = {}
+    worst_cos = 1.0
     for it in range(2):
         with torch.cuda.stream(side):
             m.decode_step(cur, am, lg)
         side.synchronize()
         g_all = lg.cpu().numpy()
         for s in check:
-            rc, _, o_lg, _ = forced_step(m, orcs[s], s, int(cur[s].item()), shp.n_layers, orc_seq=0, stats=kv)
-            assert rc == 0
-            mab, r = assert_close(g_all[s], o_lg, f"iteration {it} seq {s}")
-            worst.add((mab, r))
+            if act8:
+                rc, _, o_lg, _ = forced_step_act8(m, orcs[s], s, int(cur[s].item()), shp.n_layers, orc_seq=0,
+                                                  stats=kv)
+                assert rc == 0
+                cs = cosine(g_all[s], o_lg)
+                worst_cos = min(worst_cos, cs)
+                assert cs >= ACT8_COS, (it, s, cs)
+            else:
+                rc, _, o_lg, _ = forced_step(m, orcs[s], s, int(cur[s].item()), shp.n_layers, orc_seq=0, stats=kv)
+                assert rc == 0
+                mab, r = assert_close(g_all[s], o_lg, f"iteration {it} seq {s}")
+                worst.add((mab, r))
             assert argmax_ok(int(am[s].item()), o_lg, g_all[s])
         cur = am.clone()
-    worst.report(kv)
+    if act8:
+        _say(f"MARGIN 16 x 8192 batched q8 x q8: worst logits cosine {worst_cos:.6f} (bound {ACT8_COS}), worst "
+             f"appended K/V rel-L2 {kv.get('kv_rel', 0):.3e}")
+    else:
+        worst.report(kv)
     assert m.status() == 0
     for s in range(shp.n_seq):
         assert m.get_len(s) == wl.kv_prefill + 2

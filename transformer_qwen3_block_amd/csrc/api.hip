@@ -103,8 +103,6 @@ int32_t validate(const qw3_config_t *c, Dims *d) {
     const int q_dim = c->n_q_heads * kHeadDim;
     if (c->hidden % unit || q_dim % unit || c->intermediate % unit) return QW3_UNSUPPORTED_SHAPE;
     if (c->n_seq > kMaxSeq) return QW3_UNSUPPORTED_SHAPE;
-    // q8 x q8 products exist only in the single-launch decode of one sequence
-    if (c->weight_format == QW3_WEIGHTS_Q8_ACT8 && c->n_seq != 1) return QW3_UNSUPPORTED_SHAPE;
     if (c->input_mode == QW3_INPUT_TOKENS && c->vocab_size < 1) return QW3_INVALID_ARGUMENT;
     if (c->input_mode == QW3_INPUT_HIDDEN && c->vocab_size != 0) return QW3_INVALID_ARGUMENT;
     if (c->max_ctx > (1 << 24) || c->max_prefill > (1 << 16)) return QW3_UNSUPPORTED_SHAPE;
@@ -394,10 +392,6 @@ int32_t qw3_create(const qw3_config_t *cfg, void *arena_dev, uint64_t arena_byte
     const char *nm = getenv("QW3_NO_MEGA");  // run single-sequence steps kernel by kernel
     // the single-launch decode needs its whole grid resident at once: checked against the current device
     m->mega = mega_supported(d) && !(nm && nm[0] == '1') && mega_resident(weight_mode(d), d.G);
-    if (d.act8 && !m->mega) {  // the q8 x q8 products are implemented in the single-launch decode only
-        delete m;
-        return QW3_UNSUPPORTED_SHAPE;
-    }
     {
         // every product of a batched step must take the MFMA path, since the residual epilogues hand the
         // next RMSNorm its sums of squares
@@ -415,6 +409,12 @@ int32_t qw3_create(const qw3_config_t *cfg, void *arena_dev, uint64_t arena_byte
         g.N = d.V, g.K = d.H;
         ok = ok && gemv_mfma_supported(g, EPI_LOGITS);
         m->mfma_batched = ok;
+    }
+    // q8 x q8 products: steps of one sequence (prefills, n_seq == 1) run in the single-launch decode, steps of
+    // 2..16 sequences in the batched products' int8 form
+    if (d.act8 && (!m->mega || (d.S >= 2 && !m->mfma_batched))) {
+        delete m;
+        return QW3_UNSUPPORTED_SHAPE;
     }
     const char *sp = getenv("QW3_B1_SPLITS");  // tuning override, 1..64
     if (sp && atoi(sp) >= 1 && atoi(sp) <= kMaxSplit) m->b1_splits = atoi(sp);
@@ -612,6 +612,7 @@ static int32_t launch_decode_kernel(Model *m, int which, int l, int seq0, int S,
         g.o_lo = olo[0];
         g.ssq = at<float>(m, L.ssq);
         g.ssq_mode = (which == DK_O || which == DK_DOWN) ? 2 : 1;
+        g.act8 = d.act8 ? 1 : 0;  // q8 x q8: int8 activations from the f32 inputs (x, attention, activations)
     }
     switch (which) {
         case DK_QKV:  // Q/K/V projections with the pre-attention RMSNorm fused in

@@ -165,6 +165,7 @@ struct GemvArgs {
     uint16_t *o_hi, *o_lo;        // operand written for the next product (SwiGLU epilogue)
     float *ssq;             // [H/16][kMaxSeq] per 16-row tile sums of squares of the residual stream
     int ssq_mode;           // 1: RMSNorm input, 1/rms from ssq; 2: the residual epilogue writes ssq
+    int act8;               // q8 x q8: activations quantized to int8 per block, products on int8 MFMA (not logits)
 };
 // Index of activation element k of sequence s in an MFMA operand buffer: [K/64][4][kMaxSeq][16], so the lane
 // of column group g and sequence s reads columns 16g..16g+15 of a 64-column block pair as one 32-byte run.

@@ -35,6 +35,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4_t mfma16(const uint4 &a, const uint4 &b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
@@ -63,6 +64,9 @@ __device__ __forceinline__ uint4 ld16(const void *p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// max that keeps a NaN: once either operand is NaN the result is NaN (fmaxf would drop it)
+__device__ __forceinline__ float nan_max(float a, float b) { return (b > a || b != b) ? b : a; }
+
 // f32 -> (f16 high part, f16 remainder) bits
 __device__ __forceinline__ void split_one(float v, uint16_t &hi, uint16_t &lo) {
     const _Float16 h = (_Float16)v;
@@ -70,13 +74,21 @@ __device__ __forceinline__ void split_one(float v, uint16_t &hi, uint16_t &lo) {
     lo = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)h));
 }
 
-template <int KW, int NB, int EPI>
+// A8 (the q8 x q8 weight format): the activations are quantized to int8 per (sequence, 32-column block) while the
+// wave forms its operands ([P3] section 5 "Q8_0 Mixed-Precision Matrix Multiplication": block scale max|x| / 127,
+// codes rounded to nearest with ties away from zero, clamped to [-127, 127]) and each block is one
+// v_mfma_i32_16x16x32_i8 (lane l: A = sequence l%16, B = weight row l%16, columns 8*(l/16)..+8 of the block),
+// whose int32 sums are scaled by both block scales, (float)isum * (weight scale * activation scale), and
+// added block by block.  The inputs are the f32 values: the residual stream through the RMSNorm, or the f32
+// outputs of the attention and SwiGLU.
+template <int KW, int NB, int EPI, bool A8 = false>
 __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
     static_assert(NB % 2 == 0, "blocks come in pairs");
     constexpr int NP = NB / 2;        // 64-column block pairs per wave
     __shared__ float red[KW][4][64];  // per wave: C[4*(l/16)+r][l%16] of lane l at [r][l]
     __shared__ float s_inv[kMaxSeq];
     __shared__ __attribute__((aligned(16))) float s_gw[EPI == EPI_RESID ? 1 : KW][NB * 32];  // norm weight slices
+    __shared__ __attribute__((aligned(16))) float s_da[A8 ? KW : 1][A8 ? NB : 1][kMaxSeq];  // A8: activation scales
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -118,81 +130,165 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
     int t = blockIdx.x;
     const uint4 z4 = make_uint4(0, 0, 0, 0);
     constexpr int kSsqPer = 1024 / 16 / 16;  // RMSNorm inputs have K = 1024: 64 tile sums, 4 per thread
-    uint4 a1h[NP], a1l[NP], a2h[NP], a2l[NP];
-    if (EPI != EPI_RESID && a.norm_w) {
-        // RMSNorm input ([P1] section 2 items 1 and 6): w * (x * inv) with inv = 1 / sqrt(mean(x^2) + eps) of
-        // the sequence, from the per-16-row sums of squares (tile order, then a fixed 16-lane tree); the
-        // residual stream itself may exceed the f16 range, the normalised operand does not
-        // the tile sums of squares go out first: waiting for them does not wait for the later loads
-        float ssv[kSsqPer];
-        const int ss_s = tid >> 4, ss_p = tid & 15;
+    uint4 a1h[NP], a1l[NP], a2h[NP], a2l[NP];  // f16 operands (high part, remainder)
+    uint2 cw8[NB], ac[NB];  // A8: the tile's weight codes and the activation codes, columns 8q..8q+7 of each block
+    auto load_tile8 = [&](int t, uint2 (&cw)[NB], float (&sc)[NB]) {
+        const long long row = wrow(t < ntiles ? t : 0);
 #pragma unroll
-        for (int i = 0; i < kSsqPer; ++i)  // unconditional (in bounds for every thread); absent ones unused
-            ssv[i] = a.ssq[(ss_p + 16 * i) * kMaxSeq + (ss_s & (kMaxSeq - 1))];
-        asm volatile("" ::: "memory");  // keep these loads ahead of the others (loads return in order)
-        // the wave's slice of the norm weight (NB * 32 = 256 floats) is read once, into LDS, instead of by
-        // each of the 16 sequence lanes
-        static_assert(EPI == EPI_RESID || NB * 32 == 4 * 64, "one 16-byte norm weight chunk per lane");
-        const float4 gwl = *(const float4 *)(a.norm_w + kb0 * 32 + 4 * lane);
-        float xv[NP][16], gv[NP][16];
-        const int xrow = c < S ? c : S - 1;  // lanes of absent sequences read a present row (zeroed below)
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int k = (kb0 + 2 * p) * 32 + 16 * q;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 xx = *(const float4 *)(a.x + (size_t)xrow * a.ldx + k + 4 * i);
-                xv[p][4 * i] = xx.x; xv[p][4 * i + 1] = xx.y; xv[p][4 * i + 2] = xx.z; xv[p][4 * i + 3] = xx.w;
-            }
+        for (int b = 0; b < NB; ++b) {
+            const u32x2_t v = __builtin_nontemporal_load((const u32x2_t *)(wq + row * K + (kb0 + b) * 32 + 8 * q));
+            cw[b] = make_uint2(v.x, v.y);
         }
-        load_tile(t, cw, sc);  // after the activations: they return first and are converted while codes stream
-        *(float4 *)&s_gw[w][4 * lane] = gwl;
-        if (tid < 256) {
-            float ss = 0.f;
 #pragma unroll
-            for (int i = 0; i < kSsqPer; ++i) ss += ss_s < S ? ssv[i] : 0.f;
-            ss = row16_sum(ss);
-            if (ss_p == 0) s_inv[ss_s] = 1.0f / sqrtf(ss / (float)K + a.eps);
-        }
-        __syncthreads();
-        const float inv = s_inv[c];
-#pragma unroll
-        for (int p = 0; p < NP; ++p)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 gg = *(const float4 *)&s_gw[w][2 * p * 32 + 16 * q + 4 * i];
-                gv[p][4 * i] = gg.x; gv[p][4 * i + 1] = gg.y; gv[p][4 * i + 2] = gg.z; gv[p][4 * i + 3] = gg.w;
+        for (int j = 0; j < NB; ++j) sc[j] = a.scales[row * KB + kb0 + j];
+    };
+    if constexpr (!A8) {
+        if (EPI != EPI_RESID && a.norm_w) {
+            // RMSNorm input ([P1] section 2 items 1 and 6): w * (x * inv) with inv = 1 / sqrt(mean(x^2) + eps) of
+            // the sequence, from the per-16-row sums of squares (tile order, then a fixed 16-lane tree); the
+            // residual stream itself may exceed the f16 range, the normalised operand does not
+            // the tile sums of squares go out first: waiting for them does not wait for the later loads
+            float ssv[kSsqPer];
+            const int ss_s = tid >> 4, ss_p = tid & 15;
+    #pragma unroll
+            for (int i = 0; i < kSsqPer; ++i)  // unconditional (in bounds for every thread); absent ones unused
+                ssv[i] = a.ssq[(ss_p + 16 * i) * kMaxSeq + (ss_s & (kMaxSeq - 1))];
+            asm volatile("" ::: "memory");  // keep these loads ahead of the others (loads return in order)
+            // the wave's slice of the norm weight (NB * 32 = 256 floats) is read once, into LDS, instead of by
+            // each of the 16 sequence lanes
+            static_assert(EPI == EPI_RESID || NB * 32 == 4 * 64, "one 16-byte norm weight chunk per lane");
+            const float4 gwl = *(const float4 *)(a.norm_w + kb0 * 32 + 4 * lane);
+            float xv[NP][16], gv[NP][16];
+            const int xrow = c < S ? c : S - 1;  // lanes of absent sequences read a present row (zeroed below)
+    #pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int k = (kb0 + 2 * p) * 32 + 16 * q;
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 xx = *(const float4 *)(a.x + (size_t)xrow * a.ldx + k + 4 * i);
+                    xv[p][4 * i] = xx.x; xv[p][4 * i + 1] = xx.y; xv[p][4 * i + 2] = xx.z; xv[p][4 * i + 3] = xx.w;
+                }
             }
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            f16x8_t h1, l1, h2, l2;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v1 = c < S ? gv[p][e] * (xv[p][e] * inv) : 0.f;
-                const float v2 = c < S ? gv[p][8 + e] * (xv[p][8 + e] * inv) : 0.f;
-                h1[e] = (_Float16)v1;
-                l1[e] = (_Float16)(v1 - (float)h1[e]);
-                h2[e] = (_Float16)v2;
-                l2[e] = (_Float16)(v2 - (float)h2[e]);
+            load_tile(t, cw, sc);  // after the activations: they return first and are converted while codes stream
+            *(float4 *)&s_gw[w][4 * lane] = gwl;
+            if (tid < 256) {
+                float ss = 0.f;
+    #pragma unroll
+                for (int i = 0; i < kSsqPer; ++i) ss += ss_s < S ? ssv[i] : 0.f;
+                ss = row16_sum(ss);
+                if (ss_p == 0) s_inv[ss_s] = 1.0f / sqrtf(ss / (float)K + a.eps);
             }
-            a1h[p] = __builtin_bit_cast(uint4, h1);
-            a1l[p] = __builtin_bit_cast(uint4, l1);
-            a2h[p] = __builtin_bit_cast(uint4, h2);
-            a2l[p] = __builtin_bit_cast(uint4, l2);
+            __syncthreads();
+            const float inv = s_inv[c];
+    #pragma unroll
+            for (int p = 0; p < NP; ++p)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 gg = *(const float4 *)&s_gw[w][2 * p * 32 + 16 * q + 4 * i];
+                    gv[p][4 * i] = gg.x; gv[p][4 * i + 1] = gg.y; gv[p][4 * i + 2] = gg.z; gv[p][4 * i + 3] = gg.w;
+                }
+    #pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                f16x8_t h1, l1, h2, l2;
+    #pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v1 = c < S ? gv[p][e] * (xv[p][e] * inv) : 0.f;
+                    const float v2 = c < S ? gv[p][8 + e] * (xv[p][8 + e] * inv) : 0.f;
+                    h1[e] = (_Float16)v1;
+                    l1[e] = (_Float16)(v1 - (float)h1[e]);
+                    h2[e] = (_Float16)v2;
+                    l2[e] = (_Float16)(v2 - (float)h2[e]);
+                }
+                a1h[p] = __builtin_bit_cast(uint4, h1);
+                a1l[p] = __builtin_bit_cast(uint4, l1);
+                a2h[p] = __builtin_bit_cast(uint4, h2);
+                a2l[p] = __builtin_bit_cast(uint4, l2);
+            }
+        } else {
+            // operand written by the previous kernel (attention output, SwiGLU activations)
+    #pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const size_t o = (((size_t)(kb0 / 2 + p) * 4 + q) * kMaxSeq + c) * 16;
+                const bool on = c < S;  // absent sequences: zero operands, no read outside this batch's slots
+                const size_t oc = on ? o : 0;  // absent sequences read slot 0 and are zeroed
+                a1h[p] = sel4(on, ld16(a.a_hi + oc), z4);
+                a2h[p] = sel4(on, ld16(a.a_hi + oc + 8), z4);
+                a1l[p] = sel4(on, ld16(a.a_lo + oc), z4);
+                a2l[p] = sel4(on, ld16(a.a_lo + oc + 8), z4);
+            }
+            load_tile(t, cw, sc);
         }
     } else {
-        // operand written by the previous kernel (attention output, SwiGLU activations)
+        // f32 inputs of sequence c (lanes of absent sequences read a present row and take zeros), the tile's
+        // codes behind them; then per block the 32 values of a sequence sit in the four lanes c, c+16, c+32,
+        // c+48, which share the block's max through two shuffles
+        constexpr bool kNorm = EPI != EPI_RESID;
+        const bool norm = kNorm && a.norm_w;
+        const bool on = c < S;
+        const int xrow = on ? c : S - 1;
+        float ssv[kSsqPer];
+        const int ss_s = tid >> 4, ss_p = tid & 15;
+        float4 gwl = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (norm) {
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const size_t o = (((size_t)(kb0 / 2 + p) * 4 + q) * kMaxSeq + c) * 16;
-            const bool on = c < S;  // absent sequences: zero operands, no read outside this batch's slots
-            const size_t oc = on ? o : 0;  // absent sequences read slot 0 and are zeroed
-            a1h[p] = sel4(on, ld16(a.a_hi + oc), z4);
-            a2h[p] = sel4(on, ld16(a.a_hi + oc + 8), z4);
-            a1l[p] = sel4(on, ld16(a.a_lo + oc), z4);
-            a2l[p] = sel4(on, ld16(a.a_lo + oc + 8), z4);
+            for (int i = 0; i < kSsqPer; ++i)
+                ssv[i] = a.ssq[(ss_p + 16 * i) * kMaxSeq + (ss_s & (kMaxSeq - 1))];
+            gwl = *(const float4 *)(a.norm_w + kb0 * 32 + 4 * lane);
         }
-        load_tile(t, cw, sc);
+        float xv[NB][8];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float *xp = a.x + (size_t)xrow * a.ldx + (kb0 + b) * 32 + 8 * q;
+            const float4 x0 = *(const float4 *)xp, x1 = *(const float4 *)(xp + 4);
+            xv[b][0] = x0.x; xv[b][1] = x0.y; xv[b][2] = x0.z; xv[b][3] = x0.w;
+            xv[b][4] = x1.x; xv[b][5] = x1.y; xv[b][6] = x1.z; xv[b][7] = x1.w;
+        }
+        load_tile8(t, cw8, sc);
+        float inv = 1.f;
+        if constexpr (kNorm) {
+            if (norm) {
+                *(float4 *)&s_gw[w][4 * lane] = gwl;
+                if (tid < 256) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int i = 0; i < kSsqPer; ++i) ss += ss_s < S ? ssv[i] : 0.f;
+                    ss = row16_sum(ss);
+                    if (ss_p == 0) s_inv[ss_s] = 1.0f / sqrtf(ss / (float)K + a.eps);
+                }
+                __syncthreads();
+                inv = s_inv[c];
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v[e] = xv[b][e];
+                if constexpr (kNorm)
+                    if (norm) v[e] = s_gw[w][b * 32 + 8 * q + e] * (v[e] * inv);
+                if (!on) v[e] = 0.f;
+            }
+            // block max of |v|, NaN-sticky (a NaN anywhere in the block makes it NaN)
+            float m = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = nan_max(m, fabsf(v[e]));
+            m = nan_max(m, __shfl_xor(m, 16, 64));
+            m = nan_max(m, __shfl_xor(m, 32, 64));
+            const float d = m / 127.0f;  // NaN stays NaN
+            const bool ok = d > 0.f && d < INFINITY;
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float c0 = ok ? fminf(fmaxf(roundf(v[e] / d), -127.f), 127.f) : 0.f;
+                const float c1 = ok ? fminf(fmaxf(roundf(v[4 + e] / d), -127.f), 127.f) : 0.f;
+                lo |= ((uint32_t)(int)c0 & 0xffu) << (8 * e);
+                hi |= ((uint32_t)(int)c1 & 0xffu) << (8 * e);
+            }
+            ac[b] = make_uint2(lo, hi);
+            if (q == 0) s_da[w][b][c] = d;
+        }
+        __syncthreads();  // every sequence's block scales, for the lanes that scale its outputs
     }
 
     // logits: running greedy choice of this thread's (sequence, row slot)
@@ -205,26 +301,47 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
     constexpr bool kStride = EPI != EPI_RESID;
     for (; t < ntiles; t += gridDim.x) {
         uint4 cn[NP];
+        uint2 cn8[NB];
         float sn[NB];
-        if constexpr (kStride) load_tile(t + gridDim.x, cn, sn);
+        if constexpr (kStride) {
+            if constexpr (A8)
+                load_tile8(t + gridDim.x, cn8, sn);
+            else
+                load_tile(t + gridDim.x, cn, sn);
+        }
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (A8) {
+            // one int8 product per block: lane l's four outputs are sequences 4*(l/16)..+3 of weight row l%16
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            // one product per block: the other block's lanes contribute zero codes
-            const uint4 b1 = codes_to_f16(make_uint2(cw[p].x, cw[p].y)), b2 = codes_to_f16(make_uint2(cw[p].z, cw[p].w));
-            const uint4 b1f = sel4(first, b1, z4), b2f = sel4(first, b2, z4), b1s = sel4(first, z4, b1),
-                        b2s = sel4(first, z4, b2);
-            f32x4_t cf = {0.f, 0.f, 0.f, 0.f}, cs = {0.f, 0.f, 0.f, 0.f};
-            cf = mfma16(a1h[p], b1f, cf);
-            cs = mfma16(a1h[p], b1s, cs);
-            cf = mfma16(a1l[p], b1f, cf);
-            cs = mfma16(a1l[p], b1s, cs);
-            cf = mfma16(a2h[p], b2f, cf);
-            cs = mfma16(a2h[p], b2s, cs);
-            cf = mfma16(a2l[p], b2f, cf);
-            cs = mfma16(a2l[p], b2s, cs);
+            for (int b = 0; b < NB; ++b) {
+                const i32x4_t ci = __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, ac[b]),
+                                                                         __builtin_bit_cast(long, cw8[b]),
+                                                                         i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+                const float4 da = *(const float4 *)&s_da[w][b][4 * q];
+                acc[0] += (float)ci[0] * (sc[b] * da.x);
+                acc[1] += (float)ci[1] * (sc[b] * da.y);
+                acc[2] += (float)ci[2] * (sc[b] * da.z);
+                acc[3] += (float)ci[3] * (sc[b] * da.w);
+            }
+        } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] += sc[2 * p] * cf[r] + sc[2 * p + 1] * cs[r];
+            for (int p = 0; p < NP; ++p) {
+                // one product per block: the other block's lanes contribute zero codes
+                const uint4 b1 = codes_to_f16(make_uint2(cw[p].x, cw[p].y)), b2 = codes_to_f16(make_uint2(cw[p].z, cw[p].w));
+                const uint4 b1f = sel4(first, b1, z4), b2f = sel4(first, b2, z4), b1s = sel4(first, z4, b1),
+                            b2s = sel4(first, z4, b2);
+                f32x4_t cf = {0.f, 0.f, 0.f, 0.f}, cs = {0.f, 0.f, 0.f, 0.f};
+                cf = mfma16(a1h[p], b1f, cf);
+                cs = mfma16(a1h[p], b1s, cs);
+                cf = mfma16(a1l[p], b1f, cf);
+                cs = mfma16(a1l[p], b1s, cs);
+                cf = mfma16(a2h[p], b2f, cf);
+                cs = mfma16(a2h[p], b2s, cs);
+                cf = mfma16(a2l[p], b2f, cf);
+                cs = mfma16(a2l[p], b2s, cs);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] += sc[2 * p] * cf[r] + sc[2 * p + 1] * cs[r];
+            }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) red[w][r][lane] = acc[r];
@@ -280,6 +397,8 @@ __global__ __launch_bounds__(64 * KW) void gemv_mfma_kernel(GemvArgs a) {
         if constexpr (kStride) {
 #pragma unroll
             for (int p = 0; p < NP; ++p) cw[p] = cn[p];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) cw8[b] = cn8[b];
 #pragma unroll
             for (int j = 0; j < NB; ++j) sc[j] = sn[j];
         }
@@ -341,6 +460,15 @@ hipError_t launch_ssq_prep(const float *x, int ldx, int S, int K, float *ssq, hi
     return hipGetLastError();
 }
 
+// The f16-operand or, for the q8 x q8 format (a.act8), the int8 form of one product.
+template <int KW, int NB, int EPI>
+void launch_form(const GemvArgs &a, dim3 grid, dim3 block, hipStream_t st) {
+    if (a.act8)
+        hipLaunchKernelGGL((gemv_mfma_kernel<KW, NB, EPI, true>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((gemv_mfma_kernel<KW, NB, EPI, false>), grid, block, 0, st, a);
+}
+
 hipError_t launch_gemv_mfma(GemvEpi epi, const GemvArgs &a, hipStream_t st) {
     if (!gemv_mfma_supported(a, epi)) return hipErrorInvalidValue;
     switch (epi) {
@@ -348,23 +476,21 @@ hipError_t launch_gemv_mfma(GemvEpi epi, const GemvArgs &a, hipStream_t st) {
             // one tile per workgroup while the tiles fit the compute units in one round (Q/K/V: 256 tiles,
             // measured 7.5 us against 8.8 us for two tiles per workgroup); two beyond that
             const int ntiles = (a.N + 15) / 16;
-            hipLaunchKernelGGL((gemv_mfma_kernel<4, 8, EPI_STORE>), dim3(ntiles > 256 ? (ntiles + 1) / 2 : ntiles),
-                               dim3(256), 0, st, a);
+            launch_form<4, 8, EPI_STORE>(a, dim3(ntiles > 256 ? (ntiles + 1) / 2 : ntiles), dim3(256), st);
             break;
         }
         case EPI_SWIGLU: {
             // 384 tiles for the 3072-unit MLP: two per workgroup (one per workgroup, 384 workgroups on 256 compute
             // units, measured 11.4 us against 9.2 us)
             const int ntiles = a.N / 8;
-            hipLaunchKernelGGL((gemv_mfma_kernel<4, 8, EPI_SWIGLU>), dim3(ntiles > 128 ? (ntiles + 1) / 2 : ntiles),
-                               dim3(256), 0, st, a);
+            launch_form<4, 8, EPI_SWIGLU>(a, dim3(ntiles > 128 ? (ntiles + 1) / 2 : ntiles), dim3(256), st);
             break;
         }
         case EPI_RESID:
             switch (a.K) {
-                case 1024: hipLaunchKernelGGL((gemv_mfma_kernel<16, 2, EPI_RESID>), dim3(a.N / 16), dim3(1024), 0, st, a); break;
-                case 2048: hipLaunchKernelGGL((gemv_mfma_kernel<16, 4, EPI_RESID>), dim3(a.N / 16), dim3(1024), 0, st, a); break;
-                default: hipLaunchKernelGGL((gemv_mfma_kernel<16, 6, EPI_RESID>), dim3(a.N / 16), dim3(1024), 0, st, a); break;
+                case 1024: launch_form<16, 2, EPI_RESID>(a, dim3(a.N / 16), dim3(1024), st); break;
+                case 2048: launch_form<16, 4, EPI_RESID>(a, dim3(a.N / 16), dim3(1024), st); break;
+                default: launch_form<16, 6, EPI_RESID>(a, dim3(a.N / 16), dim3(1024), st); break;
             }
             break;
         case EPI_LOGITS: {
