@@ -235,23 +235,27 @@ __device__ __forceinline__ void load_slice(const float *v, int lane, float (&out
 }
 
 // RMSNorm of the 1024-vector xs (LDS) with weight slice w ([P1] section 2 items 1 and 6: w * (x / sqrt(mean(x^2)
-// + eps))), returning the lane's slice in registers.  Every wave reduces the whole vector itself.
+// + eps))), returning the lane's slice in registers.  Every wave reduces the whole vector itself, from the
+// same 16-byte LDS reads that fetch its slice (the slices of the 64 lanes tile the vector); 1/sqrt is one
+// v_rsq_f32 (within 1 ulp of the correctly rounded quotient, well inside the decode's tolerance).
 template <int Q8, int CH>
 __device__ __forceinline__ void rms_slice(const float *xs, const float (&w)[CH][Q8 ? 16 : 8], float eps, int lane,
                                           float (&xr)[CH][Q8 ? 16 : 8]) {
     constexpr int E = Q8 ? 16 : 8;
+    static_assert(CH * 64 * E == kHid, "the lane slices cover the vector once");
+    float xv[CH][E];
+    load_slice<Q8, CH>(xs, lane, xv);
     float ss = 0.f;
-#pragma unroll
-    for (int k = 0; k < kHid / 64; ++k) {
-        const float v = xs[lane + 64 * k];
-        ss += v * v;
-    }
-    ss = wave_sum_fast(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)kHid + eps);
 #pragma unroll
     for (int c = 0; c < CH; ++c)
 #pragma unroll
-        for (int e = 0; e < E; ++e) xr[c][e] = w[c][e] * (xs[c * 64 * E + lane * E + e] * inv);
+        for (int e = 0; e < E; ++e) ss += xv[c][e] * xv[c][e];
+    ss = wave_sum_fast(ss);
+    const float inv = __builtin_amdgcn_rsqf(ss / (float)kHid + eps);
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int e = 0; e < E; ++e) xr[c][e] = w[c][e] * (xv[c][e] * inv);
 }
 
 // ---- q8 x q8 products (weight mode 2): activations quantized to int8 per 32-block on the fly ([P3] section 5
@@ -478,8 +482,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     __shared__ __attribute__((aligned(16))) float xs[kHid];
     __shared__ __attribute__((aligned(16))) float big[4096];
-    __shared__ __attribute__((aligned(16))) float wacc[kWaves * 4 * G * kHeadDim];  // [wave][lane row][G][128]
-    __shared__ float wm[kWaves][G], wl[kWaves][4][G];
+    __shared__ __attribute__((aligned(16))) float wacc[kWaves * G * kHeadDim];  // [wave][G][128]
+    __shared__ float wm[kWaves][G], wl[kWaves][G];
     __shared__ int s_fail;
     // q8 x q8 (Q8 == 2): the workgroup's int8 codes and block scales of the current phase input
     __shared__ __attribute__((aligned(16))) uint32_t qcode[kMegaBuf / 4];
@@ -652,13 +656,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             QW3_STAMP(l, 1, 0);
 
             // QK-Norm ([P1] item 3, one 128-weight vector per projection) then RoPE on pairs (i, i + 64) at
-            // `pos` (item 4).  Every wave normalises the G query heads into LDS rows of its own (read back by the
-            // same wave: no workgroup barrier); the key head and the value matter only to the wave of the new
-            // position, which also appends both to the cache ([P1] section 6, rounded to the cache's bf16).
+            // `pos` (item 4), 1/sqrt on v_rsq_f32.  Every wave normalises the G query heads into LDS rows of its
+            // own (read back by the same wave: no workgroup barrier); the key head and the value matter only to
+            // the wave of the new position, which also appends both to the cache ([P1] section 6, rounded to the
+            // cache's bf16).
             const float c = rcs[0], s = rcs[1];
             auto norm_rope = [&](int h, float w0, float w1, float &r0, float &r1) {
                 const float v0 = raw[h * kHeadDim + lane], v1 = raw[h * kHeadDim + lane + 64];
-                const float inv = 1.0f / sqrtf(wave_sum_fast(v0 * v0 + v1 * v1) / (float)kHeadDim + a.eps);
+                const float inv = __builtin_amdgcn_rsqf(wave_sum_fast(v0 * v0 + v1 * v1) / (float)kHeadDim + a.eps);
                 const float n0 = w0 * (v0 * inv), n1 = w1 * (v1 * inv);
                 r0 = n0 * c - n1 * s;
                 r1 = n1 * c + n0 * s;
@@ -717,15 +722,52 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 }
             }
             if (ws == ws_new) attend_new<G>(kn, vn, lane, qr, sl2, m, lsum, acc);
-            // the four lane rows of each wave leave their (l, acc) in LDS (the running max is wave-uniform); one
-            // pass then combines the 16 row partials of the workgroup per output dim
+            // the four lane rows of each wave share the running max (wave-uniform), so their (l, acc) add up
+            // directly: two register swaps across rows (lanes l, l + 32, then odd and even rows) fold the 8 G
+            // values of a lane into 2 G, row r holding values r * 2G .. r * 2G + 2G - 1 of the flattened
+            // [G][8] (one head, contiguous dims); one LDS pass then combines the four waves per output dim
+            {
+                constexpr int NV = 8 * G;
+                float fv[NV];
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float *wp = wacc + ((wave * 4 + (lane >> 4)) * G + h) * kHeadDim + dsub;
-                *(float4 *)wp = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-                *(float4 *)(wp + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-                if ((lane & 15) == 0) wl[wave][lane >> 4][h] = lsum[h];
-                if (lane == 0) wm[wave][h] = m[h];
+                for (int h = 0; h < G; ++h)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) fv[h * 8 + e] = acc[h][e];
+                float r1[NV / 2];
+#pragma unroll
+                for (int k = 0; k < NV / 2; ++k) {
+                    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(fv[k]), __float_as_uint(fv[k + NV / 2]),
+                                                                    false, false);
+                    r1[k] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+                }
+                float r2[NV / 4];
+#pragma unroll
+                for (int k = 0; k < NV / 4; ++k) {
+                    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(r1[k]), __float_as_uint(r1[k + NV / 4]),
+                                                                    false, false);
+                    r2[k] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+                }
+                const int r = lane >> 4, k0 = r * (NV / 4);
+                float *wp = wacc + (wave * G + (k0 >> 3)) * kHeadDim + dsub + (k0 & 7);
+                if constexpr (G == 1) {
+                    *(float2 *)wp = make_float2(r2[0], r2[1]);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < NV / 16; ++q)
+                        *(float4 *)(wp + 4 * q) = make_float4(r2[4 * q], r2[4 * q + 1], r2[4 * q + 2], r2[4 * q + 3]);
+                }
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum[h]), __float_as_uint(lsum[h]),
+                                                                    false, false);
+                    const float t = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+                    const auto p2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+                    const float lw = __uint_as_float(p2[0]) + __uint_as_float(p2[1]);
+                    if (lane == 0) {
+                        wl[wave][h] = lw;
+                        wm[wave][h] = m[h];
+                    }
+                }
             }
             __syncthreads();
             uint64_t *pp = a.part + ((size_t)(g * SP + sp) * G) * PW;
@@ -739,14 +781,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                     for (int w = 0; w < kWaves; ++w) {
                         const float f = exp2_hw(wm[w][h] - M);
-                        float lw = 0.f, ow = 0.f;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            lw += wl[w][r][h];
-                            ow += wacc[((w * 4 + r) * G + h) * kHeadDim + d];
-                        }
-                        Ls += f * lw;
-                        O += f * ow;
+                        Ls += f * wl[w][h];
+                        O += f * wacc[(w * G + h) * kHeadDim + d];
                     }
                 }
                 uint64_t *ph = pp + (size_t)h * PW;
@@ -821,6 +857,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             nu4 = *((const float4 *)(lb + a.mlp_norm) + tid);
         else
             load_slice<Q8, CH>((const float *)(lb + a.mlp_norm), lane, nu);
+        // the down-projection rows go out here too, so the gate/up poll has no loads in front of it (its
+        // inputs are the o_proj outputs, the layer's most contended exchange): 0.37 us per layer faster than
+        // issuing them after o_proj.  Moving any other phase's weights one poll earlier measured slower.
+        load_rows<Q8, 1, KD_MAX>(lb + a.wd, (const float *)(lb + a.sd), I, ro, rov, KD, lane, wd, sd);
 
         // ================= O: o_proj + residual on the owned row
         {
@@ -838,7 +878,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (lane < kXwReps) put(a.xo + lane * xw_rep(kHid) + xw_index(gw), x_own, tag(l, 3));
         }
         QW3_STAMP(l, 3, 1);
-        load_rows<Q8, 1, KD_MAX>(lb + a.wd, (const float *)(lb + a.sd), I, ro, rov, KD, lane, wd, sd);
 
         // ================= U: RMSNorm + gate/up + SwiGLU
         {
