@@ -339,46 +339,56 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a, int KC) {
 // 4 "NaN/Inf Rejection": the generation loop stops at the failing step; section 8: completed steps stand).
 __global__ __launch_bounds__(256) void argmax_finalize_kernel(const float *argpart, int nparts, int S, int *argmax_out,
                                                               int *len, int commit_add, const int *status) {
+    // one workgroup per sequence (grid S); (value desc, id asc) is a total order, so the reduction order does not
+    // change the result
     __shared__ float bv[4];
     __shared__ int bi[4];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int s = 0; s < S; ++s) {
-        float best = -INFINITY;
-        int besti = 0x7fffffff;
-        for (int b = tid; b < nparts; b += 256) {
-            const float *p = argpart + ((size_t)s * nparts + b) * 2;
-            const float v = p[0];
-            const int i = __float_as_int(p[1]);
-            if (v > best || (v == best && i < besti)) {
-                best = v;
-                besti = i;
-            }
+    const int s = blockIdx.x;
+    if (s >= S) return;
+    const float2 *part = (const float2 *)argpart + (size_t)s * nparts;
+    float best = -INFINITY;
+    int besti = 0x7fffffff;
+    auto take = [&](float2 p) {
+        const float v = p.x;
+        const int i = __float_as_int(p.y);
+        if (v > best || (v == best && i < besti)) {
+            best = v;
+            besti = i;
         }
+    };
+    int b = tid;
+    for (; b + 768 < nparts; b += 1024) {  // four partials in flight per thread
+        const float2 p0 = part[b], p1 = part[b + 256], p2 = part[b + 512], p3 = part[b + 768];
+        take(p0);
+        take(p1);
+        take(p2);
+        take(p3);
+    }
+    for (; b < nparts; b += 256) take(part[b]);
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const float ov = __shfl_xor(best, o, 64);
-            const int oi = __shfl_xor(besti, o, 64);
-            if (ov > best || (ov == best && oi < besti)) {
-                best = ov;
-                besti = oi;
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(besti, o, 64);
+        if (ov > best || (ov == best && oi < besti)) {
+            best = ov;
+            besti = oi;
+        }
+    }
+    if (lane == 0) {
+        bv[wave] = best;
+        bi[wave] = besti;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        for (int w = 1; w < 4; ++w)
+            if (bv[w] > bv[0] || (bv[w] == bv[0] && bi[w] < bi[0])) {
+                bv[0] = bv[w];
+                bi[0] = bi[w];
             }
-        }
-        if (lane == 0) {
-            bv[wave] = best;
-            bi[wave] = besti;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            for (int w = 1; w < 4; ++w)
-                if (bv[w] > bv[0] || (bv[w] == bv[0] && bi[w] < bi[0])) {
-                    bv[0] = bv[w];
-                    bi[0] = bi[w];
-                }
-            // all logits NaN: no index qualifies; report 0 (the status word carries the failure)
-            if (argmax_out) argmax_out[s] = bi[0] == 0x7fffffff ? 0 : bi[0];
-            if (len && *status == 0) len[s] += commit_add;
-        }
-        __syncthreads();
+        // all logits NaN: no index qualifies; report 0 (the status word carries the failure)
+        if (argmax_out) argmax_out[s] = bi[0] == 0x7fffffff ? 0 : bi[0];
+        if (len && *status == 0) len[s] += commit_add;
     }
 }
 
@@ -458,7 +468,7 @@ hipError_t gemv_dispatch(const GemvArgs &a, hipStream_t st) {
     hipError_t e = a.S == 1 ? gemv_launch_r<Q8, 1, EPI>(R, KS, grid, a, KC, lds, st)
                             : gemv_launch_r<Q8, kMaxSeq, EPI>(R, KS, grid, a, KC, lds, st);
     if (e != hipSuccess || EPI != EPI_LOGITS) return e;
-    hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(256), 0, st, a.argpart, grid, a.S, a.argmax_out, a.len,
+    hipLaunchKernelGGL(argmax_finalize_kernel, dim3(a.S), dim3(256), 0, st, a.argpart, grid, a.S, a.argmax_out, a.len,
                        a.commit_add, (const int *)a.status);
     return hipGetLastError();
 }
@@ -800,7 +810,7 @@ __global__ void dequant_kernel(const void *w, const float *scales, long long tot
 
 hipError_t launch_argmax_finalize(const float *argpart, int nparts, int S, int *argmax_out, int *len, int commit_add,
                                   const int *status, hipStream_t st) {
-    hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(256), 0, st, argpart, nparts, S, argmax_out, len,
+    hipLaunchKernelGGL(argmax_finalize_kernel, dim3(S), dim3(256), 0, st, argpart, nparts, S, argmax_out, len,
                        commit_add, status);
     return hipGetLastError();
 }
