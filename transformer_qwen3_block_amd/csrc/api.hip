@@ -202,6 +202,7 @@ int32_t plan(const Dims &d, Layout *lay, qw3_sizes_t *sz) {
     L.act16 = take(c.mul(c.mul(M, d.I), 2));
     L.part = take(c.mul(c.mul(c.mul(c.mul(d.S, d.HQ), kMaxSplit), kPartStride), 4));
     L.pf_part = take(attn_prefill_partial_bytes(d));
+    L.pf_split = take(splitk_scratch_bytes(d));
     L.argpart = take(c.mul(c.mul(c.mul(kMaxSeq, kLmMaxBlocks), 2), 4));
     L.logits = d.hidden_mode ? take(0) : take(c.mul(c.mul(d.S, d.V), 4));
     L.tokens = take(c.mul(M, 4));

@@ -55,6 +55,7 @@ struct Layout {
     uint64_t x, xn16, qkv, q16, attn, attn16, act, act16, part, argpart, logits, tokens, ssq;
     uint64_t opnd_hi, opnd_lo;  // batched Q8 products: f16 operand pair handed from a kernel to the next product
     uint64_t pf_part;           // prefill attention: per-thread partial softmax state of each key-range half
+    uint64_t pf_split;          // prefill products of short prompts: f32 partial tiles of the K ranges
     uint64_t weights_end, kv_end, state_end, scratch_end;
 };
 

@@ -16,6 +16,8 @@
 //   [P4] "Portable WebAssembly Runtime Architecture for TinyRustLM"
 #include <math.h>
 
+#include <type_traits>
+
 #include "prefill.h"
 
 namespace qw3 {
@@ -145,7 +147,9 @@ hipError_t launch_rmsnorm_rows(const float *x, int T, int H, const float *w, flo
 // their weight rows in that XCD's L2.
 // Epilogues: f32 store, f16 store, f32 residual add (in place), or SwiGLU into f16: with GLU, each wave's columns are
 // half gate rows and half the matching up rows (up rows start at W row `up_off`), so gate and up of one
-// output element meet in the same lane.
+// output element meet in the same lane.  Split K (short prompts, whose few tiles would otherwise walk every K
+// step on a few compute units): each workgroup stores the f32 partial tile of its K range and
+// splitk_reduce_kernel adds the ranges in split order and applies the epilogue.
 // ---------------------------------------------------------------------------------------------------
 enum GemmEpi { G_STORE = 0, G_RESID = 1, G_SWIGLU = 2, G_STORE16 = 3, G_QKNORM = 4 };
 
@@ -168,6 +172,8 @@ struct GemmArgs {
     uint16_t *ks16, *vt16;
     int ps;
     int *status;        // kStatusF16Range is latched when a shadow value overflows the f16 range
+    // split K (gemm_split_kernel): the f32 partial tiles of the K ranges
+    float *part;
 };
 
 __host__ __device__ inline int kv16_stride(int max_ctx) { return (max_ctx + 63) & ~63; }
@@ -545,6 +551,188 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
             return launch_gemm_cfg<128, 256, 4, 4, EPI>(g, st);
         return launch_gemm_cfg<128, 128, 4, 2, EPI>(g, st);
     }
+}
+
+// Split-K products for prompts of up to kSplitMaxT tokens: 64 x 64 tiles, K split so that about kSplitWg
+// workgroups run (each range an even number of 64-column steps); the partial tiles stay within
+// kSplitScratchFloats.  Reduction: output element (m, n) adds its ranges' partials in split order, then the
+// epilogue of the unsplit product (residual add, f16 store, or SwiGLU of gate column u and up column up_off + u).
+constexpr int kSplitBM = 64, kSplitBN = 64;
+constexpr int kSplitWg = 1024;  // split tiles at most (kSplitScratchFloats / (64 x 64))
+constexpr int kSplitMax = 16;   // K ranges at most
+constexpr int kSplitSteps = 8;  // K steps per range at most (all in flight in registers)
+static_assert((uint64_t)kSplitWg * kSplitBM * kSplitBN <= kSplitScratchFloats, "partial tiles fit the scratch");
+
+// One 64 x 64 tile over KS steps of 64 columns (K range split * KS .. split * KS + KS - 1, split = blockIdx.y),
+// for prompts too short for the K loop of gemm_f16_kernel to hide its load latency: every step's loads are
+// issued at once, then the steps go through two LDS buffers (one barrier each) into the MFMA accumulators.
+// Four waves of 32 x 32; the f32 tile is stored whole to part[(split * tiles + tile) * 64 * 64 + row * 64 + col].
+template <int KS>
+__global__ __launch_bounds__(256) void gemm_split_kernel(GemmArgs g) {
+    constexpr int BM = kSplitBM, BN = kSplitBN, WN = 2, WTM = 32, WTN = 32, TM = 2, TN = 2;
+    constexpr int LDR = kBK + kLdsPad, NT = 256;
+    constexpr int ACH = BM * kBK / 8 / NT, BCH = BN * kBK / 8 / NT;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDR];
+    uint16_t(*As)[BM * LDR] = reinterpret_cast<uint16_t(*)[BM * LDR]>(smem);
+    uint16_t(*Bs)[BN * LDR] = reinterpret_cast<uint16_t(*)[BN * LDR]>(smem + 2 * BM * LDR);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / WN, wn = wave % WN;
+    const int ntm = (g.M + BM - 1) / BM, nt = ntm * (g.N / BN);
+    int tile = blockIdx.x;
+    if (nt % 8 == 0) tile = (blockIdx.x & 7) * (nt / 8) + (blockIdx.x >> 3);
+    const int m0 = (tile % ntm) * BM, n0 = (tile / ntm) * BN;
+    const int kbase = (int)blockIdx.y * KS * kBK;
+    uint4 ra[KS][ACH], rb[KS][BCH];
+    int la[ACH], lb[BCH];
+#pragma unroll
+    for (int c = 0; c < ACH; ++c) {
+        const int ch = tid + NT * c, r = ch >> 3, kc = (ch & 7) * 8;
+        const uint16_t *pa = g.A + (size_t)min(m0 + r, g.M - 1) * g.K + kbase + kc;  // rows past M: row M-1
+        la[c] = r * LDR + kc;
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+            const u32x4_t v = *(const u32x4_t *)(pa + st * kBK);
+            ra[st][c] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < BCH; ++c) {
+        const int ch = tid + NT * c, r = ch >> 3, kc = (ch & 7) * 8;
+        const uint16_t *pb = g.W + (size_t)(n0 + r) * g.K + kbase + kc;
+        lb[c] = r * LDR + kc;
+#pragma unroll
+        for (int st = 0; st < KS; ++st) rb[st][c] = load_nt16(pb + st * kBK);
+    }
+    f32x4_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int ksub = 8 * (lane >> 4), lrow = lane & 15;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+        // buffer st & 1 was last read by step st - 2, which every wave finished before step st - 1's barrier
+        uint16_t *as = As[st & 1], *bs = Bs[st & 1];
+#pragma unroll
+        for (int c = 0; c < ACH; ++c) *(uint4 *)(as + la[c]) = ra[st][c];
+#pragma unroll
+        for (int c = 0; c < BCH; ++c) *(uint4 *)(bs + lb[c]) = rb[st][c];
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kBK; kk += 32) {
+            uint4 af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) af[i] = *(const uint4 *)(as + (wm * WTM + i * 16 + lrow) * LDR + kk + ksub);
+#pragma unroll
+            for (int jj = 0; jj < TN; ++jj) bfr[jj] = *(const uint4 *)(bs + (wn * WTN + jj * 16 + lrow) * LDR + kk + ksub);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int jj = 0; jj < TN; ++jj) acc[i][jj] = mfma16(af[i], bfr[jj], acc[i][jj]);
+        }
+    }
+    // lane holds C[4*(lane/16) + r][lane%16] of each 16x16 tile; rows past M are stored too (never read)
+    const int crow = 4 * (lane >> 4), ccol = lane & 15;
+    float *pt = g.part + ((size_t)blockIdx.y * nt + tile) * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int jj = 0; jj < TN; ++jj)
+                pt[(wm * WTM + i * 16 + crow + r) * BN + wn * WTN + jj * 16 + ccol] = acc[i][jj][r];
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int nsplit, int ntm, int nout) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // group of 4 output columns
+    const int gpr = nout / 4;
+    if (i >= (long long)g.M * gpr) return;
+    const int m = (int)(i / gpr), c4 = (int)(i % gpr) * 4;
+    const int nt = ntm * (g.N / kSplitBN);
+    auto sum4 = [&](int n) {  // columns n..n+3 of row m, summed over the splits in order
+        const int t = (m / kSplitBM) + ntm * (n / kSplitBN);
+        const size_t off = (size_t)t * (kSplitBM * kSplitBN) + (m % kSplitBM) * kSplitBN + (n % kSplitBN);
+        const size_t sstride = (size_t)nt * (kSplitBM * kSplitBN);
+        float4 s = *(const float4 *)(g.part + off);
+        // loads of up to kSplitMax ranges in flight together; the additions keep the split order
+        float4 v[kSplitMax - 1];
+#pragma unroll
+        for (int k = 1; k < kSplitMax; ++k)
+            if (k < nsplit) v[k - 1] = *(const float4 *)(g.part + k * sstride + off);
+#pragma unroll
+        for (int k = 1; k < kSplitMax; ++k)
+            if (k < nsplit) {
+                s.x += v[k - 1].x;
+                s.y += v[k - 1].y;
+                s.z += v[k - 1].z;
+                s.w += v[k - 1].w;
+            }
+        return s;
+    };
+    if constexpr (EPI == G_RESID) {
+        float4 *p = (float4 *)(g.outf + (size_t)m * g.ldo + c4);
+        const float4 s = sum4(c4), x = *p;
+        *p = make_float4(x.x + s.x, x.y + s.y, x.z + s.z, x.w + s.w);
+    } else if constexpr (EPI == G_STORE16) {
+        const float4 s = sum4(c4);
+        uint16_t *o = g.out16 + (size_t)m * g.ldo + c4;
+        *(uint2 *)o = make_uint2(pack_h16x2(s.x, s.y), pack_h16x2(s.z, s.w));
+    } else {
+        static_assert(EPI == G_SWIGLU, "residual, f16 store or SwiGLU");
+        const float4 gt = sum4(c4), up = sum4(g.up_off + c4);
+        const float gv[4] = {gt.x, gt.y, gt.z, gt.w}, uv[4] = {up.x, up.y, up.z, up.w};
+        float a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // SwiGLU, [P1] section 5: (g * sigmoid(g)) * u, as the unsplit epilogue computes it
+            const float sig = 1.0f / (1.0f + __expf(-gv[e]));
+            a[e] = (gv[e] * sig) * uv[e];
+        }
+        uint16_t *o = g.out16 + (size_t)m * g.ldo + c4;
+        *(uint2 *)o = make_uint2(pack_h16x2(a[0], a[1]), pack_h16x2(a[2], a[3]));
+    }
+}
+
+// Splits of K for g (1: the product is left unsplit): the fewest ranges of at most kSplitSteps steps that give
+// at least 256 workgroups, within kSplitWg split tiles.
+int splitk_count(const GemmArgs &g) {
+    if (g.N % kSplitBN || g.K % kBK) return 1;
+    const int nt = ((g.M + kSplitBM - 1) / kSplitBM) * (g.N / kSplitBN), steps = g.K / kBK;
+    int best = 1;
+    for (int s = 2; s <= kSplitMax && s <= steps; ++s) {
+        if (steps % s || steps / s > kSplitSteps || (long long)nt * s > kSplitWg) continue;
+        best = s;
+        if ((long long)nt * s >= 256) break;
+    }
+    return best;
+}
+
+// EPI: the unsplit product's epilogue (G_RESID, G_STORE16 or G_SWIGLU, the latter over N = 2 x up_off plain
+// rows: gate rows 0..up_off-1, up rows up_off..).  g.part must hold nsplit x tiles x 64 x 64 floats.
+template <int EPI>
+hipError_t launch_gemm_split(GemmArgs g, int nsplit, hipStream_t st) {
+    const int ntm = (g.M + kSplitBM - 1) / kSplitBM, nt = ntm * (g.N / kSplitBN);
+    if (nsplit < 2 || nsplit > kSplitMax || g.K % (kBK * nsplit) || g.N % kSplitBN || (long long)nt * nsplit > kSplitWg)
+        return hipErrorInvalidValue;
+    const int ks = g.K / kBK / nsplit;
+    const dim3 grid(nt, nsplit);
+    switch (ks) {
+        case 1: hipLaunchKernelGGL(gemm_split_kernel<1>, grid, dim3(256), 0, st, g); break;
+        case 2: hipLaunchKernelGGL(gemm_split_kernel<2>, grid, dim3(256), 0, st, g); break;
+        case 3: hipLaunchKernelGGL(gemm_split_kernel<3>, grid, dim3(256), 0, st, g); break;
+        case 4: hipLaunchKernelGGL(gemm_split_kernel<4>, grid, dim3(256), 0, st, g); break;
+        case 5: hipLaunchKernelGGL(gemm_split_kernel<5>, grid, dim3(256), 0, st, g); break;
+        case 6: hipLaunchKernelGGL(gemm_split_kernel<6>, grid, dim3(256), 0, st, g); break;
+        case 7: hipLaunchKernelGGL(gemm_split_kernel<7>, grid, dim3(256), 0, st, g); break;
+        case 8: hipLaunchKernelGGL(gemm_split_kernel<8>, grid, dim3(256), 0, st, g); break;
+        default: return hipErrorInvalidValue;
+    }
+    const int nout = EPI == G_SWIGLU ? g.up_off : g.N;
+    const long long groups = (long long)g.M * (nout / 4);
+    hipLaunchKernelGGL((splitk_reduce_kernel<EPI>), dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, g, nsplit, ntm,
+                       nout);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -992,6 +1180,8 @@ uint64_t attn_prefill_counter_bytes(const Dims &d) {
 uint64_t attn_prefill_kv16_bytes(const Dims &d) {
     return d.mfma_prefill ? 2ull * d.HKV * kv16_stride(d.max_ctx) * kHeadDim * sizeof(uint16_t) : 0;
 }
+uint64_t splitk_scratch_bytes(const Dims &d) { return d.mfma_prefill ? kSplitScratchFloats * sizeof(float) : 0; }
+
 uint64_t attn_prefill_partial_bytes(const Dims &d) {
     return attn_prefill_counter_bytes(d) / sizeof(unsigned) * kPfState * 512 * sizeof(unsigned);
 }
@@ -1017,6 +1207,15 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
     uint16_t *ks16 = (uint16_t *)(arena + L.kv16);
     uint16_t *vt16 = ks16 + (size_t)d.HKV * kv16_stride(d.max_ctx) * kHeadDim;
     int *status = (int *)(arena + L.status);
+    float *split_part = (float *)(arena + L.pf_split);
+    // a product of a short prompt splits K when that spreads it over more workgroups
+    auto product = [&](auto epi, GemmArgs g) -> hipError_t {
+        constexpr int EPI = decltype(epi)::value;
+        const int ns = T <= kSplitMaxT ? splitk_count(g) : 1;
+        if (ns < 2) return launch_gemm<EPI>(g, st);
+        g.part = split_part;
+        return launch_gemm_split<EPI>(g, ns, st);
+    };
     for (int l = 0; l < d.L; ++l) {
         const uint64_t b = L.layer0 + (uint64_t)l * L.layer_stride;
         const uint16_t *wqkv = (const uint16_t *)(arena + b + L.l_wqkv16);
@@ -1040,7 +1239,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         // starting on a 64-position boundary the epilogue also writes the chunk's part of the f16 K / V^T
         // shadow, and only the earlier positions are converted from the cache (before, so the epilogue's
         // writes land last)
-        const bool fused = T > 64;
+        const bool fused = T > kSplitMaxT;
         const bool fused_shadow = fused && pos0 % 64 == 0;
         if (fused_shadow && pos0 > 0)
             hipLaunchKernelGGL(kv16_convert_kernel, dim3(pos0 / 64, d.HKV), dim3(256), 0, st, kc, vc, d.max_ctx, pos0,
@@ -1064,7 +1263,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
             g.status = status;
             QW3_PF_TRY(launch_gemm<G_QKNORM>(g, st));
         } else {
-            QW3_PF_TRY(launch_gemm<G_STORE16>(g, st));
+            QW3_PF_TRY(product(std::integral_constant<int, G_STORE16>{}, g));
             hipLaunchKernelGGL(qknorm_rope_append_kernel, dim3(T), dim3(256), 0, st, qkv16, d.Nqkv, d.HQ,
                                d.HKV, (const float *)(arena + b + L.l_q_norm), (const float *)(arena + b + L.l_k_norm),
                                rc, rs, pos0, d.eps, q16, kc, vc, d.max_ctx);
@@ -1093,7 +1292,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         g.K = d.q_dim;
         g.outf = x;
         g.ldo = d.H;
-        QW3_PF_TRY(launch_gemm<G_RESID>(g, st));
+        QW3_PF_TRY(product(std::integral_constant<int, G_RESID>{}, g));
         QW3_PF_TRY(launch_rmsnorm_rows(x, T, d.H, (const float *)(arena + b + L.l_mlp_norm), d.eps, xn16, st));
         g.A = xn16;
         g.W = wgu;
@@ -1103,7 +1302,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         g.outf = nullptr;
         g.out16 = act16;
         g.ldo = d.I;
-        QW3_PF_TRY(launch_gemm<G_SWIGLU>(g, st));
+        QW3_PF_TRY(product(std::integral_constant<int, G_SWIGLU>{}, g));
         g.A = act16;
         g.W = wd;
         g.N = d.H;
@@ -1111,7 +1310,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         g.out16 = nullptr;
         g.outf = x;
         g.ldo = d.H;
-        QW3_PF_TRY(launch_gemm<G_RESID>(g, st));
+        QW3_PF_TRY(product(std::integral_constant<int, G_RESID>{}, g));
     }
     return dev_rc(hipGetLastError());
 }
