@@ -694,6 +694,63 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int nspl
     }
 }
 
+// Residual products of a short prompt whose output feeds an RMSNorm (o_proj -> the MLP norm, down -> the next
+// layer's attention norm): one workgroup per row, each thread a group of four columns per 1024, adds the K
+// ranges' partials to the row in split order (as splitk_reduce_kernel<G_RESID>), writes the row back and, with
+// nw, normalises it into the f16 operand of the next product (the same arithmetic as rmsnorm_rows_kernel,
+// sum of squares by wave then by workgroup): one launch instead of two.
+template <int GPT>  // column groups of four per thread (H = 1024 GPT)
+__global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, int nsplit, int ntm, const float *nw,
+                                                                float eps, uint16_t *out16) {
+    constexpr int H = 1024 * GPT;
+    __shared__ float red[4];
+    const int m = blockIdx.x, tid = threadIdx.x;
+    const size_t sstride = (size_t)ntm * (H / kSplitBN) * (kSplitBM * kSplitBN);
+    float4 xv[GPT];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+        const int n = 1024 * i + 4 * tid;
+        const int t = m / kSplitBM + ntm * (n / kSplitBN);
+        const size_t off = (size_t)t * (kSplitBM * kSplitBN) + (m % kSplitBM) * kSplitBN + (n % kSplitBN);
+        float4 sm = *(const float4 *)(g.part + off);
+        float4 v[kSplitMax - 1];
+#pragma unroll
+        for (int k = 1; k < kSplitMax; ++k)
+            if (k < nsplit) v[k - 1] = *(const float4 *)(g.part + k * sstride + off);
+#pragma unroll
+        for (int k = 1; k < kSplitMax; ++k)
+            if (k < nsplit) {
+                sm.x += v[k - 1].x;
+                sm.y += v[k - 1].y;
+                sm.z += v[k - 1].z;
+                sm.w += v[k - 1].w;
+            }
+        float4 *px = (float4 *)(g.outf + (size_t)m * g.ldo + n);
+        const float4 x0 = *px;
+        const float4 x = make_float4(x0.x + sm.x, x0.y + sm.y, x0.z + sm.z, x0.w + sm.w);
+        *px = x;
+        xv[i] = x;
+        ss += (x.x * x.x + x.y * x.y) + (x.z * x.z + x.w * x.w);
+    }
+    if (!nw) return;
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)H + eps);
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+        const int k = 1024 * i + 4 * tid;
+        const float4 w = *(const float4 *)(nw + k);
+        ushort4 o;
+        o.x = f32_to_h16(w.x * (xv[i].x * inv));
+        o.y = f32_to_h16(w.y * (xv[i].y * inv));
+        o.z = f32_to_h16(w.z * (xv[i].z * inv));
+        o.w = f32_to_h16(w.w * (xv[i].w * inv));
+        *(ushort4 *)(out16 + (size_t)m * H + k) = o;
+    }
+}
+
 // Splits of K for g (1: the product is left unsplit): the fewest ranges of at most kSplitSteps steps that give
 // at least 256 workgroups, within kSplitWg split tiles.
 int splitk_count(const GemmArgs &g) {
@@ -710,8 +767,7 @@ int splitk_count(const GemmArgs &g) {
 
 // EPI: the unsplit product's epilogue (G_RESID, G_STORE16 or G_SWIGLU, the latter over N = 2 x up_off plain
 // rows: gate rows 0..up_off-1, up rows up_off..).  g.part must hold nsplit x tiles x 64 x 64 floats.
-template <int EPI>
-hipError_t launch_gemm_split(GemmArgs g, int nsplit, hipStream_t st) {
+hipError_t launch_split_partials(const GemmArgs &g, int nsplit, hipStream_t st) {
     const int ntm = (g.M + kSplitBM - 1) / kSplitBM, nt = ntm * (g.N / kSplitBN);
     if (nsplit < 2 || nsplit > kSplitMax || g.K % (kBK * nsplit) || g.N % kSplitBN || (long long)nt * nsplit > kSplitWg)
         return hipErrorInvalidValue;
@@ -728,10 +784,34 @@ hipError_t launch_gemm_split(GemmArgs g, int nsplit, hipStream_t st) {
         case 8: hipLaunchKernelGGL(gemm_split_kernel<8>, grid, dim3(256), 0, st, g); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_gemm_split(GemmArgs g, int nsplit, hipStream_t st) {
+    const hipError_t e = launch_split_partials(g, nsplit, st);
+    if (e != hipSuccess) return e;
+    const int ntm = (g.M + kSplitBM - 1) / kSplitBM;
     const int nout = EPI == G_SWIGLU ? g.up_off : g.N;
     const long long groups = (long long)g.M * (nout / 4);
     hipLaunchKernelGGL((splitk_reduce_kernel<EPI>), dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, g, nsplit, ntm,
                        nout);
+    return hipGetLastError();
+}
+
+// Split residual product + the RMSNorm of its output (nw null: the residual add only).  g.N = g.ldo = H.
+hipError_t launch_split_resid_norm(GemmArgs g, int nsplit, const float *nw, float eps, uint16_t *out16,
+                                   hipStream_t st) {
+    if (g.ldo != g.N) return hipErrorInvalidValue;
+    const hipError_t e = launch_split_partials(g, nsplit, st);
+    if (e != hipSuccess) return e;
+    const int ntm = (g.M + kSplitBM - 1) / kSplitBM;
+    const dim3 grid(g.M);
+    switch (g.N) {
+        case 1024: hipLaunchKernelGGL((splitk_resid_norm_kernel<1>), grid, dim3(256), 0, st, g, nsplit, ntm, nw, eps, out16); break;
+        case 2048: hipLaunchKernelGGL((splitk_resid_norm_kernel<2>), grid, dim3(256), 0, st, g, nsplit, ntm, nw, eps, out16); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -853,7 +933,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(const uint16_t 
 // head, 16 queries per wave.  The key tiles of a query block are split into two halves run by two
 // workgroups, so the longest causal rows take half as long; each half writes its per-thread softmax state
 // (running max, partial sum, unnormalised output) and the later of the two to arrive merges both, always
-// with the first half as the left operand, so the result does not depend on which arrives first.  Work
+// with the first half as the left operand, so the result does not depend on which arrives first (a prompt
+// whose causal range stays within kAttnSplitKeys keys runs each unit as one workgroup over all its keys).  Work
 // units are ordered longest first in the first half of the grid and shortest first in the second, so two
 // workgroups resident together on a compute unit carry complementary amounts of work.  Each 64-key tile of K ([key][dim]) and V (transposed to [dim][key]) is staged in LDS once for
 // all waves.  Scores are computed transposed, S^T = K Q^T, so each lane holds four keys of one query
@@ -869,6 +950,7 @@ struct AttnPrefillArgs {
     unsigned *part;           // [query block][HKV][kPfState][512] f32 bits: state of the first half to finish
     unsigned *cnt;            // [query block][HKV] arrival counters, even between launches
     int *status;              // bit 4 set if a published state never arrived (bounded wait)
+    int split;                // 1: the key range of each unit is split between two workgroups (see below)
 };
 constexpr int kPfState = 34;              // per thread: m, l, then o[32]
 constexpr unsigned kPfEmpty = 0xffffffffu;  // slot word not yet published
@@ -924,12 +1006,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
         const int j = blockIdx.x;
         const bool by_xcd = a.HKV % 8 == 0;
         const int hpg = by_xcd ? a.HKV / 8 : a.HKV;       // heads per group of units
-        const int nunits = 2 * nqb * hpg;                  // units per group
+        const int nh = a.split ? 2 : 1;                     // workgroups per (query block, KV head)
+        const int nunits = nh * nqb * hpg;                  // units per group
         const int idx = by_xcd ? j >> 3 : j;
         const int rank = idx < (nunits + 1) / 2 ? idx : nunits - 1 - (idx - (nunits + 1) / 2);  // 0 = most work
-        half = rank & 1;
-        qb = nqb - 1 - (rank >> 1) / hpg;
-        kvh = (by_xcd ? (j & 7) : 0) + (by_xcd ? 8 : 1) * ((rank >> 1) % hpg);
+        half = a.split ? rank & 1 : 0;
+        qb = nqb - 1 - (rank / nh) / hpg;
+        kvh = (by_xcd ? (j & 7) : 0) + (by_xcd ? 8 : 1) * ((rank / nh) % hpg);
         // uniform by construction; keeping them in scalar registers lets the tile loads use a scalar base
         half = __builtin_amdgcn_readfirstlane(half);
         qb = __builtin_amdgcn_readfirstlane(qb);
@@ -941,7 +1024,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
     const int qpos = a.pos0 + tq;
     const int t_last = min(a.T - 1, t0 + QB - 1);
     const int n_keys = a.pos0 + t_last + 1;
-    const int hsplit = ((n_keys + kKT - 1) / kKT + 1) / 2 * kKT;  // first key of the second half
+    const int hsplit = a.split ? ((n_keys + kKT - 1) / kKT + 1) / 2 * kKT : n_keys;  // first key of the second half
     const int kbeg = half ? hsplit : 0;
     const int kend = half ? n_keys : min(n_keys, hsplit);
     const int g4 = lane >> 4;
@@ -1081,7 +1164,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
     // uses, and every word is stored and loaded at device scope, so the second workgroup can tell a word
     // that has not landed yet from a published one without a cache-wide fence; the merger restores the empty
     // pattern after reading.  m is uniform over the four lanes of a query; l is this lane's partial sum.
-    {
+    if (a.split) {
         const size_t unit = (size_t)qb * a.HKV + kvh;
         unsigned *slot = a.part + unit * kPfState * 512 + tid;
         unsigned &s_second = *(unsigned *)&KsB[0][0];  // the tile buffers are free after the loop's last barrier
@@ -1150,9 +1233,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
     }
 }
 
-hipError_t launch_attn_prefill(int G, const AttnPrefillArgs &a, hipStream_t st) {
+// Short causal ranges (every query block within kAttnSplitKeys keys) gain nothing from splitting the key range,
+// whose merge costs device-scope round trips: one workgroup per (query block, KV head) then.
+constexpr int kAttnSplitKeys = 256;
+
+hipError_t launch_attn_prefill(int G, AttnPrefillArgs a, hipStream_t st) {
     const int QB = 16 * (8 / G);
-    const dim3 grid(2 * ((a.T + QB - 1) / QB) * a.HKV);
+    a.split = a.pos0 + a.T > kAttnSplitKeys ? 1 : 0;
+    const dim3 grid((a.split ? 2 : 1) * ((a.T + QB - 1) / QB) * a.HKV);
     switch (G) {
         case 1: hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(512), 0, st, a); break;
         case 2: hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, dim3(512), 0, st, a); break;
@@ -1216,6 +1304,18 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         g.part = split_part;
         return launch_gemm_split<EPI>(g, ns, st);
     };
+    // a residual product followed by an RMSNorm (nw; null: none follows): split, the reduction also normalises;
+    // returns whether xn16 now holds the normalised rows
+    auto resid_product = [&](GemmArgs g, const float *nw, bool &normed) -> hipError_t {
+        const int ns = T <= kSplitMaxT ? splitk_count(g) : 1;
+        normed = false;
+        if (ns < 2) return launch_gemm<G_RESID>(g, st);
+        g.part = split_part;
+        if (g.N != 1024 && g.N != 2048) return launch_gemm_split<G_RESID>(g, ns, st);  // no fused form
+        normed = nw != nullptr;
+        return launch_split_resid_norm(g, ns, nw, d.eps, xn16, st);
+    };
+    bool xn_ready = false;  // xn16 already holds this layer's normalised input
     for (int l = 0; l < d.L; ++l) {
         const uint64_t b = L.layer0 + (uint64_t)l * L.layer_stride;
         const uint16_t *wqkv = (const uint16_t *)(arena + b + L.l_wqkv16);
@@ -1226,7 +1326,8 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         uint16_t *kc = (uint16_t *)(arena + L.kcache) + layer_off;
         uint16_t *vc = (uint16_t *)(arena + L.vcache) + layer_off;
 
-        QW3_PF_TRY(launch_rmsnorm_rows(x, T, d.H, (const float *)(arena + b + L.l_attn_norm), d.eps, xn16, st));
+        if (!xn_ready)
+            QW3_PF_TRY(launch_rmsnorm_rows(x, T, d.H, (const float *)(arena + b + L.l_attn_norm), d.eps, xn16, st));
         GemmArgs g{};
         g.A = xn16;
         g.W = wqkv;
@@ -1292,8 +1393,12 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         g.K = d.q_dim;
         g.outf = x;
         g.ldo = d.H;
-        QW3_PF_TRY(product(std::integral_constant<int, G_RESID>{}, g));
-        QW3_PF_TRY(launch_rmsnorm_rows(x, T, d.H, (const float *)(arena + b + L.l_mlp_norm), d.eps, xn16, st));
+        {
+            bool normed;
+            const float *mlp_norm = (const float *)(arena + b + L.l_mlp_norm);
+            QW3_PF_TRY(resid_product(g, mlp_norm, normed));
+            if (!normed) QW3_PF_TRY(launch_rmsnorm_rows(x, T, d.H, mlp_norm, d.eps, xn16, st));
+        }
         g.A = xn16;
         g.W = wgu;
         g.N = 2 * d.I;
@@ -1310,7 +1415,10 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         g.out16 = nullptr;
         g.outf = x;
         g.ldo = d.H;
-        QW3_PF_TRY(product(std::integral_constant<int, G_RESID>{}, g));
+        // the next layer's attention RMSNorm rides on the down product's reduction when K is split
+        const float *next_norm =
+            l + 1 < d.L ? (const float *)(arena + L.layer0 + (uint64_t)(l + 1) * L.layer_stride + L.l_attn_norm) : nullptr;
+        QW3_PF_TRY(resid_product(g, next_norm, xn_ready));
     }
     return dev_rc(hipGetLastError());
 }
