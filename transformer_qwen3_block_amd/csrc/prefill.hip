@@ -824,16 +824,18 @@ hipError_t launch_split_resid_norm(GemmArgs g, int nsplit, const float *nw, floa
 // values (their attention weights are 0).  The values are f16(bf16 cache value), exact in the f16 range.
 // ---------------------------------------------------------------------------------------------------
 
-// Cache positions [0, n) of every KV head into the shadow, 64 positions per workgroup: K rows are converted
-// in place of their layout, V goes through LDS to be written as 128-byte V^T rows.  Positions past n in the
-// last tile get zero V.
+// Cache positions [0, n) of every KV head into the shadow, 64 positions and a quarter of the head's dims per
+// workgroup (grid: position tiles, KV heads, 4): K rows are converted in place of their layout, V goes through
+// LDS to be written as 128-byte V^T rows.  Positions past n in the last tile get zero V.
 __global__ __launch_bounds__(256) void kv16_convert_kernel(const uint16_t *kc, const uint16_t *vc, int max_ctx,
                                                            int n, uint16_t *ks16, uint16_t *vt16, int *status) {
-    __shared__ __attribute__((aligned(16))) uint16_t t[kHeadDim][64 + 8];
-    const int p0 = blockIdx.x * 64, hk = blockIdx.y, tid = threadIdx.x;
+    constexpr int DQ = kHeadDim / 4;  // dims per workgroup
+    __shared__ __attribute__((aligned(16))) uint16_t t[DQ][64 + 8];
+    const int p0 = blockIdx.x * 64, hk = blockIdx.y, dq0 = blockIdx.z * DQ, tid = threadIdx.x;
     const int ps = kv16_stride(max_ctx);
-    for (int c = tid; c < 64 * kHeadDim / 8; c += 256) {
-        const int key = c >> 4, d8 = (c & 15) * 8, p = p0 + key;
+    {
+        const int c = tid;  // 64 keys x 4 chunks of 8 dims
+        const int key = c >> 2, d8 = dq0 + (c & 3) * 8, p = p0 + key;
         uint32_t kw[4] = {0, 0, 0, 0}, vw[4] = {0, 0, 0, 0};
         if (p < n) {
             const size_t at = ((size_t)hk * max_ctx + p) * kHeadDim + d8;
@@ -850,17 +852,18 @@ __global__ __launch_bounds__(256) void kv16_convert_kernel(const uint16_t *kc, c
             if (bad) atomicOr(status, kStatusF16Range);
             *(uint4 *)(ks16 + ((size_t)hk * ps + p) * kHeadDim + d8) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
         }
-        const int pp = vt_perm(key);
+        const int pp = vt_perm(key), dl = d8 - dq0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            t[d8 + 2 * e][pp] = (uint16_t)(vw[e] & 0xffffu);
-            t[d8 + 2 * e + 1][pp] = (uint16_t)(vw[e] >> 16);
+            t[dl + 2 * e][pp] = (uint16_t)(vw[e] & 0xffffu);
+            t[dl + 2 * e + 1][pp] = (uint16_t)(vw[e] >> 16);
         }
     }
     __syncthreads();
-    for (int c = tid; c < kHeadDim * 64 / 8; c += 256) {
+    {
+        const int c = tid;  // DQ rows x 8 chunks of 8 keys
         const int dim = c >> 3, k8 = (c & 7) * 8;
-        *(uint4 *)(vt16 + ((size_t)hk * kHeadDim + dim) * ps + p0 + k8) = *(const uint4 *)&t[dim][k8];
+        *(uint4 *)(vt16 + ((size_t)hk * kHeadDim + dq0 + dim) * ps + p0 + k8) = *(const uint4 *)&t[dim][k8];
     }
 }
 
@@ -872,14 +875,37 @@ __global__ __launch_bounds__(256) void kv16_convert_kernel(const uint16_t *kc, c
 // ---------------------------------------------------------------------------------------------------
 constexpr int kQkMaxHeadsPerWave = 8;  // query + key heads of a wave whose loads are in flight together
 
+// SPLIT: the projection ran with K split (gemm_split_kernel) into at most kQkMaxSplit ranges; each element is the
+// sum of its ranges' partial tiles in split order, rounded to f16 as the unsplit product's f16 epilogue would.
+constexpr int kQkMaxSplit = 4;
+template <bool SPLIT>
 __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(const uint16_t *qkv, int ldqkv, int HQ, int HKV,
                                                                  const float *q_norm, const float *k_norm,
                                                                  const float *rope_cos, const float *rope_sin,
                                                                  int pos0, float eps, uint16_t *q16, uint16_t *kc,
-                                                                 uint16_t *vc, int max_ctx) {
+                                                                 uint16_t *vc, int max_ctx, const float *part,
+                                                                 int nsplit, int ntm) {
     const int t = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int pos = pos0 + t;
     const uint16_t *row = qkv + (size_t)t * ldqkv;
+    const size_t sstride = (size_t)ntm * (ldqkv / kSplitBN) * (kSplitBM * kSplitBN);
+    auto elem = [&](int col) -> uint16_t {  // element (t, col) of the f16 projection
+        if constexpr (SPLIT) {
+            const int tl = t / kSplitBM + ntm * (col / kSplitBN);
+            const float *pp = part + (size_t)tl * (kSplitBM * kSplitBN) + (t % kSplitBM) * kSplitBN + (col % kSplitBN);
+            float v[kQkMaxSplit];
+#pragma unroll
+            for (int k = 0; k < kQkMaxSplit; ++k)
+                if (k < nsplit) v[k] = pp[k * sstride];
+            float sm = v[0];
+#pragma unroll
+            for (int k = 1; k < kQkMaxSplit; ++k)
+                if (k < nsplit) sm += v[k];
+            return f32_to_h16(sm);
+        } else {
+            return row[col];
+        }
+    };
     const float c = rope_cos[(size_t)pos * 64 + lane], sn = rope_sin[(size_t)pos * 64 + lane];
     const float qw0 = q_norm[lane], qw1 = q_norm[lane + 64], kw0 = k_norm[lane], kw1 = k_norm[lane + 64];
     // the wave's query and key heads h = wave, wave + 4, ... in groups of kQkMaxHeadsPerWave: every load of a
@@ -890,12 +916,12 @@ __global__ __launch_bounds__(256) void qknorm_rope_append_kernel(const uint16_t 
         for (int i = 0; i < kQkMaxHeadsPerWave; ++i) {
             const int h = h0 + 4 * i;
             const int hh = h < HQ + HKV ? h : 0;
-            const uint16_t *src = row + (size_t)hh * kHeadDim;  // query heads, then key heads
-            const uint16_t *vs = row + (size_t)(HQ + HKV + (hh >= HQ ? hh - HQ : 0)) * kHeadDim;
-            raw[i][0] = src[lane];
-            raw[i][1] = src[lane + 64];
-            raw[i][2] = vs[lane];
-            raw[i][3] = vs[lane + 64];
+            const int src = hh * kHeadDim;  // query heads, then key heads
+            const int vs = (HQ + HKV + (hh >= HQ ? hh - HQ : 0)) * kHeadDim;
+            raw[i][0] = elem(src + lane);
+            raw[i][1] = elem(src + lane + 64);
+            raw[i][2] = elem(vs + lane);
+            raw[i][3] = elem(vs + lane + 64);
         }
 #pragma unroll
         for (int i = 0; i < kQkMaxHeadsPerWave; ++i) {
@@ -1343,7 +1369,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         const bool fused = T > kSplitMaxT;
         const bool fused_shadow = fused && pos0 % 64 == 0;
         if (fused_shadow && pos0 > 0)
-            hipLaunchKernelGGL(kv16_convert_kernel, dim3(pos0 / 64, d.HKV), dim3(256), 0, st, kc, vc, d.max_ctx, pos0,
+            hipLaunchKernelGGL(kv16_convert_kernel, dim3(pos0 / 64, d.HKV, 4), dim3(256), 0, st, kc, vc, d.max_ctx, pos0,
                                ks16, vt16, status);
         if (fused) {
             g.q_norm = (const float *)(arena + b + L.l_q_norm);
@@ -1364,14 +1390,29 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
             g.status = status;
             QW3_PF_TRY(launch_gemm<G_QKNORM>(g, st));
         } else {
-            QW3_PF_TRY(product(std::integral_constant<int, G_STORE16>{}, g));
-            hipLaunchKernelGGL(qknorm_rope_append_kernel, dim3(T), dim3(256), 0, st, qkv16, d.Nqkv, d.HQ,
-                               d.HKV, (const float *)(arena + b + L.l_q_norm), (const float *)(arena + b + L.l_k_norm),
-                               rc, rs, pos0, d.eps, q16, kc, vc, d.max_ctx);
+            // a split projection leaves its K ranges to the QK-Norm kernel, which adds them as it reads
+            const int ns = splitk_count(g);
+            const float *qn = (const float *)(arena + b + L.l_q_norm), *kn = (const float *)(arena + b + L.l_k_norm);
+            if (ns > kQkMaxSplit) {
+                g.part = split_part;
+                QW3_PF_TRY(launch_gemm_split<G_STORE16>(g, ns, st));
+                hipLaunchKernelGGL(qknorm_rope_append_kernel<false>, dim3(T), dim3(256), 0, st, qkv16, d.Nqkv, d.HQ,
+                                   d.HKV, qn, kn, rc, rs, pos0, d.eps, q16, kc, vc, d.max_ctx, nullptr, 0, 0);
+            } else if (ns >= 2) {
+                g.part = split_part;
+                QW3_PF_TRY(launch_split_partials(g, ns, st));
+                hipLaunchKernelGGL(qknorm_rope_append_kernel<true>, dim3(T), dim3(256), 0, st, qkv16, d.Nqkv, d.HQ,
+                                   d.HKV, qn, kn, rc, rs, pos0, d.eps, q16, kc, vc, d.max_ctx, split_part, ns,
+                                   (T + kSplitBM - 1) / kSplitBM);
+            } else {
+                QW3_PF_TRY(launch_gemm<G_STORE16>(g, st));
+                hipLaunchKernelGGL(qknorm_rope_append_kernel<false>, dim3(T), dim3(256), 0, st, qkv16, d.Nqkv, d.HQ,
+                                   d.HKV, qn, kn, rc, rs, pos0, d.eps, q16, kc, vc, d.max_ctx, nullptr, 0, 0);
+            }
         }
         // every cached position of this layer (earlier chunks and the new one) into the f16 shadow
         if (!fused_shadow)
-            hipLaunchKernelGGL(kv16_convert_kernel, dim3((pos0 + T + 63) / 64, d.HKV), dim3(256), 0, st, kc, vc,
+            hipLaunchKernelGGL(kv16_convert_kernel, dim3((pos0 + T + 63) / 64, d.HKV, 4), dim3(256), 0, st, kc, vc,
                                d.max_ctx, pos0 + T, ks16, vt16, status);
         AttnPrefillArgs at{};
         at.q16 = q16;
