@@ -92,13 +92,17 @@ def test_prefill_single_token_tiles_bf16():
     _prefill_vs_oracle(replace(SMALL, max_prefill=1), seed=37, T=12, decode_steps=2)
 
 
-@pytest.mark.parametrize("chunk,T", [(300, 610), (128, 300), (100, 290)])
+@pytest.mark.parametrize("chunk,T", [(600, 1250), (128, 300), (100, 290), (256, 256), (512, 512), (520, 513)])
 def test_prefill_chunks_every_projection_path(chunk, T):
-    """Chunked prefill through every projection path: chunks of more than 64 tokens take the fused Q/K/V
-    epilogue, which writes the attention's f16 K/V shadow when the chunk starts on a 64-position boundary (0,
-    128) and leaves it to the conversion kernel when not (300, 100, 200); the last chunks of 64 tokens or fewer
-    (10, 44) take the plain products and the separate QK-Norm kernel."""
-    _prefill_vs_oracle(replace(SMALL, max_prefill=chunk, max_ctx=640), seed=36, T=T, decode_steps=2)
+    """Chunked prefill through every projection path.  Chunks of more than 512 tokens (600, 513) take the tiled
+    products with the fused Q/K/V epilogue, which writes the attention's f16 K/V shadow when the chunk starts on
+    a 64-position boundary (0) and leaves it to the conversion kernel when not (600); chunks of 512 tokens or
+    fewer (128, 100, 50, 44, 90, and exactly 256 and 512) split K over more workgroups, with the QK-Norm kernel
+    adding the projection's K ranges and the residual products' reductions normalising for the next product.
+    The attention runs each query block's keys in one workgroup while the causal range stays within 256 keys
+    (first chunks of 100, 128 and 256 tokens, and the second of 100 or 128 at a nonzero start) and splits them
+    between two workgroups past it."""
+    _prefill_vs_oracle(replace(SMALL, max_prefill=chunk, max_ctx=1280), seed=36, T=T, decode_steps=2)
 
 
 @pytest.mark.parametrize("heads", [(8, 8), (8, 2)])

@@ -14,9 +14,10 @@ uint64_t attn_prefill_counter_bytes(const Dims &d);
 // f16 shadow of one layer's K and V^T for the prefill attention (zeroed state memory, reused by every layer)
 uint64_t attn_prefill_kv16_bytes(const Dims &d);
 uint64_t attn_prefill_partial_bytes(const Dims &d);
-// Prompts of up to kSplitMaxT tokens run their four products with K split over more workgroups; the f32
+// Prompts of up to kSplitMaxT tokens run their four products with K split over more workgroups (measured on
+// 128- to 2048-token prompts: faster up to 512 tokens, no change beyond); the f32
 // partial tiles take at most kSplitScratchFloats (1024 split tiles of 64 x 64, 16 MiB) in scratch memory.
-constexpr int kSplitMaxT = 256;
+constexpr int kSplitMaxT = 512;
 constexpr uint64_t kSplitScratchFloats = 1024ull * 64 * 64;
 uint64_t splitk_scratch_bytes(const Dims &d);
 

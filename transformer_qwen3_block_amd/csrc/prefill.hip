@@ -1366,7 +1366,9 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
         // starting on a 64-position boundary the epilogue also writes the chunk's part of the f16 K / V^T
         // shadow, and only the earlier positions are converted from the cache (before, so the epilogue's
         // writes land last)
-        const bool fused = T > kSplitMaxT;
+        // (a short prompt whose projection splits K adds the ranges in the QK-Norm kernel instead)
+        const int ns_qkv = T <= kSplitMaxT ? splitk_count(g) : 1;
+        const bool fused = T > 64 && ns_qkv < 2;
         const bool fused_shadow = fused && pos0 % 64 == 0;
         if (fused_shadow && pos0 > 0)
             hipLaunchKernelGGL(kv16_convert_kernel, dim3(pos0 / 64, d.HKV, 4), dim3(256), 0, st, kc, vc, d.max_ctx, pos0,
@@ -1391,7 +1393,7 @@ int32_t prefill_layers(uint8_t *arena, const Layout &L, const Dims &d, int seq, 
             QW3_PF_TRY(launch_gemm<G_QKNORM>(g, st));
         } else {
             // a split projection leaves its K ranges to the QK-Norm kernel, which adds them as it reads
-            const int ns = splitk_count(g);
+            const int ns = ns_qkv;
             const float *qn = (const float *)(arena + b + L.l_q_norm), *kn = (const float *)(arena + b + L.l_k_norm);
             if (ns > kQkMaxSplit) {
                 g.part = split_part;
