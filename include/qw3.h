@@ -374,7 +374,7 @@ int32_t qw3_bench_kernel(uint64_t handle, int32_t kernel, int32_t layer, int32_t
  * fractions can be stated against both the nominal peak and what a plain kernel reaches.
  * qw3_probe_hbm_read streams `bytes` (16-byte aligned device buffer) once with 16-byte nontemporal loads on
  * `grid` workgroups of 256 threads, writing one word per workgroup to out_dev (uint32 [grid]).
- * qw3_probe_mfma_f16 runs `iters` rounds of four independent v_mfma_f32_16x16x32_f16 per wave on `grid`
+ * qw3_probe_mfma_f16 runs `iters` rounds of sixteen independent v_mfma_f32_16x16x32_f16 per wave on `grid`
  * workgroups of four waves (16384 flops per instruction), writing one float per wave to out_dev
  * (float [grid * 4]).  QW3_INVALID_ARGUMENT for null or misaligned pointers, grid outside 1..65536. */
 int32_t qw3_probe_hbm_read(const void *buf_dev, uint64_t bytes, uint32_t *out_dev, int32_t grid, void *stream);
