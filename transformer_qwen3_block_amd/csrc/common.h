@@ -117,6 +117,17 @@ __device__ __forceinline__ float row16_max(float v) {
 __device__ __forceinline__ float lane_get(float v, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
+// Sums over the two halves of the wave (lanes l and l + 32) and over row pairs (odd and even rows of 16
+// lanes), two values per register swap: v_permlane32_swap / v_permlane16_swap exchange half of one register
+// with half of another, so a + b of the swapped pair folds two values at once.
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
 // Whole-wave sum / max, wave-uniform result: row reductions on DPP, then the four row results.
 __device__ __forceinline__ float wave_sum_fast(float v) {
     v = row16_sum(v);

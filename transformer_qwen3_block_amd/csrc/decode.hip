@@ -153,6 +153,22 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a, int KC) {
     }
 
     auto epilogue = [&](int grp, float (&acc)[NR][SM]) {
+        if constexpr (EPI == EPI_LOGITS && SM == 1 && NR == 4) {
+            // the four rows' lane partials folded at once: lane row r ends up with row r's logit (the same
+            // reduction tree for every row, so equal rows give equal logits); each lane row keeps its own
+            // greedy choice over the rows it sees, in increasing order, and the rows are combined at the end
+            const float v = row16_sum(swap16_sum(swap32_sum(acc[0][0], acc[2][0]), swap32_sum(acc[1][0], acc[3][0])));
+            const int unit = grp * R + (lane >> 4);
+            if (unit < a.N) {
+                if ((lane & 15) == 0) a.y[unit] = v;
+                if (!isfinite(v)) my_bad = 1;
+                if (v > best[0]) {
+                    best[0] = v;
+                    besti[0] = unit;
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < NR; ++j)
 #pragma unroll
@@ -303,6 +319,18 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a, int KC) {
         // per-workgroup greedy partial: greatest value, lowest index on ties ([P4] "Sampling order"); a
         // non-finite logit latches a numerical failure ([P1] section 4).  The final choice over the
         // workgroups is made by argmax_finalize_kernel.
+        if constexpr (SM == 1 && NR == 4) {  // the four lane rows' choices (see the epilogue)
+#pragma unroll
+            for (int o = 16; o <= 32; o <<= 1) {
+                const float ov = __shfl_xor(best[0], o, 64);
+                const int oi = __shfl_xor(besti[0], o, 64);
+                if (ov > best[0] || (ov == best[0] && oi < besti[0])) {
+                    best[0] = ov;
+                    besti[0] = oi;
+                }
+            }
+            my_bad = __any(my_bad) ? 1 : 0;
+        }
         if (lane == 0) {
 #pragma unroll
             for (int s = 0; s < SM; ++s) {
