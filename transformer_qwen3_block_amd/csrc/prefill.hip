@@ -140,9 +140,13 @@ hipError_t launch_rmsnorm_rows(const float *x, int T, int H, const float *w, flo
 // ---------------------------------------------------------------------------------------------------
 // C[M, N] = A[M, K] * W[N, K]^T on f16 MFMA with f32 accumulation.
 // Workgroup tile BM x BN; WM x WN waves, each owning a (BM/WM) x (BN/WN) block of 16x16 tiles.  K runs in
-// steps of 64: step j is multiplied from LDS buffer j&1 while step j+1 is written into the other buffer from
-// registers, and the global loads of step j+3 are issued into the registers that step j+1 just left, so
-// every load has two steps of products to hide behind and each step needs one barrier.  Workgroups are mapped
+// steps of 64 through a ring of S LDS stages filled by direct-to-LDS loads (global_load_lds_dwordx4: each
+// wave instruction lands 1 KB, lane l's 16 bytes at byte 16 l, with no registers or LDS store instructions
+// on the way): while step j is multiplied, steps j+1 .. j+S-2 are in flight, and each step needs one
+// barrier.  A stage holds the A and B tiles as 128-byte rows (64 f16) whose eight 16-byte chunks are stored
+// XOR-swizzled (chunk c of row r at slot c ^ (r & 7)), so the eight rows one fragment read touches hit
+// eight different bank groups; the swizzle is applied by choosing which global chunk each lane loads.
+// Workgroups are mapped
 // so that the tiles one XCD runs (workgroup b runs on XCD b mod 8) share their column blocks, which keeps
 // their weight rows in that XCD's L2.
 // Epilogues: f32 store, f16 store, f32 residual add (in place), or SwiGLU into f16: with GLU, each wave's columns are
@@ -191,23 +195,63 @@ __device__ __forceinline__ bool h16x2_nonfinite(uint32_t w) {
 }
 
 constexpr int kBK = 64;
-constexpr int kLdsPad = 16;  // 16-bit elements of padding per LDS row (32 bytes: measured fastest of 0, 8, 16, 24, 32)
+constexpr int kLdsPad = 16;  // 16-bit elements of padding per LDS row of the split-K kernel's register-staged tiles
 
+// Wait until at most N vector-memory operations of this wave are outstanding and every LDS operation has
+// completed (the waitcnt immediate of gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 left at its maximum,
+// lgkmcnt 11:8 = 0).
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
+}
+// The wait before step j's barrier: every load of step j done, those of the `ahead` (< D) later steps that
+// have been issued may still fly.  Loads of one wave complete in issue order.
+template <int LPS, int D>
+__device__ __forceinline__ void wait_steps(int ahead) {
+    if constexpr (D <= 0) {
+        wait_vm_lds<0>();
+    } else {
+        if (ahead >= D)
+            wait_vm_lds<D * LPS>();
+        else
+            wait_steps<LPS, D - 1>(ahead);
+    }
+}
+// One 16-byte direct-to-LDS load per lane: lane l's bytes land at LDS byte `lds` + 16 l (`lds` is the same
+// for the whole wave).  Written as an instruction the compiler does not see into, so that it adds no wait
+// for these loads before LDS reads of other stages; the K loop's own waits order them.  The instruction
+// has no register results.
+__device__ __forceinline__ void lds_dma16(const void *gaddr, const void *lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(m0) : "memory", "m0");
+}
+
+// LDS bytes an epilogue stages after the K loop (the ring is reused)
 template <int BM, int BN, int WM, int WN, int EPI>
+constexpr int gemm_epi_bytes() {
+    return EPI == G_SWIGLU   ? BM * (BN / 2 + 8) * 2
+           : EPI == G_RESID  ? BM * (BN + 4) * 4
+           : EPI == G_QKNORM ? BM * (BN + 8) * 2 + WM * WN * (8 * 64 + BM / WM) * 4
+                             : 0;
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int S>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
-    constexpr int NT = 64 * WM * WN;             // threads
+    constexpr int NW = WM * WN, NT = 64 * NW;    // waves, threads
     constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
     constexpr int TM = WTM / 16, TN = WTN / 16;
-    constexpr int LDR = kBK + kLdsPad;
-    constexpr int ACH = BM * kBK / 8 / NT;  // 16-byte chunks per thread per A step
-    constexpr int BCH = BN * kBK / 8 / NT;
-    static_assert(ACH >= 1 && BCH >= 1 && TM >= 1 && TN >= 1, "tile too small for the wave layout");
-    // one LDS region: the double-buffered A and B staging tiles, reused by the fused Q/K/V epilogue
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDR];
-    uint16_t(*As)[BM * LDR] = reinterpret_cast<uint16_t(*)[BM * LDR]>(smem);
-    uint16_t(*Bs)[BN * LDR] = reinterpret_cast<uint16_t(*)[BN * LDR]>(smem + 2 * BM * LDR);
+    constexpr int ACH = BM * 8 / NT, BCH = BN * 8 / NT;  // 1 KB load instructions per wave per step (A, B)
+    constexpr int LPS = ACH + BCH;
+    constexpr int STAGE = (BM + BN) * kBK;  // f16 elements per ring stage
+    static_assert(ACH * NT == BM * 8 && BCH * NT == BN * 8 && TM >= 1 && TN >= 1, "tile does not fit the wave layout");
+    static_assert(S >= 2 && (S - 2) * LPS < 64, "ring depth");
+    constexpr int RING = S * STAGE * 2, EPIB = gemm_epi_bytes<BM, BN, WM, WN, EPI>();
+    // one LDS region: the ring of staging tiles, reused by the epilogue
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[(RING > EPIB ? RING : EPIB) / 2];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     // XCD-aware tile order: the tiles of one XCD are consecutive in column-major tile order
     const int ntm = (g.M + BM - 1) / BM, nt = ntm * (g.N / BN);
@@ -226,44 +270,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
         }
     };
 
-    // Loads are unconditional (rows past M read row M-1, whose products the epilogue drops; steps past the
-    // last re-read it), so the loop body is branch-free and the compiler can wait for exactly the step it
-    // stores instead of for every load in flight.
-    // Per-thread chunk addresses are formed once; a step only adds its column offset.
+    // Load instruction c of this wave covers tile rows 8 (c NW + wave) .. +7; lane l fetches the chunk stored
+    // at slot l & 7 of row l >> 3 there, i.e. logical chunk (l & 7) ^ (row & 7).  Rows past M read row M-1
+    // (the epilogue drops their products).  Addresses are formed once; a step adds its column offset.
     const uint16_t *pa[ACH];
     const uint16_t *pb[BCH];
-    int la[ACH], lb[BCH];
 #pragma unroll
     for (int c = 0; c < ACH; ++c) {
-        const int ch = tid + NT * c, r = ch >> 3, kc = (ch & 7) * 8;
-        pa[c] = g.A + (size_t)min(m0 + r, g.M - 1) * g.K + kc;
-        la[c] = r * LDR + kc;
+        const int ch = (c * NW + wave) * 64 + lane, r = ch >> 3, lc = (ch & 7) ^ (r & 7);
+        pa[c] = g.A + (size_t)min(m0 + r, g.M - 1) * g.K + lc * 8;
     }
 #pragma unroll
     for (int c = 0; c < BCH; ++c) {
-        const int ch = tid + NT * c, r = ch >> 3, kc = (ch & 7) * 8;
-        pb[c] = g.W + (size_t)wrow(r) * g.K + kc;
-        lb[c] = r * LDR + kc;
+        const int ch = (c * NW + wave) * 64 + lane, r = ch >> 3, lc = (ch & 7) ^ (r & 7);
+        pb[c] = g.W + (size_t)wrow(r) * g.K + lc * 8;
     }
-    // Two register stages in named arrays (no indexing, so they stay in registers and every load keeps its
-    // own destination until it is stored): while step j is multiplied, steps j+1 and j+2 are in flight.
     const int nsteps = g.K / kBK;
-    uint4 a0[ACH], b0[BCH], a1[ACH], b1[BCH];
-    auto load_step = [&](uint4 (&xa)[ACH], uint4 (&xb)[BCH], int step) {
-        const int k0 = min(step, nsteps - 1) * kBK;
+    auto issue = [&](int step) {
+        const int k0 = step * kBK;
+        uint16_t *sa = smem + (step % S) * STAGE, *sb = sa + BM * kBK;
 #pragma unroll
-        for (int c = 0; c < ACH; ++c) {
-            const u32x4_t v = *(const u32x4_t *)(pa[c] + k0);  // vector-typed load: stays in registers
-            xa[c] = make_uint4(v.x, v.y, v.z, v.w);
-        }
+        for (int c = 0; c < ACH; ++c) lds_dma16(pa[c] + k0, sa + (c * NW + wave) * 512);
 #pragma unroll
-        for (int c = 0; c < BCH; ++c) xb[c] = load_nt16(pb[c] + k0);
-    };
-    auto store_step = [&](const uint4 (&xa)[ACH], const uint4 (&xb)[BCH], int buf) {
-#pragma unroll
-        for (int c = 0; c < ACH; ++c) *(uint4 *)(&As[buf][la[c]]) = xa[c];
-#pragma unroll
-        for (int c = 0; c < BCH; ++c) *(uint4 *)(&Bs[buf][lb[c]]) = xb[c];
+        for (int c = 0; c < BCH; ++c) lds_dma16(pb[c] + k0, sb + (c * NW + wave) * 512);
     };
 
     f32x4_t acc[TM][TN];
@@ -272,17 +301,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
 #pragma unroll
         for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int ksub = 8 * (lane >> 4), lrow = lane & 15;
-    auto multiply = [&](int buf) {
-        const uint16_t *as = As[buf], *bs = Bs[buf];
+    // fragment reads: lane (row lrow of a 16-row block, column group lq) takes logical chunk 4 kk + lq of its
+    // row, stored at slot (4 kk + lq) ^ (lrow & 7) (block bases are multiples of 8 rows)
+    const int lrow = lane & 15, lq = lane >> 4, sw = lane & 7;
+    auto multiply = [&](int step) {
+        const uint16_t *as = smem + (step % S) * STAGE, *bs = as + BM * kBK;
 #pragma unroll
-        for (int kk = 0; kk < kBK; kk += 32) {
+        for (int kk = 0; kk < 2; ++kk) {
+            const int slot = ((4 * kk + lq) ^ sw) * 8;
             uint4 af[TM], bfr[TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) af[i] = *(const uint4 *)(as + (wm * WTM + i * 16 + lrow) * LDR + kk + ksub);
+            for (int i = 0; i < TM; ++i) af[i] = *(const uint4 *)(as + (wm * WTM + i * 16 + lrow) * kBK + slot);
 #pragma unroll
-            for (int jj = 0; jj < TN; ++jj)
-                bfr[jj] = *(const uint4 *)(bs + (wn * WTN + jj * 16 + lrow) * LDR + kk + ksub);
+            for (int jj = 0; jj < TN; ++jj) bfr[jj] = *(const uint4 *)(bs + (wn * WTN + jj * 16 + lrow) * kBK + slot);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -290,24 +321,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
         }
     };
 
-    // steps past the last re-read the last one (their stores are never multiplied)
-    load_step(a0, b0, 0);
-    load_step(a1, b1, 1);
-    store_step(a0, b0, 0);
-    load_step(a0, b0, 2);
-    __syncthreads();
-    for (int j = 0; j < nsteps; j += 2) {  // nsteps is even
-        // a1: step j+1, a0: step j+2 in flight; LDS buffer 0 holds step j
-        store_step(a1, b1, 1);
-        load_step(a1, b1, j + 3);
-        multiply(0);
-        __syncthreads();
-        // a0: step j+2, a1: step j+3; buffer 1 holds step j+1
-        store_step(a0, b0, 0);
-        load_step(a0, b0, j + 4);
-        multiply(1);
-        __syncthreads();
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st)
+        if (st < nsteps) issue(st);
+    for (int j = 0; j < nsteps; ++j) {
+        // this wave's loads of step j have landed and its reads of step j-1 are done; after the barrier the
+        // same holds for every wave, so step j is complete in LDS and stage (j-1) mod S may be refilled
+        wait_steps<LPS, S - 2>(nsteps - 1 - j);
+        asm volatile("s_barrier" ::: "memory");
+        if (j + S - 1 < nsteps) issue(j + S - 1);
+        multiply(j);
     }
+    __syncthreads();  // every wave's last reads done before an epilogue reuses the ring (no loads in flight)
 
     // epilogue: lane holds C[4*(lane/16) + r][lane%16] of each 16x16 tile
     const int crow = 4 * (lane >> 4), ccol = lane & 15;
@@ -527,29 +552,32 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_f16_kernel(GemmArgs g) {
     }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI, int S>
 hipError_t launch_gemm_cfg(const GemmArgs &g, hipStream_t st) {
-    if (g.K % (2 * kBK) || g.N % BN) return hipErrorInvalidValue;
+    if (g.K % kBK || g.N % BN || g.M < 1) return hipErrorInvalidValue;
     const int nt = ((g.M + BM - 1) / BM) * (g.N / BN);
-    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, WM, WN, EPI>), dim3(nt), dim3(64 * WM * WN), 0, st, g);
+    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, WM, WN, EPI, S>), dim3(nt), dim3(64 * WM * WN), 0, st, g);
     return hipGetLastError();
 }
 
-// Tile shapes measured fastest on the 2048-token shapes (Q/K/V 4096 x 1024, gate/up 6144 x 1024, o_proj
-// 1024 x 2048, down 1024 x 3072).
+// Tile shapes and ring depths measured fastest on the 2048-token shapes with the weights streaming from HBM
+// (Q/K/V 4096 x 1024, gate/up 6144 x 1024, o_proj 1024 x 2048, down 1024 x 3072).
 template <int EPI>
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
     if (g.K % (2 * kBK) || g.N % 128) return hipErrorInvalidValue;
     if constexpr (EPI == G_QKNORM) {  // tiles whose waves hold 64 columns: two waves per 128-column head
         if (g.M <= 64) return hipErrorInvalidValue;
-        if (g.N % 256 == 0 && ((g.M + 127) / 128) * (g.N / 256) >= 256) return launch_gemm_cfg<128, 256, 4, 4, EPI>(g, st);
-        return launch_gemm_cfg<128, 128, 4, 2, EPI>(g, st);
+        if (g.N % 256 == 0 && ((g.M + 127) / 128) * (g.N / 256) >= 256)
+            return launch_gemm_cfg<128, 256, 4, 4, EPI, 3>(g, st);
+        return launch_gemm_cfg<128, 128, 4, 2, EPI, 2>(g, st);
     } else {
-        if (g.M <= 64) return launch_gemm_cfg<64, 32, 4, 1, EPI>(g, st);  // short prompts: weight-streaming bound
-        if (EPI != G_SWIGLU && g.N <= 1024) return launch_gemm_cfg<128, 64, 4, 2, EPI>(g, st);  // narrow outputs
+        if (g.M <= 64) return launch_gemm_cfg<64, 32, 4, 1, EPI, 3>(g, st);  // short prompts: weight-streaming bound
+        if (EPI != G_SWIGLU && g.N <= 1024) return launch_gemm_cfg<128, 64, 4, 2, EPI, 4>(g, st);  // narrow outputs
+        if constexpr (EPI == G_SWIGLU)
+            if (g.M > 512 && g.N % 256 == 0) return launch_gemm_cfg<256, 256, 4, 4, EPI, 2>(g, st);
         if ((EPI == G_STORE || EPI == G_STORE16) && g.N % 256 == 0 && ((g.M + 127) / 128) * (g.N / 256) >= 256)
-            return launch_gemm_cfg<128, 256, 4, 4, EPI>(g, st);
-        return launch_gemm_cfg<128, 128, 4, 2, EPI>(g, st);
+            return launch_gemm_cfg<128, 256, 4, 4, EPI, 3>(g, st);
+        return launch_gemm_cfg<128, 128, 4, 2, EPI, 2>(g, st);
     }
 }
 
